@@ -1,0 +1,238 @@
+"""Seeded synthetic inputs for the attention hot path.
+
+This module holds no attention arithmetic: it draws random numbers, rounds
+them to the storage type, and lays out paged caches and block tables.  Both
+the HIP path and the CPU oracle consume what it produces, so it is the only
+code they have in common.
+
+Storage conventions (see ``include/attn.h``):
+
+* dense prefill tensors are [B, H, T, D], row-major;
+* a paged cache is [num_pages, Hkv, page_size, D], one [page_size, D] tile per
+  (page, kv head) contiguous in memory;
+* block tables are int32 [B, max_pages]; entries past a sequence's last page
+  hold 0 (a valid page, never read);
+* bf16 tensors are carried on the host as uint16 bit patterns.
+
+Draw order for a workload (one ``numpy.random.Generator(PCG64(seed))``):
+lengths, page permutation, Q, K pool, V pool.  Large pools are drawn in
+fixed-size chunks, each from its own PCG64 stream seeded by the parent
+generator, so the values do not depend on how many threads draw them.
+"""
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+PAGE_SIZE = 16
+_CHUNK = 1 << 22
+
+# Values written into the unused slots of each sequence's last page.  They are
+# large so that reading a slot past kv_len shows up in any result.
+TAIL_K = 30.0
+TAIL_V = 1000.0
+
+
+def generator(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def bf16_bits(x):
+    """Round float32 values to bfloat16 (round to nearest, ties to even) and
+    return the 16-bit patterns as uint16.  NaN stays NaN."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return out
+
+
+def bf16_to_f32(bits):
+    """Exact widening of bf16 bit patterns (uint16) to float32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def normal(gen, shape, dtype):
+    """N(0,1) draws of ``shape`` in storage ``dtype`` ('bf16' -> uint16 bits,
+    'f32' -> float32).  Drawn in fixed chunks from child streams."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    nchunks = max(1, (n + _CHUNK - 1) // _CHUNK)
+    seeds = gen.integers(0, 2**63 - 1, size=nchunks, dtype=np.int64)
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def fill(c):
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        x = generator(int(seeds[c])).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = bf16_bits(x) if dtype == "bf16" else x
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def _const(value, dtype):
+    return bf16_bits(np.float32(value)).item() if dtype == "bf16" else np.float32(value)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def prefill_inputs(B, Hq, Hkv, Tq, Tk, D, dtype, seed):
+    """Q [B,Hq,Tq,D], K and V [B,Hkv,Tk,D], i.i.d. N(0,1)."""
+    gen = generator(seed)
+    q = normal(gen, (B, Hq, Tq, D), dtype)
+    k = normal(gen, (B, Hkv, Tk, D), dtype)
+    v = normal(gen, (B, Hkv, Tk, D), dtype)
+    return dict(q=q, k=k, v=v, B=B, Hq=Hq, Hkv=Hkv, Tq=Tq, Tk=Tk, D=D,
+                dtype=dtype, scale=1.0 / math.sqrt(D), seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# paged decode
+# ---------------------------------------------------------------------------
+
+def uniform_lengths(gen, n, lo, hi):
+    """Integer lengths uniform on [lo, hi] (both ends included)."""
+    return gen.integers(lo, hi, size=n, endpoint=True).astype(np.int32)
+
+
+def log_uniform_lengths(gen, n, lo, hi):
+    """floor(exp(U(ln lo, ln hi))), clamped to [lo, hi]."""
+    x = np.floor(np.exp(gen.uniform(math.log(lo), math.log(hi), size=n)))
+    return np.clip(x, lo, hi).astype(np.int32)
+
+
+def pages_for(lengths, page_size=PAGE_SIZE):
+    return (np.asarray(lengths, np.int64) + page_size - 1) // page_size
+
+
+def _tables(lengths, physical, page_size, max_pages=None):
+    """Block tables that map each sequence's logical pages, in order, onto
+    consecutive entries of ``physical``."""
+    npages = pages_for(lengths, page_size)
+    maxp = int(max_pages if max_pages is not None else max(1, int(npages.max(initial=1))))
+    table = np.zeros((len(lengths), maxp), np.int32)
+    pos = 0
+    for b, n in enumerate(npages):
+        table[b, :n] = physical[pos:pos + n]
+        pos += n
+    return table
+
+
+def _fill_tails(k_pages, v_pages, table, lengths, page_size, dtype):
+    """Write the tail-slot sentinels past each sequence's last token."""
+    kt, vt = _const(TAIL_K, dtype), _const(TAIL_V, dtype)
+    for b, L in enumerate(np.asarray(lengths)):
+        if L % page_size:
+            pg = table[b, (L - 1) // page_size]
+            k_pages[pg, :, L % page_size:, :] = kt
+            v_pages[pg, :, L % page_size:, :] = vt
+
+
+def paged_decode_inputs(B, Hq, Hkv, D, dtype, seed, lengths=None,
+                        length_range=(512, 8192), length_dist="uniform",
+                        page_size=PAGE_SIZE, tail_garbage=True, permute=True):
+    """One query token per sequence over a paged cache.
+
+    The physical pool holds exactly sum(ceil(L_b / page_size)) pages; logical
+    pages map through one random permutation of the pool (identity if
+    ``permute`` is False).
+    """
+    gen = generator(seed)
+    if lengths is None:
+        lo, hi = length_range
+        draw = uniform_lengths if length_dist == "uniform" else log_uniform_lengths
+        lengths = draw(gen, B, lo, hi)
+    lengths = np.asarray(lengths, np.int32)
+    total_pages = int(pages_for(lengths, page_size).sum())
+    pool = max(1, total_pages)
+    physical = gen.permutation(pool).astype(np.int32) if permute else \
+        np.arange(pool, dtype=np.int32)
+    table = _tables(lengths, physical, page_size)
+    q = normal(gen, (B, Hq, D), dtype)
+    k_pages = normal(gen, (pool, Hkv, page_size, D), dtype)
+    v_pages = normal(gen, (pool, Hkv, page_size, D), dtype)
+    if tail_garbage:
+        _fill_tails(k_pages, v_pages, table, lengths, page_size, dtype)
+    return dict(q=q, k_pages=k_pages, v_pages=v_pages, block_table=table,
+                kv_lens=lengths, B=B, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype,
+                page_size=page_size, scale=1.0 / math.sqrt(D), seed=seed,
+                max_kv_len=int(lengths.max(initial=0)))
+
+
+def cascade_inputs(R, H, D, dtype, seed, prefix_len=4096, suffix_range=(128, 1024),
+                   suffix_lens=None, page_size=PAGE_SIZE, Hkv=None,
+                   tail_garbage=True):
+    """Shared-prefix decode: R requests share one prefix of ``prefix_len``
+    tokens, stored once, plus their own suffixes.  Prefix and suffix pages
+    are all placed by one permutation of the pool."""
+    Hkv = Hkv or H
+    gen = generator(seed)
+    if suffix_lens is None:
+        suffix_lens = uniform_lengths(gen, R, *suffix_range)
+    suffix_lens = np.asarray(suffix_lens, np.int32)
+    npre = (prefix_len + page_size - 1) // page_size
+    total = npre + int(pages_for(suffix_lens, page_size).sum())
+    physical = gen.permutation(max(1, total)).astype(np.int32)
+    prefix_pages = physical[:npre].copy()
+    suffix_table = _tables(suffix_lens, physical[npre:], page_size)
+    q = normal(gen, (R, H, D), dtype)
+    k_pages = normal(gen, (max(1, total), Hkv, page_size, D), dtype)
+    v_pages = normal(gen, (max(1, total), Hkv, page_size, D), dtype)
+    if tail_garbage:
+        _fill_tails(k_pages, v_pages, suffix_table, suffix_lens, page_size, dtype)
+        if prefix_len % page_size:
+            pg = prefix_pages[-1]
+            k_pages[pg, :, prefix_len % page_size:, :] = _const(TAIL_K, dtype)
+            v_pages[pg, :, prefix_len % page_size:, :] = _const(TAIL_V, dtype)
+    return dict(q=q, k_pages=k_pages, v_pages=v_pages, prefix_pages=prefix_pages,
+                prefix_len=prefix_len, suffix_table=suffix_table,
+                suffix_lens=suffix_lens, R=R, H=H, Hkv=Hkv, D=D, dtype=dtype,
+                page_size=page_size, scale=1.0 / math.sqrt(D), seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads
+# ---------------------------------------------------------------------------
+
+WORKLOADS = {
+    1: "non-causal prefill B1 H1 T128 D64 fp32",
+    2: "causal prefill B4 H32 T1024 D128 bf16 (Llama2-7B attention shape)",
+    3: "paged decode MHA B32 H32 D128 bf16, L~U[512,8192], page 16",
+    4: "paged decode GQA B128 Hq32 Hkv8 D128 bf16, L~logU[1024,32768], page 16, "
+       "split <= 512",
+    5: "shared-prefix cascade decode, 64 requests, prefix 4096, suffix U[128,1024], "
+       "H32 D128 bf16, page 16",
+}
+
+
+def workload(n, seed=None):
+    """Inputs of workload ``n`` (1..5), seeded with 1000 + n by default."""
+    seed = 1000 + n if seed is None else seed
+    if n == 1:
+        return prefill_inputs(1, 1, 1, 128, 128, 64, "f32", seed) | dict(causal=False)
+    if n == 2:
+        return prefill_inputs(4, 32, 32, 1024, 1024, 128, "bf16", seed) | dict(causal=True)
+    if n == 3:
+        return paged_decode_inputs(32, 32, 32, 128, "bf16", seed,
+                                   length_range=(512, 8192), length_dist="uniform")
+    if n == 4:
+        return paged_decode_inputs(128, 32, 8, 128, "bf16", seed,
+                                   length_range=(1024, 32768), length_dist="log-uniform") \
+            | dict(split_tokens=512)
+    if n == 5:
+        return cascade_inputs(64, 32, 128, "bf16", seed)
+    raise ValueError(f"no workload {n}")

@@ -1,0 +1,269 @@
+/*
+ * Plain CPU fp64 oracle for fused scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header or constant with
+ * the HIP library.
+ *
+ * What it computes is the plain definition, written out with no blocking,
+ * no fusion and no reordering beyond the definition itself:
+ *
+ *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
+ *     -- "FlashInfer kernel library ..." (zyxy.net/archives/24491),
+ *        section 1 "Background and challenges": similarity of Q and K, a
+ *        softmax that turns the weights into a probability distribution, then
+ *        the weighted sum with V.
+ *
+ * The softmax is the numerically stable form (subtract the row maximum
+ * before exponentiating, then divide by the sum), as the same page's
+ * section 3 example and the TensorRT-LLM FMHA page (zyxy.net/?p=24414,
+ * section 2, "numerical stability") ask for.  The full score matrix of each
+ * (batch, head) is materialised in fp64.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - the scale is an explicit argument (1/sqrt(d) in every workload);
+ *   - lse_i = ln sum_j exp(s_ij), natural log of the scaled scores, so
+ *     lse_i = m_i + ln l_i with m_i the row max and l_i the sum of
+ *     exp(s_ij - m_i);
+ *   - causal: key j is masked for query i when j > i + (Tk - Tq)
+ *     (bottom-right alignment; identical to top-left when Tq == Tk);
+ *   - a row with every key masked gives O = 0 and lse = -inf;
+ *   - grouped heads: query head h reads key/value head h / (Hq / Hkv);
+ *   - paged cache: token t of sequence b lives in physical page
+ *     block_table[b][t / page_size], slot t % page_size, and a page holds
+ *     [Hkv][page_size][D] elements (the paged-attention description on the
+ *     xhh.club page, "how does paged attention manage the KV cache": fixed
+ *     size blocks mapped logical-to-physical through a block table);
+ *   - merging two partial states (o_a, lse_a), (o_b, lse_b) of disjoint key
+ *     sets gives the state of their union:
+ *       M = max(lse_a, lse_b); w_x = exp(lse_x - M);
+ *       lse = M + ln(w_a + w_b); o = (w_a o_a + w_b o_b) / (w_a + w_b),
+ *     with (anything, -inf) as the identity.  (The FlashDecoding++ summary,
+ *     wenjunhu.com/d/2311396.html, section 1, says split partial softmax
+ *     results are combined at the end; the formula is not printed there.)
+ *
+ * Element types: inputs may be fp64, fp32 or bf16 (given as raw 16-bit
+ * patterns); every element is widened to fp64 exactly before use.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2 };
+
+/* Exact widening of one stored element to fp64. */
+static double load_elem(const void *base, int dtype, size_t idx)
+{
+    if (dtype == ORC_F64)
+        return ((const double *)base)[idx];
+    if (dtype == ORC_F32)
+        return (double)((const float *)base)[idx];
+    /* bf16: the 16 stored bits are the top half of an fp32 pattern */
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Attention of tq query rows against tk key/value rows, all in fp64.
+ * Q is [tq][d], K and V are [tk][d], O is [tq][d], lse is [tq].
+ * S is a caller-provided [tq][tk] buffer: the materialised score matrix.
+ */
+static void attend_rows(const double *Q, const double *K, const double *V,
+                        int tq, int tk, int d, int causal, double scale,
+                        double *S, double *O, double *lse)
+{
+    /* step 1: similarity, S = scale * Q K^T (summed in d order) */
+    for (int i = 0; i < tq; i++) {
+        for (int j = 0; j < tk; j++) {
+            double acc = 0.0;
+            for (int c = 0; c < d; c++)
+                acc += Q[(size_t)i * d + c] * K[(size_t)j * d + c];
+            S[(size_t)i * tk + j] = scale * acc;
+        }
+    }
+    /* causal mask (bottom-right aligned) */
+    if (causal) {
+        for (int i = 0; i < tq; i++)
+            for (int j = 0; j < tk; j++)
+                if (j > i + (tk - tq))
+                    S[(size_t)i * tk + j] = -INFINITY;
+    }
+    /* step 2: stable softmax per row; step 3: weighted sum with V */
+    for (int i = 0; i < tq; i++) {
+        double *row = S + (size_t)i * tk;
+        double m = -INFINITY;
+        for (int j = 0; j < tk; j++)
+            if (row[j] > m)
+                m = row[j];
+        double *o = O + (size_t)i * d;
+        if (m == -INFINITY) {          /* no key attended */
+            for (int c = 0; c < d; c++)
+                o[c] = 0.0;
+            lse[i] = -INFINITY;
+            continue;
+        }
+        double l = 0.0;
+        for (int j = 0; j < tk; j++) {
+            row[j] = exp(row[j] - m);
+            l += row[j];
+        }
+        for (int c = 0; c < d; c++) {
+            double acc = 0.0;
+            for (int j = 0; j < tk; j++)
+                acc += row[j] * V[(size_t)j * d + c];
+            o[c] = acc / l;
+        }
+        lse[i] = m + log(l);
+    }
+}
+
+static void set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/*
+ * Dense attention.  q is [B][Hq][Tq][D]; k, v are [B][Hkv][Tk][D];
+ * o is fp64 [B][Hq][Tq][D]; lse is fp64 [B][Hq][Tq].
+ * Returns 0, or -1 on a bad shape, -2 if memory runs out.
+ */
+int oracle_attention(const void *q, const void *k, const void *v, int dtype,
+                     double *o, double *lse,
+                     int B, int Hq, int Hkv, int Tq, int Tk, int D,
+                     int causal, double scale, int nthreads)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Tq < 0 || Tk < 0 || D <= 0)
+        return -1;
+    const int group = Hq / Hkv;
+    int failed = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic)
+    for (long bh = 0; bh < (long)B * Hq; bh++) {
+        const int b = (int)(bh / Hq), h = (int)(bh % Hq), kvh = h / group;
+        double *Q = malloc(sizeof(double) * ((size_t)Tq * D + 1));
+        double *K = malloc(sizeof(double) * ((size_t)Tk * D + 1));
+        double *V = malloc(sizeof(double) * ((size_t)Tk * D + 1));
+        double *S = malloc(sizeof(double) * ((size_t)Tq * Tk + 1));
+        if (!Q || !K || !V || !S) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            const size_t qbase = ((size_t)b * Hq + h) * Tq * D;
+            const size_t kbase = ((size_t)b * Hkv + kvh) * Tk * D;
+            for (size_t e = 0; e < (size_t)Tq * D; e++)
+                Q[e] = load_elem(q, dtype, qbase + e);
+            for (size_t e = 0; e < (size_t)Tk * D; e++) {
+                K[e] = load_elem(k, dtype, kbase + e);
+                V[e] = load_elem(v, dtype, kbase + e);
+            }
+            attend_rows(Q, K, V, Tq, Tk, D, causal, scale, S,
+                        o + qbase, lse + ((size_t)b * Hq + h) * Tq);
+        }
+        free(Q); free(K); free(V); free(S);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Decode over a paged cache: one query row per (sequence, query head).
+ * q is [B][Hq][D]; k_pages, v_pages are [num_pages][Hkv][page_size][D];
+ * block_table is int32 [B][max_pages]; kv_lens is int32 [B].
+ * The query of sequence b attends exactly its kv_lens[b] cached tokens.
+ * o is fp64 [B][Hq][D], lse fp64 [B][Hq].
+ */
+int oracle_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                        int dtype, const int32_t *block_table,
+                        const int32_t *kv_lens, double *o, double *lse,
+                        int B, int Hq, int Hkv, int D, int page_size,
+                        int max_pages, long num_pages, double scale, int nthreads)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || page_size <= 0)
+        return -1;
+    for (int b = 0; b < B; b++) {
+        const int L = kv_lens[b];
+        if (L < 0 || (L + page_size - 1) / page_size > max_pages)
+            return -1;
+        for (int p = 0; p < (L + page_size - 1) / page_size; p++) {
+            const int32_t pg = block_table[(size_t)b * max_pages + p];
+            if (pg < 0 || pg >= num_pages)
+                return -1;
+        }
+    }
+    const int group = Hq / Hkv;
+    int failed = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic)
+    for (long bk = 0; bk < (long)B * Hkv; bk++) {
+        const int b = (int)(bk / Hkv), kvh = (int)(bk % Hkv);
+        const int L = kv_lens[b];
+        double *K = malloc(sizeof(double) * ((size_t)L * D + 1));
+        double *V = malloc(sizeof(double) * ((size_t)L * D + 1));
+        double *Q = malloc(sizeof(double) * ((size_t)D + 1));
+        double *S = malloc(sizeof(double) * ((size_t)L + 1));
+        if (!K || !V || !Q || !S) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            /* gather the logical key/value rows through the block table */
+            for (int t = 0; t < L; t++) {
+                const size_t page = (size_t)block_table[(size_t)b * max_pages + t / page_size];
+                const size_t src = ((page * Hkv + kvh) * page_size + t % page_size) * D;
+                for (int c = 0; c < D; c++) {
+                    K[(size_t)t * D + c] = load_elem(k_pages, dtype, src + c);
+                    V[(size_t)t * D + c] = load_elem(v_pages, dtype, src + c);
+                }
+            }
+            for (int g = 0; g < group; g++) {
+                const int h = kvh * group + g;
+                const size_t row = (size_t)b * Hq + h;
+                for (int c = 0; c < D; c++)
+                    Q[c] = load_elem(q, dtype, row * D + c);
+                attend_rows(Q, K, V, 1, L, D, 0, scale, S, o + row * D, lse + row);
+            }
+        }
+        free(K); free(V); free(Q); free(S);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Merge of two partial states over disjoint key sets, row by row.
+ * o_a, o_b, o_out are fp64 [rows][D]; lse_* are fp64 [rows].
+ * o_out/lse_out may alias either input.
+ */
+void oracle_merge_states(const double *o_a, const double *lse_a,
+                         const double *o_b, const double *lse_b,
+                         double *o_out, double *lse_out, long rows, int D)
+{
+    for (long r = 0; r < rows; r++) {
+        const double la = lse_a[r], lb = lse_b[r];
+        const double M = la > lb ? la : lb;
+        if (M == -INFINITY) {
+            for (int c = 0; c < D; c++)
+                o_out[r * D + c] = 0.0;
+            lse_out[r] = -INFINITY;
+            continue;
+        }
+        const double wa = exp(la - M), wb = exp(lb - M);
+        for (int c = 0; c < D; c++) {
+            /* a side with weight 0 (lse = -inf) is absent, whatever its o */
+            const double ta = wa > 0.0 ? wa * o_a[r * D + c] : 0.0;
+            const double tb = wb > 0.0 ? wb * o_b[r * D + c] : 0.0;
+            o_out[r * D + c] = (ta + tb) / (wa + wb);
+        }
+        lse_out[r] = M + log(wa + wb);
+    }
+}

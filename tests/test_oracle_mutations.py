@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in copies of the oracle (CPU only) and check that
+the pin suite catches each one: a dropped term, a wrong sign or index, a
+transposed operand, the wrong log base, a mask off by one.
+
+The mutated copies are compiled into a temporary directory; oracle.c itself is
+never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTATIONS = {
+    "scale dropped": ("S[(size_t)i * tk + j] = scale * acc;", "S[(size_t)i * tk + j] = acc;"),
+    "mask off by one": ("if (j > i + (tk - tq))", "if (j >= i + (tk - tq))"),
+    "mask alignment top-left": ("if (j > i + (tk - tq))", "if (j > i)"),
+    "exp sign": ("row[j] = exp(row[j] - m);", "row[j] = exp(m - row[j]);"),
+    "max not subtracted in lse": ("lse[i] = m + log(l);", "lse[i] = log(l);"),
+    "lse base 2": ("lse[i] = m + log(l);", "lse[i] = m + log2(l);"),
+    "not normalised": ("o[c] = acc / l;", "o[c] = acc;"),
+    "V columns reversed": ("acc += row[j] * V[(size_t)j * d + c];",
+                           "acc += row[j] * V[(size_t)j * d + (d - 1 - c)];"),
+    "K used for V": ("acc += row[j] * V[(size_t)j * d + c];",
+                     "acc += row[j] * K[(size_t)j * d + c];"),
+    "GQA interleaved": ("kvh = h / group;", "kvh = h % Hkv;"),
+    "paged slot shifted": ("t % page_size) * D;", "(t + 1) % page_size) * D;"),
+    "paged head ignored": ("((page * Hkv + kvh) * page_size", "((page * Hkv + 0) * page_size"),
+    "merge weights swapped": ("const double ta = wa > 0.0 ? wa * o_a[r * D + c] : 0.0;",
+                              "const double ta = wa > 0.0 ? wb * o_a[r * D + c] : 0.0;"),
+    "merge lse without max": ("lse_out[r] = M + log(wa + wb);", "lse_out[r] = log(wa + wb);"),
+    "bf16 widened as low half": ("<< 16;\n    float f;", ";\n    float f;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, source, tmp_path):
+    old, new = MUTATIONS[name]
+    assert source.count(old) >= 1, f"mutation anchor for '{name}' not found"
+    mutated = source.replace(old, new)
+    src = tmp_path / "oracle_mut.c"
+    src.write_text(mutated)
+    lib_path = oracle.build(str(tmp_path / "liboracle_mut.so"), str(src))
+    lib = oracle.load(lib_path)
+    failures = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, RuntimeError, ValueError):
+            failures.append(check.__name__)
+    assert failures, f"no pin caught the planted mistake '{name}'"

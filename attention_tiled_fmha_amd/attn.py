@@ -1,0 +1,215 @@
+"""Python binding of libattn.so (the C ABI in include/attn.h).
+
+Argument marshalling only: shapes and element types are read off torch
+device tensors, pointers and the current HIP stream are passed through
+ctypes, and a non-zero status becomes an :class:`AttnError`.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.  If
+libattn.so has not been built, the first call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+BF16, F32 = 0, 1
+_lib = None
+
+# Every symbol include/attn.h declares, with (restype, argtypes).
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_ip = ctypes.POINTER(ctypes.c_int)
+SIGNATURES = {
+    "attn_status_str": (ctypes.c_char_p, [_i]),
+    "attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp]),
+    "attn_decode_plan": (_i, [_i, _i, _i, _i, _i, _ip, _ip]),
+    "attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "attn_decode_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                               _i, _i, _f, _vp, _sz, _vp]),
+    "attn_decode_paged_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                  _i, _i, _i, _f, _vp, _sz, _vp, _vp]),
+    "attn_merge_states": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
+    "attn_shared_prefix_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "attn_decode_shared_prefix": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
+                                       _i, _i, _f, _vp, _sz, _vp]),
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("split_tokens", ctypes.c_int), ("reserved", ctypes.c_int * 7)]
+
+
+def load(path=LIB_PATH):
+    """Load libattn.so and declare every exported signature."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
+                               "python -m attention_tiled_fmha_amd.build")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_str(status):
+    return load().attn_status_str(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise AttnError(status, where)
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dense(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+# ---------------------------------------------------------------------------
+
+def attn_prefill(q, k, v, o, lse=None, causal=False, scale=None, stream=None):
+    """q, o [B,Hq,Tq,D]; k, v [B,Hkv,Tk,D]; lse fp32 [B,Hq,Tq] or None."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _dense(t, n)
+    B, Hq, Tq, D = q.shape
+    _, Hkv, Tk, _ = k.shape
+    if o.shape != q.shape or v.shape != k.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if lse is not None:
+        _dense(lse, "lse")
+        if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, Hq, Tq]")
+    dt = _dtype(q)
+    if not (_dtype(k) == _dtype(v) == _dtype(o) == dt):
+        raise TypeError("q, k, v, o must share one element type")
+    scale = D ** -0.5 if scale is None else scale
+    _check(load().attn_prefill(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, Tq, Tk, D, dt,
+                               int(bool(causal)), float(scale), _stream(stream)), "attn_prefill")
+
+
+def attn_decode_plan(batch, heads_kv, max_kv_len, num_cus=0, requested_split=0):
+    split, max_splits = ctypes.c_int(), ctypes.c_int()
+    _check(load().attn_decode_plan(batch, heads_kv, max_kv_len, num_cus, requested_split,
+                                   ctypes.byref(split), ctypes.byref(max_splits)),
+           "attn_decode_plan")
+    return split.value, max_splits.value
+
+
+def attn_decode_workspace_bytes(batch, heads_q, heads_kv, head_dim, max_kv_len, split_tokens=0):
+    return load().attn_decode_workspace_bytes(batch, heads_q, heads_kv, head_dim, max_kv_len,
+                                              split_tokens)
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse=None, max_kv_len=None,
+                      scale=None, workspace=None, split_tokens=0, stream=None):
+    """q, o [B,Hq,D]; k_pages, v_pages [P,Hkv,16,D]; block_table int32 [B,maxp];
+    kv_lens int32 [B]; lse fp32 [B,Hq] or None.  max_kv_len is the host-side
+    bound of kv_lens (required).  A workspace of the needed size is allocated
+    with torch when none is given."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"),
+                 (block_table, "block_table"), (kv_lens, "kv_lens"), (o, "o")):
+        _dense(t, n)
+    if max_kv_len is None:
+        raise ValueError("max_kv_len (host-side bound of kv_lens) is required")
+    B, Hq, D = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    if o.shape != q.shape or v_pages.shape != k_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if block_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
+        raise TypeError("block_table and kv_lens must be int32")
+    if block_table.shape[0] != B or kv_lens.shape != (B,):
+        raise ValueError("block_table / kv_lens shape mismatch")
+    if lse is not None:
+        _dense(lse, "lse")
+        if lse.shape != (B, Hq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, Hq]")
+    dt = _dtype(q)
+    if not (_dtype(k_pages) == _dtype(v_pages) == dt):
+        raise TypeError("q and the pages must share one element type")
+    scale = D ** -0.5 if scale is None else scale
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, D, max_kv_len, split_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    opts = DecodeOpts(split_tokens=int(split_tokens))
+    _check(load().attn_decode_paged_ex(
+        _p(q), _p(k_pages), _p(v_pages), _p(block_table), _p(kv_lens), _p(o), _p(lse),
+        B, Hq, Hkv, D, page, block_table.shape[1], int(max_kv_len), dt, _dtype(o),
+        float(scale), _p(workspace), ws_bytes, _stream(stream), ctypes.byref(opts)),
+        "attn_decode_paged")
+
+
+def attn_merge_states(o_a, lse_a, o_b, lse_b, stream=None):
+    """In place into (o_a, lse_a); o_* [rows..., D], lse_* fp32 [rows...]."""
+    for t, n in ((o_a, "o_a"), (lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b")):
+        _dense(t, n)
+    if o_a.shape != o_b.shape or lse_a.shape != lse_b.shape or o_a.shape[:-1] != lse_a.shape:
+        raise ValueError("shape mismatch")
+    if lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
+        raise TypeError("lse must be fp32")
+    dt = _dtype(o_a)
+    if _dtype(o_b) != dt:
+        raise TypeError("o_a and o_b must share one element type")
+    D = o_a.shape[-1]
+    rows = lse_a.numel()
+    _check(load().attn_merge_states(_p(o_a), _p(lse_a), _p(o_b), _p(lse_b), rows, D, dt,
+                                    _stream(stream)), "attn_merge_states")
+
+
+def attn_shared_prefix_workspace_bytes(batch, heads_q, heads_kv, head_dim, prefix_len, dtype=BF16):
+    return load().attn_shared_prefix_workspace_bytes(batch, heads_q, heads_kv, head_dim,
+                                                     prefix_len, dtype)
+
+
+def attn_decode_shared_prefix(q, k_pages, v_pages, prefix_pages, prefix_len, o, lse=None,
+                              scale=None, workspace=None, stream=None):
+    """q, o [B,Hq,D]; prefix_pages int32 [ceil(prefix_len/16)]; lse fp32 [B,Hq]."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (o, "o")):
+        _dense(t, n)
+    B, Hq, D = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    if prefix_len > 0:
+        _dense(prefix_pages, "prefix_pages")
+        if prefix_pages.dtype != torch.int32 or prefix_pages.numel() * page < prefix_len:
+            raise ValueError("prefix_pages must be int32 covering prefix_len tokens")
+    if lse is not None:
+        _dense(lse, "lse")
+    dt = _dtype(q)
+    scale = D ** -0.5 if scale is None else scale
+    need = attn_shared_prefix_workspace_bytes(B, Hq, Hkv, D, prefix_len, dt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().attn_decode_shared_prefix(
+        _p(q), _p(k_pages), _p(v_pages), _p(prefix_pages), int(prefix_len), _p(o), _p(lse),
+        B, Hq, Hkv, D, page, dt, _dtype(o), float(scale), _p(workspace), ws_bytes,
+        _stream(stream)), "attn_decode_shared_prefix")

@@ -1,0 +1,300 @@
+// The C ABI of libattn.so (declared in include/attn.h): argument checks,
+// split planning and kernel launches.  Every check runs on the host before
+// anything is enqueued; on any error nothing is launched.  The library keeps
+// no state between calls.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kPageSize = 16;
+constexpr int kPlanCUs = 256;      // MI355X compute units (planning only)
+constexpr int kMaxSplit = 512;     // longest chunk one workgroup takes
+constexpr int kMinSplit = 64;      // 4 wavefronts x one 16-token page
+constexpr int kGridYZ = 65535;
+
+bool dim_ok(int d) { return d == 64 || d == 128; }
+bool dtype_ok(int t) { return t == ATTN_BF16 || t == ATTN_F32; }
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int plan(int batch, int heads_kv, int max_kv_len, int num_cus, int requested, int* split,
+         int* max_splits) {
+    if (batch < 0 || heads_kv <= 0 || max_kv_len < 0) return ATTN_E_SHAPE;
+    if (num_cus <= 0) num_cus = kPlanCUs;
+    int s;
+    if (requested > 0) {
+        s = (requested + kMinSplit - 1) / kMinSplit * kMinSplit;
+    } else {
+        // Aim for ~8 chunks per compute unit over the batch's worst case, in
+        // power-of-two chunks between 64 and 512 tokens: long contexts and
+        // big batches get long chunks (less combine traffic), small batches
+        // get short ones (enough workgroups to fill the GPU).
+        const double per_item =
+            (double)batch * heads_kv * (double)max_kv_len / (8.0 * num_cus);
+        s = kMinSplit;
+        while (s < kMaxSplit && 2.0 * s <= per_item) s *= 2;
+    }
+    *split = s;
+    *max_splits = max_kv_len > 0 ? (max_kv_len + s - 1) / s : 1;
+    return ATTN_OK;
+}
+
+size_t decode_ws_bytes(int batch, int heads_q, int head_dim, int max_splits) {
+    if (max_splits <= 1) return 0;
+    const size_t rows = (size_t)batch * heads_q * max_splits;
+    return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int check_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+// Shared-prefix chunking: a workgroup covers 4 wavefronts x tpw tiles of 32
+// keys; aim for about two workgroups per compute unit over all kv heads and
+// 64-row query blocks.
+void prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int* chunk, int* tpw,
+                 int* n_chunks) {
+    const long rows = (long)batch * (heads_q / heads_kv);
+    const long base = (long)heads_kv * ((rows + 63) / 64);
+    const long want = std::max(1L, (2L * kPlanCUs + base - 1) / base);
+    const long tiles = (prefix_len + 31) / 32;
+    const long t = std::max(1L, (tiles + 4 * want - 1) / (4 * want));
+    *tpw = (int)t;
+    *chunk = (int)(128 * t);
+    *n_chunks = (int)((prefix_len + *chunk - 1) / *chunk);
+}
+
+int decode_common(const void* q, const void* k_pages, const void* v_pages,
+                  const int32_t* block_table, long bt_stride, const int32_t* kv_lens,
+                  int fixed_len, void* o, float* lse, int batch, int heads_q, int heads_kv,
+                  int head_dim, int page_size, int max_pages_per_seq, int max_kv_len, int dtype,
+                  int o_dtype, float scale, void* workspace, size_t workspace_bytes,
+                  void* stream, int requested_split) {
+    if (!dtype_ok(dtype) || !dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
+    if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || max_kv_len < 0 || max_pages_per_seq < 0)
+        return ATTN_E_SHAPE;
+    if (heads_q % heads_kv) return ATTN_E_SHAPE;
+    if (!dim_ok(head_dim) || page_size != kPageSize) return ATTN_E_UNSUPPORTED;
+    const int G = heads_q / heads_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return ATTN_E_UNSUPPORTED;
+    if ((long)max_pages_per_seq * page_size < max_kv_len) return ATTN_E_SHAPE;
+    if (!scale_ok(scale)) return ATTN_E_ARG;
+    if (batch == 0) return ATTN_OK;
+    if (!q || !k_pages || !v_pages || !o || (!block_table && max_kv_len > 0))
+        return ATTN_E_NULL;
+    if (batch > kGridYZ || heads_kv > kGridYZ) return ATTN_E_UNSUPPORTED;
+    int split = 0, max_splits = 0;
+    const int rc = plan(batch, heads_kv, max_kv_len, kPlanCUs, requested_split, &split, &max_splits);
+    if (rc != ATTN_OK) return rc;
+    const size_t need = decode_ws_bytes(batch, heads_q, head_dim, max_splits);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
+
+    attn::DecodeArgs a{};
+    a.q = q;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.kv_lens = kv_lens;
+    a.fixed_len = fixed_len;
+    a.max_len = max_kv_len;
+    a.o = o;
+    a.lse = lse;
+    const size_t rows = (size_t)batch * heads_q * max_splits;
+    a.ws_o = need ? (float*)workspace : nullptr;
+    a.ws_lse = need ? (float*)((char*)workspace + align256(rows * head_dim * sizeof(float))) : nullptr;
+    a.B = batch;
+    a.Hq = heads_q;
+    a.Hkv = heads_kv;
+    a.D = head_dim;
+    a.split_tokens = split;
+    a.max_splits = max_splits;
+    a.in_f32 = dtype == ATTN_F32;
+    a.out_f32 = o_dtype == ATTN_F32;
+    a.scale = scale;
+    return check_hip(attn::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_E_NULL: return "a required pointer is NULL";
+        case ATTN_E_SHAPE: return "invalid or inconsistent sizes";
+        case ATTN_E_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_E_WORKSPACE: return "workspace missing or too small";
+        case ATTN_E_HIP: return "HIP launch error";
+        case ATTN_E_ARG: return "argument value out of domain";
+        default: return "unknown status";
+    }
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                 int heads_q, int heads_kv, int seq_q, int seq_kv, int head_dim, int dtype,
+                 int causal, float scale, void* stream) {
+    if (!dtype_ok(dtype)) return ATTN_E_UNSUPPORTED;
+    if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || seq_q < 0 || seq_kv < 0)
+        return ATTN_E_SHAPE;
+    if (heads_q % heads_kv) return ATTN_E_SHAPE;
+    if (!dim_ok(head_dim)) return ATTN_E_UNSUPPORTED;
+    if (!scale_ok(scale)) return ATTN_E_ARG;
+    if (batch == 0 || seq_q == 0) return ATTN_OK;
+    if (!q || !o || (seq_kv > 0 && (!k || !v))) return ATTN_E_NULL;
+    if ((long)batch * heads_q * ((seq_q + 255) / 256) > 0x7fffffffL) return ATTN_E_UNSUPPORTED;
+    hipError_t e;
+    if (dtype == ATTN_F32)
+        e = attn::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, (float*)o,
+                                     lse, batch, heads_q, heads_kv, seq_q, seq_kv, head_dim,
+                                     causal != 0, scale, (hipStream_t)stream);
+    else
+        e = attn::launch_prefill_bf16(q, k, v, o, lse, batch, heads_q, heads_kv, seq_q, seq_kv,
+                                      head_dim, causal != 0, scale, (hipStream_t)stream);
+    return check_hip(e);
+}
+
+int attn_decode_plan(int batch, int heads_kv, int max_kv_len, int num_cus, int requested_split,
+                     int* split_tokens, int* max_splits) {
+    if (!split_tokens || !max_splits) return ATTN_E_NULL;
+    return plan(batch, heads_kv, max_kv_len, num_cus, requested_split, split_tokens, max_splits);
+}
+
+size_t attn_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int head_dim,
+                                   int max_kv_len, int split_tokens) {
+    int split = 0, max_splits = 0;
+    if (heads_q <= 0 || head_dim <= 0 ||
+        plan(batch, heads_kv, max_kv_len, kPlanCUs, split_tokens, &split, &max_splits) != ATTN_OK)
+        return 0;
+    return decode_ws_bytes(batch, heads_q, head_dim, max_splits);
+}
+
+int attn_decode_paged_ex(const void* q, const void* k_pages, const void* v_pages,
+                         const int32_t* block_table, const int32_t* kv_lens, void* o, float* lse,
+                         int batch, int heads_q, int heads_kv, int head_dim, int page_size,
+                         int max_pages_per_seq, int max_kv_len, int dtype, int o_dtype,
+                         float scale, void* workspace, size_t workspace_bytes, void* stream,
+                         const attn_decode_opts* opts) {
+    if (batch > 0 && !kv_lens) return ATTN_E_NULL;
+    const int requested = opts ? opts->split_tokens : 0;
+    if (requested < 0) return ATTN_E_ARG;
+    return decode_common(q, k_pages, v_pages, block_table, max_pages_per_seq, kv_lens, 0, o,
+                         lse, batch, heads_q, heads_kv, head_dim, page_size, max_pages_per_seq,
+                         max_kv_len, dtype, o_dtype, scale, workspace, workspace_bytes, stream,
+                         requested);
+}
+
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* kv_lens, void* o, float* lse,
+                      int batch, int heads_q, int heads_kv, int head_dim, int page_size,
+                      int max_pages_per_seq, int max_kv_len, int dtype, int o_dtype,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return attn_decode_paged_ex(q, k_pages, v_pages, block_table, kv_lens, o, lse, batch,
+                                heads_q, heads_kv, head_dim, page_size, max_pages_per_seq,
+                                max_kv_len, dtype, o_dtype, scale, workspace, workspace_bytes,
+                                stream, nullptr);
+}
+
+int attn_merge_states(void* o_a, float* lse_a, const void* o_b, const float* lse_b, int rows,
+                      int head_dim, int o_dtype, void* stream) {
+    if (!dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
+    if (rows < 0) return ATTN_E_SHAPE;
+    if (!dim_ok(head_dim)) return ATTN_E_UNSUPPORTED;
+    if (rows == 0) return ATTN_OK;
+    if (!o_a || !lse_a || !o_b || !lse_b) return ATTN_E_NULL;
+    return check_hip(attn::launch_merge_states(o_a, lse_a, o_b, lse_b, rows, head_dim,
+                                               o_dtype == ATTN_F32, (hipStream_t)stream));
+}
+
+size_t attn_shared_prefix_workspace_bytes(int batch, int heads_q, int heads_kv, int head_dim,
+                                          int prefix_len, int dtype) {
+    if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || heads_q % heads_kv || head_dim <= 0 ||
+        prefix_len < 0)
+        return 0;
+    if (dtype == ATTN_BF16 && prefix_len > 0) {
+        int chunk = 0, tpw = 0, n_chunks = 0;
+        prefix_plan(batch, heads_q, heads_kv, prefix_len, &chunk, &tpw, &n_chunks);
+        return decode_ws_bytes(batch, heads_q, head_dim, n_chunks);
+    }
+    int split = 0, max_splits = 0;
+    if (plan(batch, heads_kv, prefix_len, kPlanCUs, 0, &split, &max_splits) != ATTN_OK) return 0;
+    return decode_ws_bytes(batch, heads_q, head_dim, max_splits);
+}
+
+int attn_decode_shared_prefix(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* prefix_pages, int prefix_len, void* o, float* lse,
+                              int batch, int heads_q, int heads_kv, int head_dim, int page_size,
+                              int dtype, int o_dtype, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (prefix_len < 0) return ATTN_E_SHAPE;
+    const int npages = (prefix_len + kPageSize - 1) / kPageSize;
+    if (dtype != ATTN_BF16 || prefix_len == 0) {
+        // fp32 test mode (and the empty prefix): every request runs the paged
+        // decode over the one shared table.
+        return decode_common(q, k_pages, v_pages, prefix_pages, 0, nullptr, prefix_len, o, lse,
+                             batch, heads_q, heads_kv, head_dim, page_size, npages, prefix_len,
+                             dtype, o_dtype, scale, workspace, workspace_bytes, stream, 0);
+    }
+    if (!dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
+    if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || heads_q % heads_kv) return ATTN_E_SHAPE;
+    if (!dim_ok(head_dim) || page_size != kPageSize) return ATTN_E_UNSUPPORTED;
+    if (!scale_ok(scale)) return ATTN_E_ARG;
+    if (batch == 0) return ATTN_OK;
+    if (!q || !k_pages || !v_pages || !prefix_pages || !o) return ATTN_E_NULL;
+    const long rows = (long)batch * (heads_q / heads_kv);
+    if ((rows + 63) / 64 > kGridYZ || heads_kv > kGridYZ) return ATTN_E_UNSUPPORTED;
+    int chunk = 0, tpw = 0, n_chunks = 0;
+    prefix_plan(batch, heads_q, heads_kv, prefix_len, &chunk, &tpw, &n_chunks);
+    const size_t need = decode_ws_bytes(batch, heads_q, head_dim, n_chunks);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
+    const size_t nrow = (size_t)batch * heads_q * n_chunks;
+    float* ws_o = need ? (float*)workspace : nullptr;
+    float* ws_lse = need ? (float*)((char*)workspace + align256(nrow * head_dim * sizeof(float)))
+                         : nullptr;
+
+    attn::PrefixArgs a{};
+    a.q = q;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.pages = prefix_pages;
+    a.prefix_len = prefix_len;
+    a.o = o;
+    a.lse = lse;
+    a.ws_o = ws_o;
+    a.ws_lse = ws_lse;
+    a.R = batch;
+    a.Hq = heads_q;
+    a.Hkv = heads_kv;
+    a.D = head_dim;
+    a.chunk = chunk;
+    a.tiles_per_wave = tpw;
+    a.out_f32 = o_dtype == ATTN_F32;
+    a.scale = scale;
+    hipError_t e = attn::launch_prefix(a, (hipStream_t)stream);
+    if (e != hipSuccess || n_chunks <= 1) return check_hip(e);
+
+    attn::DecodeArgs c{};
+    c.kv_lens = nullptr;
+    c.fixed_len = prefix_len;
+    c.max_len = prefix_len;
+    c.o = o;
+    c.lse = lse;
+    c.ws_o = ws_o;
+    c.ws_lse = ws_lse;
+    c.B = batch;
+    c.Hq = heads_q;
+    c.Hkv = heads_kv;
+    c.D = head_dim;
+    c.split_tokens = chunk;
+    c.max_splits = n_chunks;
+    c.out_f32 = a.out_f32;
+    return check_hip(attn::launch_decode_combine(c, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Host-side launchers of the gfx950 kernels.  Each launcher assumes its
+// arguments were validated by the C ABI layer (attn_api.cpp) and returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Dense prefill, bf16 in/out, bf16 MFMA with fp32 accumulation.
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o,
+                               float* lse, int B, int Hq, int Hkv, int Tq, int Tk,
+                               int D, bool causal, float scale, hipStream_t stream);
+
+// Dense prefill, fp32 in/out, fp32 arithmetic (the exactness test mode).
+hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* o,
+                              float* lse, int B, int Hq, int Hkv, int Tq, int Tk, int D,
+                              bool causal, float scale, hipStream_t stream);
+
+// Paged decode, split-KV.  One workgroup per (chunk, kv head, sequence).
+// bt_stride is the row stride of the block table (0: every sequence reads
+// row 0); kv_lens may be NULL, then every sequence has fixed_len tokens.
+struct DecodeArgs {
+    const void* q;
+    const void* k_pages;
+    const void* v_pages;
+    const int32_t* block_table;
+    long bt_stride;
+    const int32_t* kv_lens;
+    int fixed_len;
+    int max_len;    // host bound; every length is clamped to [0, max_len]
+    void* o;
+    float* lse;
+    float* ws_o;    // [B*Hq][max_splits][D] fp32 partial outputs
+    float* ws_lse;  // [B*Hq][max_splits]    fp32 partial lse
+    int B, Hq, Hkv, D;
+    int split_tokens, max_splits;
+    bool in_f32, out_f32;
+    float scale;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Log-sum-exp combine of per-chunk partial states in the workspace into the
+// output (rows = B*Hq, chunks = ceil(length / split_tokens)).
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
+
+// Shared-prefix stage of cascade decode (bf16 MFMA).  Grid: one workgroup
+// per (prefix chunk, kv head, block of 64 query rows); each chunk is
+// 4 wavefronts x tiles_per_wave x 32 keys long.  With more than one chunk the
+// per-chunk states go to ws_o / ws_lse ([R*Hq][n_chunks][D], [R*Hq][n_chunks])
+// and must be combined with launch_decode_combine.
+struct PrefixArgs {
+    const void* q;           // [R, Hq, D] bf16
+    const void* k_pages;     // [P, Hkv, 16, D] bf16
+    const void* v_pages;
+    const int32_t* pages;    // prefix pages
+    int prefix_len;
+    void* o;                 // [R, Hq, D] bf16 or fp32
+    float* lse;              // [R, Hq] or null
+    float* ws_o;
+    float* ws_lse;
+    int R, Hq, Hkv, D;
+    int chunk, tiles_per_wave;
+    bool out_f32;
+    float scale;
+};
+hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
+
+// In-place merge of two partial states.
+hipError_t launch_merge_states(void* o_a, float* lse_a, const void* o_b, const float* lse_b,
+                               int rows, int D, bool f32, hipStream_t stream);
+
+}  // namespace attn

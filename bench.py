@@ -1,0 +1,282 @@
+"""Benchmark of the fused-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+The bench line's workload is causal prefill in the Llama2-7B attention shape
+(B4 H32 T1024 D128, bf16 Q/K/V i.i.d. N(0,1), fp32 accumulation, scale
+1/sqrt(128)); one step is one attn_prefill launch over one batch.  `value`
+is its throughput in algorithmic TFLOP/s: 4*D flop per attended
+(query, key) pair, T(T+1)/2 pairs per (b, h) under the causal mask.
+
+The paged-decode workloads (MHA B32, GQA 32/8 B128, shared-prefix cascade)
+are timed in the same run and reported under "decode" in KV GB/s: unique
+K+V bytes read, the shared prefix counted once.
+
+Timing: W untimed warm-up steps, then K steps bracketed by a device
+synchronisation on both sides; HIP events on the launch stream give each
+launch's duration (the roofline uses their mean).  The prefill rotates
+through three input sets so the 256 MB last-level cache cannot hold the
+working set; the cascade flushes it before every timed repetition.
+
+The CPU baseline runs the fp64 oracle on a bounded sample of the same
+workload (a few (b, h) pairs, ~10-30 s of CPU work) on the host's cores.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from attention_tiled_fmha_amd import attn  # noqa: E402
+from attention_tiled_fmha_amd import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_launches(fn, steps, warmup, before=None):
+    """Per-launch durations (ms) from HIP events on the current stream, plus
+    the wall span of the K timed steps."""
+    for i in range(warmup):
+        if before:
+            before(i)
+        fn(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if before:
+            before(i)
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    span = starts[0].elapsed_time(ends[-1])
+    return durs, span, wall
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "attention_tiled_fmha_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"{name}_counters.json")
+    try:
+        with open(path) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_digest") != digest:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+def bench_prefill(steps, warmup):
+    sets = []
+    for s in range(3):
+        inp = wl.workload(2, seed=1002 + 100 * s)
+        sets.append(tuple(dev(inp[x]) for x in ("q", "k", "v")))
+    B, H, T, D = 4, 32, 1024, 128
+    o = torch.empty((B, H, T, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), device="cuda")
+    scale = 1.0 / math.sqrt(D)
+
+    def step(i):
+        q, k, v = sets[i % 3]
+        attn.attn_prefill(q, k, v, o, lse, causal=True, scale=scale)
+
+    durs, span, wall = time_launches(step, steps, warmup)
+    flops = 4.0 * D * (T * (T + 1) / 2) * B * H
+    mean_ms = float(np.mean(durs))
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    digest = source_digest("prefill_bf16.hip", "common.h")
+    traffic = measured_traffic("prefill_bf16_causal_b4h32t1024d128", digest)
+    return dict(
+        ms_per_step=span / steps, mean_launch_ms=mean_ms, median_launch_ms=float(np.median(durs)),
+        tflops=flops / (span / steps * 1e-3) / 1e12, flops=flops, wall_s=wall,
+        roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
+                      traffic=traffic, kernel="prefill_bf16_kernel<128,true>",
+                      algorithmic_bytes=int(4 * B * H * T * D * 2 + B * H * T * 4),
+                      source_digest=digest))
+
+
+def kv_bytes(lengths, hkv, d, elem=2):
+    return int(np.sum(np.asarray(lengths, np.int64))) * hkv * d * 2 * elem
+
+
+def bench_decode(n, steps, warmup):
+    d = wl.workload(n)
+    q = dev(d["q"])
+    kp, vp = dev(d["k_pages"]), dev(d["v_pages"])
+    bt, kl = dev(d["block_table"]), dev(d["kv_lens"])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], device="cuda")
+    maxlen = int(d["kv_lens"].max())
+    split = d.get("split_tokens", 0)
+    ws_bytes = attn.attn_decode_workspace_bytes(d["B"], d["Hq"], d["Hkv"], d["D"], maxlen, split)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        attn.attn_decode_paged(q, kp, vp, bt, kl, o, lse, max_kv_len=maxlen, scale=d["scale"],
+                               workspace=ws, split_tokens=split)
+
+    durs, span, _ = time_launches(step, steps, warmup)
+    nbytes = kv_bytes(d["kv_lens"], d["Hkv"], d["D"])
+    mean_ms = float(np.mean(durs))
+    split_used, nsplit = attn.attn_decode_plan(d["B"], d["Hkv"], maxlen, 0, split)
+    del kp, vp
+    return dict(workload=wl.WORKLOADS[n], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
+                mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
+                frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                split_tokens=split_used, max_splits=nsplit)
+
+
+def bench_cascade(steps, warmup):
+    c = wl.workload(5)
+    q = dev(c["q"])
+    kp, vp = dev(c["k_pages"]), dev(c["v_pages"])
+    pp, st, sl = dev(c["prefix_pages"]), dev(c["suffix_table"]), dev(c["suffix_lens"])
+    R, H, D = q.shape
+    o_p, o_s = torch.empty_like(q), torch.empty_like(q)
+    l_p, l_s = (torch.empty((R, H), device="cuda") for _ in range(2))
+    maxlen = int(c["suffix_lens"].max())
+    ws_p = torch.empty(max(1, attn.attn_shared_prefix_workspace_bytes(R, H, c["Hkv"], D,
+                                                                          c["prefix_len"])),
+                       dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(max(1, attn.attn_decode_workspace_bytes(R, H, c["Hkv"], D, maxlen)),
+                       dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def before(i):
+        flush.fill_(i & 0xFF)   # evict the last-level cache between repetitions
+
+    def step(i):
+        attn.attn_decode_shared_prefix(q, kp, vp, pp, c["prefix_len"], o_p, l_p, scale=c["scale"],
+                                       workspace=ws_p)
+        attn.attn_decode_paged(q, kp, vp, st, sl, o_s, l_s, max_kv_len=maxlen, scale=c["scale"],
+                               workspace=ws_s)
+        attn.attn_merge_states(o_p, l_p, o_s, l_s)
+
+    durs, span, _ = time_launches(step, steps, warmup, before=before)
+    nbytes = kv_bytes([c["prefix_len"]], c["Hkv"], D) + kv_bytes(c["suffix_lens"], c["Hkv"], D)
+    mean_ms = float(np.mean(durs))
+    return dict(workload=wl.WORKLOADS[5], kv_bytes=nbytes, mean_ms=mean_ms,
+                gbs=nbytes / (mean_ms * 1e-3) / 1e9,
+                frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+
+
+def cpu_baseline(target_s=15.0):
+    """The fp64 oracle on (b, h) pairs of the prefill workload, timed on the
+    host cores; throughput in the bench's unit (algorithmic causal TFLOP/s)."""
+    import oracle
+    inp = wl.workload(2)
+    T, D = 1024, 128
+    threads = oracle.default_threads()
+    pairs, flops, t_used = 0, 0.0, 0.0
+    t0 = time.perf_counter()
+    while t_used < target_s and pairs < 128:
+        n = max(1, min(threads, 128 - pairs))
+        idx = [(p // 32, p % 32) for p in range(pairs, pairs + n)]
+        q = np.stack([inp["q"][b, h] for b, h in idx])[:, None]
+        k = np.stack([inp["k"][b, h] for b, h in idx])[:, None]
+        v = np.stack([inp["v"][b, h] for b, h in idx])[:, None]
+        oracle.attention(q, k, v, True, inp["scale"], threads=threads)
+        pairs += n
+        flops += n * 4.0 * D * T * (T + 1) / 2
+        t_used = time.perf_counter() - t0
+    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{pairs} of 128 (b,h) pairs of the causal B4 H32 T1024 D128 prefill, "
+                       f"{t_used:.1f} s, fp64, full score matrix",
+                seconds=round(t_used, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    log("prefill B4 H32 T1024 D128 causal bf16 ...")
+    pre = bench_prefill(args.steps, args.warmup)
+    log(f"  {pre['tflops']:.1f} TFLOP/s, mean launch {pre['mean_launch_ms'] * 1e3:.1f} us")
+    decode = {}
+    if not args.prefill_only:
+        for n in (3, 4):
+            log(f"decode workload {n} ...")
+            decode[f"workload{n}"] = bench_decode(n, args.steps, args.warmup)
+            log(f"  {decode[f'workload{n}']['gbs']:.0f} GB/s")
+            torch.cuda.empty_cache()
+        log("cascade workload 5 ...")
+        decode["workload5"] = bench_cascade(args.steps, args.warmup)
+        log(f"  {decode['workload5']['gbs']:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle) ...")
+        cpu = cpu_baseline()
+        log(f"  {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "prefill attn TFLOP/s + decode attn KV GB/s, % of MI355X roofline",
+        "value": round(pre["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal prefill B4 H32 T1024 D128 bf16 (Llama2-7B attention "
+                               "shape), scale 1/sqrt(128), seeded N(0,1) inputs",
+                   "global_batch": 4, "seq_len": 1024, "heads": 32, "head_dim": 128},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+        "decode": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                       for kk, vv in v.items()} for k, v in decode.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

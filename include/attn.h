@@ -1,0 +1,227 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused-attention library, libattn.so.
+ *
+ * What every call computes is scaled-dot-product attention,
+ *
+ *     O = softmax(scale * Q K^T) V,        lse_i = ln sum_j exp(scale * q_i . k_j),
+ *
+ * as defined in "FlashInfer kernel library: accelerating cascade-inference
+ * attention with CUDA warp-level primitives" (zyxy.net/archives/24491),
+ * section 1: similarity of Q and K, softmax into a probability distribution,
+ * weighted sum with V.  The kernels compute it tile by tile with an online or
+ * partial softmax so the score matrix never reaches device memory (the tiled
+ * FlashAttention scheme in the xhh.club summary "fast attention kernels and
+ * operator fusion", section "FlashAttention and paged attention").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains them.  Scratch space (where needed)
+ *    is passed in by the caller as `workspace`.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL = the default stream).  Results are valid once the stream has
+ *    synchronised.  Nothing is launched when a call returns an error.
+ *  - Element types: ATTN_BF16 (bfloat16) or ATTN_F32 (IEEE float).  Scores,
+ *    softmax statistics and accumulators are always fp32.  lse is always
+ *    fp32, natural log of the scaled scores.
+ *  - Dense layouts are row-major with the last dimension contiguous.
+ *  - Grouped heads: query head h reads key/value head h / (heads_q / heads_kv)
+ *    (heads_q must be a multiple of heads_kv).
+ *  - Calls return an attn_status (0 = success).  No call prints, throws or
+ *    aborts.  Device-side data (block tables, kv_lens) is NOT validated: the
+ *    caller guarantees the preconditions stated per call.
+ *  - Supported: head_dim 64 or 128; page_size 16; scale finite and > 0
+ *    (ATTN_E_ARG otherwise).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_E_NULL = 1,        /* a required pointer is NULL                       */
+    ATTN_E_SHAPE = 2,       /* a size is negative or sizes are inconsistent     */
+    ATTN_E_UNSUPPORTED = 3, /* well-formed but not implemented (head_dim, ...)  */
+    ATTN_E_WORKSPACE = 4,   /* workspace missing or smaller than required       */
+    ATTN_E_HIP = 5,         /* the HIP runtime reported an error on launch      */
+    ATTN_E_ARG = 6          /* a value outside its domain (scale <= 0 or NaN)   */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+
+/* Text for a status code (static storage; never NULL). */
+const char *attn_status_str(int status);
+
+/*
+ * attn_prefill -- fused multi-head attention over dense Q, K, V.
+ *
+ * The FMHA of "TensorRT-LLM deep optimization: FMHA kernels on Hopper"
+ * (zyxy.net/?p=24414), section 2: score, softmax and weighted sum in one
+ * kernel, K/V tiles staged on chip, numerically stable softmax.
+ *
+ *   q, o : [batch, heads_q,  seq_q,  head_dim]   element type `dtype`
+ *   k, v : [batch, heads_kv, seq_kv, head_dim]   element type `dtype`
+ *   lse  : [batch, heads_q, seq_q] fp32, or NULL to skip it
+ *   causal != 0 masks key j for query i when j > i + (seq_kv - seq_q)
+ *            (bottom-right aligned; the usual mask when seq_q == seq_kv).
+ *            A query row with no visible key gets O = 0 and lse = -inf.
+ *   scale : multiplies Q K^T (1/sqrt(head_dim) for standard attention).
+ *
+ * Any of batch, seq_q, seq_kv may be 0 (nothing to do, or O = 0 rows).
+ * Errors: ATTN_E_NULL (q/k/v/o NULL with work to do), ATTN_E_SHAPE (negative
+ * sizes, heads_q % heads_kv != 0), ATTN_E_UNSUPPORTED (head_dim not 64/128,
+ * unknown dtype), ATTN_E_HIP.
+ */
+int attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int batch, int heads_q, int heads_kv, int seq_q, int seq_kv,
+                 int head_dim, int dtype, int causal, float scale, void *stream);
+
+/*
+ * Split-KV planning for paged decode.
+ *
+ * FlashDecoding splits the key/value length into independent partial
+ * softmax results that are combined at the end (FlashDecoding++ summary,
+ * wenjunhu.com/d/2311396.html, section 1); the chunk size is chosen from the
+ * batch size and the KV length (the per-shape kernel choice of the
+ * TensorRT-LLM FMHA page, section 3, and the heuristic dataflow of the
+ * FlashDecoding++ summary, section 5).
+ *
+ * attn_decode_plan: host-only.  Given the shape, the host-side upper bound
+ * max_kv_len and the device's compute-unit count (num_cus <= 0: 256),
+ * returns in *split_tokens the chunk length (a multiple of 64, at most 512)
+ * and in *max_splits the number of chunks of the longest sequence.
+ * requested_split > 0 forces that chunk length (rounded up to a multiple of
+ * 64).  Returns ATTN_OK or ATTN_E_SHAPE.
+ */
+int attn_decode_plan(int batch, int heads_kv, int max_kv_len, int num_cus,
+                     int requested_split, int *split_tokens, int *max_splits);
+
+/*
+ * Bytes of workspace attn_decode_paged needs for this shape (0 if none).
+ * split_tokens: 0 = the planner's choice, else as for attn_decode_plan.
+ */
+size_t attn_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int head_dim,
+                                   int max_kv_len, int split_tokens);
+
+/*
+ * attn_decode_paged -- one query token per sequence over a paged KV cache.
+ *
+ * Paged attention as in the xhh.club summary ("how does paged attention
+ * manage the KV cache"): the cache is cut into fixed-size blocks and a block
+ * table maps each sequence's logical blocks to physical ones; the kernel
+ * reads K and V through the table, so logical order is contiguous while the
+ * physical placement is arbitrary.
+ *
+ *   q, o        : [batch, heads_q, head_dim]                   `dtype` / `o_dtype`
+ *   k_pages,
+ *   v_pages     : [num_pages, heads_kv, page_size, head_dim]   `dtype`
+ *                 (each (page, kv head) tile is contiguous)
+ *   block_table : int32 [batch, max_pages_per_seq]; token t of sequence b is
+ *                 slot t % page_size of page block_table[b][t / page_size]
+ *   kv_lens     : int32 [batch]; sequence b's query attends exactly its
+ *                 kv_lens[b] cached tokens
+ *   lse         : fp32 [batch, heads_q], or NULL
+ *   max_kv_len  : host-side upper bound of kv_lens (plans the splits with no
+ *                 device-to-host copy)
+ *   workspace   : device memory of at least attn_decode_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0)
+ *
+ * Device-side preconditions (not checked): 0 <= kv_lens[b] <= max_kv_len
+ * (a larger value is clamped to max_kv_len, a negative one counts as 0) and
+ * the first ceil(kv_lens[b] / page_size) entries of row b are valid page
+ * indices.
+ * A sequence with kv_lens[b] == 0 gets O = 0 and lse = -inf.
+ * Page slots past kv_lens[b] are never used, whatever they hold.
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_UNSUPPORTED (page_size != 16,
+ * head_dim, dtype, heads_q / heads_kv not in {1,2,4,8}), ATTN_E_WORKSPACE,
+ * ATTN_E_HIP.
+ */
+int attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                      const int32_t *block_table, const int32_t *kv_lens,
+                      void *o, float *lse,
+                      int batch, int heads_q, int heads_kv, int head_dim,
+                      int page_size, int max_pages_per_seq, int max_kv_len,
+                      int dtype, int o_dtype, float scale,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Options of attn_decode_paged_ex (zero-initialise, then set what you need).
+ *   split_tokens : 0 = planner's choice; > 0 forces the chunk length.
+ */
+typedef struct {
+    int split_tokens;
+    int reserved[7];
+} attn_decode_opts;
+
+/* attn_decode_paged with options (opts may be NULL = defaults). */
+int attn_decode_paged_ex(const void *q, const void *k_pages, const void *v_pages,
+                         const int32_t *block_table, const int32_t *kv_lens,
+                         void *o, float *lse,
+                         int batch, int heads_q, int heads_kv, int head_dim,
+                         int page_size, int max_pages_per_seq, int max_kv_len,
+                         int dtype, int o_dtype, float scale,
+                         void *workspace, size_t workspace_bytes, void *stream,
+                         const attn_decode_opts *opts);
+
+/*
+ * attn_merge_states -- combine two partial attention states in place.
+ *
+ * (o_a, lse_a) and (o_b, lse_b) are attention results of the same query
+ * rows over two disjoint key sets; the result, written into (o_a, lse_a), is
+ * the attention over their union:
+ *     M = max(lse_a, lse_b),  w_x = exp(lse_x - M),
+ *     lse = M + ln(w_a + w_b),  o = (w_a o_a + w_b o_b) / (w_a + w_b).
+ * A side with lse = -inf is empty and contributes nothing (its o is ignored);
+ * two empty sides give o = 0, lse = -inf.  This is the "update all partial
+ * softmax results together at the end" step of FlashDecoding (FlashDecoding++
+ * summary, section 1) and the combining stage of cascade inference
+ * ("FlashInfer kernel library ...", section 4).
+ *
+ *   o_a, o_b   : [rows, head_dim], element type o_dtype (o_a is overwritten)
+ *   lse_a, lse_b : fp32 [rows] (lse_a is overwritten)
+ * o_b/lse_b may alias o_a/lse_a exactly (giving o, lse + ln 2).
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_UNSUPPORTED, ATTN_E_HIP.
+ */
+int attn_merge_states(void *o_a, float *lse_a, const void *o_b, const float *lse_b,
+                      int rows, int head_dim, int o_dtype, void *stream);
+
+/*
+ * attn_decode_shared_prefix -- stage one of shared-prefix cascade decode.
+ *
+ * All `batch` requests attend the same prefix of prefix_len tokens, stored
+ * once in the paged cache (prefix sharing of KV blocks, xhh.club summary,
+ * "paged attention"; the staged cascade of "FlashInfer kernel library ...",
+ * sections 2 and 4).  Each prefix page is read once per kv head for all
+ * requests.  Combine the result with each request's own suffix attention
+ * (attn_decode_paged over the suffix tables) using attn_merge_states.
+ *
+ *   q, o         : [batch, heads_q, head_dim]                 `dtype` / `o_dtype`
+ *   k_pages,
+ *   v_pages      : [num_pages, heads_kv, page_size, head_dim]  `dtype`
+ *   prefix_pages : int32 [ceil(prefix_len / page_size)] physical pages
+ *   lse          : fp32 [batch, heads_q], or NULL
+ *   workspace    : at least attn_shared_prefix_workspace_bytes(...) bytes
+ * prefix_len == 0 gives O = 0 and lse = -inf.  bf16 runs the MFMA prefix
+ * kernel; fp32 (the exactness test mode) runs the paged decode kernel with
+ * the one prefix table shared by every request.
+ */
+size_t attn_shared_prefix_workspace_bytes(int batch, int heads_q, int heads_kv, int head_dim,
+                                          int prefix_len, int dtype);
+int attn_decode_shared_prefix(const void *q, const void *k_pages, const void *v_pages,
+                              const int32_t *prefix_pages, int prefix_len,
+                              void *o, float *lse,
+                              int batch, int heads_q, int heads_kv, int head_dim,
+                              int page_size, int dtype, int o_dtype, float scale,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,166 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/attn.h declares, and its host-side checks reject bad arguments
+before anything is launched (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_tiled_fmha_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, E_NULL, E_SHAPE, E_UNSUP, E_WS, E_HIP, E_ARG = range(7)
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its checks
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.LIB_PATH):
+        from attention_tiled_fmha_amd import build
+        build.build()
+    return attn.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in attn.h but not exported"
+    assert set(names) == set(attn.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert attn.status_str(s) and attn.status_str(s) != "unknown status"
+    assert attn.status_str(99) == "unknown status"
+
+
+def prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=1, Hkv=1, Tq=8, Tk=8, D=64,
+             dt=0, causal=0, scale=0.125)
+    a.update(kw)
+    return lib.attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["Tq"], a["Tk"], a["D"], a["dt"], a["causal"], a["scale"], None)
+
+
+def test_prefill_checks(lib):
+    assert prefill(lib, q=None) == E_NULL
+    assert prefill(lib, o=None) == E_NULL
+    assert prefill(lib, k=None) == E_NULL
+    assert prefill(lib, B=-1) == E_SHAPE
+    assert prefill(lib, Tq=-3) == E_SHAPE
+    assert prefill(lib, Hq=4, Hkv=3) == E_SHAPE
+    assert prefill(lib, Hkv=0) == E_SHAPE
+    assert prefill(lib, D=96) == E_UNSUP
+    assert prefill(lib, dt=7) == E_UNSUP
+    assert prefill(lib, scale=0.0) == E_ARG
+    assert prefill(lib, scale=-1.0) == E_ARG
+    assert prefill(lib, scale=float("nan")) == E_ARG
+    assert prefill(lib, scale=float("inf")) == E_ARG
+    # nothing to do: no pointers needed, nothing launched
+    assert prefill(lib, B=0, q=None, k=None, v=None, o=None) == OK
+    assert prefill(lib, Tq=0, q=None, k=None, v=None, o=None) == OK
+
+
+def decode(lib, ws=None, ws_bytes=0, opts=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, kl=FAKE, o=FAKE, lse=None, B=2, Hq=8, Hkv=2,
+             D=128, page=16, maxp=4, maxlen=64, dt=0, odt=0, scale=0.1)
+    a.update(kw)
+    return lib.attn_decode_paged_ex(a["q"], a["k"], a["v"], a["bt"], a["kl"], a["o"], a["lse"],
+                                    a["B"], a["Hq"], a["Hkv"], a["D"], a["page"], a["maxp"],
+                                    a["maxlen"], a["dt"], a["odt"], a["scale"], ws, ws_bytes,
+                                    None, opts)
+
+
+def test_decode_checks(lib):
+    assert decode(lib, q=None) == E_NULL
+    assert decode(lib, bt=None) == E_NULL
+    assert decode(lib, kl=None) == E_NULL
+    assert decode(lib, Hq=6, Hkv=4) == E_SHAPE
+    assert decode(lib, maxp=3) == E_SHAPE            # 3 pages cannot hold 64 tokens
+    assert decode(lib, maxlen=-1) == E_SHAPE
+    assert decode(lib, page=32) == E_UNSUP
+    assert decode(lib, D=80) == E_UNSUP
+    assert decode(lib, Hq=32, Hkv=2) == E_UNSUP       # group of 16
+    assert decode(lib, odt=5) == E_UNSUP
+    assert decode(lib, scale=0.0) == E_ARG
+    opts = attn.DecodeOpts(split_tokens=-5)
+    assert decode(lib, opts=ctypes.byref(opts)) == E_ARG
+    # a long sequence needs a workspace for its partial states
+    need = lib.attn_decode_workspace_bytes(2, 8, 2, 128, 100000, 0)
+    assert need > 0
+    assert decode(lib, maxlen=100000, maxp=6250) == E_WS
+    assert decode(lib, maxlen=100000, maxp=6250, ws=FAKE, ws_bytes=need - 1) == E_WS
+    assert decode(lib, B=0, q=None, k=None, v=None, bt=None, kl=None, o=None) == OK
+
+
+def test_merge_checks(lib):
+    m = lambda **kw: lib.attn_merge_states(kw.get("oa", FAKE), kw.get("la", FAKE),
+                                           kw.get("ob", FAKE), kw.get("lb", FAKE),
+                                           kw.get("rows", 4), kw.get("D", 128),
+                                           kw.get("dt", 0), None)
+    assert m(oa=None) == E_NULL
+    assert m(lb=None) == E_NULL
+    assert m(rows=-1) == E_SHAPE
+    assert m(D=48) == E_UNSUP
+    assert m(dt=3) == E_UNSUP
+    assert m(rows=0, oa=None, la=None, ob=None, lb=None) == OK
+
+
+def test_shared_prefix_checks(lib):
+    f = lambda **kw: lib.attn_decode_shared_prefix(
+        kw.get("q", FAKE), FAKE, FAKE, kw.get("pp", FAKE), kw.get("plen", 64), FAKE, None,
+        kw.get("B", 4), kw.get("Hq", 4), kw.get("Hkv", 4), 128, kw.get("page", 16), 0, 0,
+        kw.get("scale", 0.1), None, 0, None)
+    assert f(q=None) == E_NULL
+    assert f(pp=None) == E_NULL
+    assert f(plen=-1) == E_SHAPE
+    assert f(page=8) == E_UNSUP
+    assert f(scale=-2.0) == E_ARG
+    assert f(B=0) == OK
+
+
+def test_decode_plan(lib):
+    # workload shapes: long contexts over many sequences get 512-token chunks
+    assert attn.attn_decode_plan(32, 32, 8192) == (512, 16)
+    assert attn.attn_decode_plan(128, 8, 32768) == (512, 64)
+    # a small batch gets short chunks, so there are enough workgroups
+    s, n = attn.attn_decode_plan(1, 8, 4096)
+    assert s == 64 and n == 64
+    assert attn.attn_decode_plan(1, 1, 0) == (64, 1)
+    # forced chunk lengths round up to a multiple of 64
+    assert attn.attn_decode_plan(4, 4, 1000, requested_split=100) == (128, 8)
+    for B, H, L in ((1, 1, 1), (3, 5, 777), (64, 32, 1024), (256, 8, 131072)):
+        s, n = attn.attn_decode_plan(B, H, L)
+        assert s % 64 == 0 and 64 <= s <= 512
+        assert (n - 1) * s < max(L, 1) <= n * s
+    with pytest.raises(attn.AttnError):
+        attn.attn_decode_plan(1, 0, 10)
+
+
+def test_workspace_bytes(lib):
+    assert attn.attn_decode_workspace_bytes(4, 8, 8, 128, 512, 512) == 0   # one chunk: none
+    assert attn.attn_decode_workspace_bytes(4, 8, 8, 128, 512) > 0        # small batch: split
+    B, Hq, D = 32, 32, 128
+    s, n = attn.attn_decode_plan(B, 32, 8192)
+    rows = B * Hq * n
+    expect = -(-rows * D * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert attn.attn_decode_workspace_bytes(B, Hq, 32, D, 8192) == expect
+
+
+def test_shared_prefix_workspace(lib):
+    # 64 requests x 32 heads over a 4096-token prefix: 16 chunks of 256 keys
+    n = attn.attn_shared_prefix_workspace_bytes(64, 32, 32, 128, 4096, 0)
+    rows = 64 * 32 * 16
+    assert n == -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert attn.attn_shared_prefix_workspace_bytes(64, 32, 32, 128, 0, 0) == 0
+    assert attn.attn_shared_prefix_workspace_bytes(64, 32, 5, 128, 4096, 0) == 0  # bad group

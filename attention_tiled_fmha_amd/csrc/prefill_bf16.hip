@@ -2,7 +2,7 @@
 //
 // Method: the fused, tiled attention of the TensorRT-LLM FMHA page
 // (zyxy.net/?p=24414, section 2: score, softmax and weighted sum fused in one
-// kernel, tiles staged on chip, bank-conflict-aware on-chip layout, stable
+// kernel, tiles staged on chip, a bank-conflict-free on-chip layout, stable
 // softmax) with the online softmax update of FlashAttention (FlashDecoding++
 // summary, wenjunhu.com/d/2311396.html, section 1), so the T x T score matrix
 // never leaves registers.  K/V tiles are double-buffered in LDS: the next
@@ -11,31 +11,42 @@
 //
 // gfx950 mapping
 // --------------
-// Workgroup = 4 wavefronts (one per SIMD) = BM = 256 query rows of one
-// (batch, head); each wavefront owns 64 rows as two 32-row blocks.  Per key
-// tile of BN = 32 keys:
+// A workgroup is 8 wavefronts = 256 query rows of one (batch, head); each
+// wavefront owns 32 rows.  Per key tile of BN = 32 keys a wavefront does
 //
-//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS (row-major),
-//                   B = Q held in VGPRs for the whole kernel.
-//   softmax         the accumulator of S^T gives lane l the scores of query
-//                   row (l % 32) for 16 of the 32 keys; the other 16 are in
-//                   lane l ^ 32.  Row max / sum are lane-local plus one
-//                   permlane32 swap -- no LDS, no cross-row shuffles.
-//   O^T += V^T P^T  A = V^T from LDS (V is transposed while it is written to
-//                   LDS), B = P: the S^T accumulator registers, rounded to
-//                   bf16, already sit in B-operand order.
+//   S^T = K Q^T     8 x v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q held in
+//                   VGPRs for the whole kernel.  Computing S^T rather than S
+//                   gives lane l the scores of query row l % 32 for 16 of the
+//                   32 keys (the other 16 sit in lane l ^ 32): row max and
+//                   row sum are lane-local plus one v_permlane32_swap.
+//   softmax         exp2 of the scaled scores against the running max, P
+//                   rounded to bf16 (already in B-operand order for PV).
+//   O^T += V^T P^T  8 MFMAs, A = V^T from LDS.
 //
-// The running max is only raised (and O, l rescaled) when a row's max grows
+// MFMA and VALU work of one wavefront do not overlap on gfx950; those of two
+// wavefronts on one SIMD do.  So the eight wavefronts form two groups (one
+// wavefront of each per SIMD) that run half a tile apart: while group 0
+// issues the MFMAs of tile t (PV of t-1, then S of t), group 1 runs the
+// softmax of tile t-1, and the other way round.  A workgroup barrier
+// separates the phases.  Each wavefront stays under 256 VGPRs (two per SIMD).
+//
+// LDS: K row-major with a 16-byte row pad (conflict-free 16-row reads, affine
+// addresses).  V is transposed while it is written (V^T: one row per head
+// dimension) with the keys of each 16-key group ordered so that the 8 keys
+// one MFMA lane needs are 16 contiguous bytes; the 80-byte V^T row stride
+// makes the 16-row reads conflict-free.
+//
+// The running max is raised (and O, l rescaled) only when a row's max grows
 // by more than 2^8; otherwise exponentials are taken against the stale max.
 // Results are identical in exact arithmetic (numerator and denominator share
-// the same reference), and every exponential stays <= 2^8, so nothing
-// overflows in fp32.  The row sum l adds up the bf16-rounded P that the MFMA
-// multiplies with V, so numerator and denominator see the same weights.
+// the reference) and every exponential stays <= 2^8.  The row sum adds the
+// bf16-rounded P that the MFMA multiplies with V.
 //
-// Causal masking (key j visible to query i iff j <= i + Tk - Tq) costs only
-// on tiles that cross the diagonal; tiles wholly above it are skipped per
-// wavefront.  Workgroups are issued heaviest (longest key range) first, and
-// all query tiles of one (b, h) land on one XCD so K/V reuse stays in its L2.
+// Causal masking (key j visible to query i iff j <= i + Tk - Tq) is applied
+// only on tiles that cross the diagonal; tiles wholly above a wavefront's
+// rows are skipped.  Workgroups are issued heaviest (longest key range)
+// first, and all query tiles of one (b, h) land on one XCD so their shared
+// K/V stay in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,90 +54,109 @@ namespace attn {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kIB = 2;                      // 32-row blocks per wavefront
-constexpr int kBM = kWaves * kIB * 32;      // 256 query rows per workgroup
-constexpr int kBN = 32;                     // keys per tile
-constexpr float kRescaleThresh = 8.0f;      // log2 units
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBM = kWaves * 32;         // 256 query rows per workgroup
+constexpr int kBN = 32;                  // keys per tile
+constexpr float kRescaleThresh = 8.0f;   // log2 units
 
 template <int D>
 struct Cfg {
-    static constexpr int KS = D / 16;             // MFMA k-steps of Q K^T
-    static constexpr int DB = D / 32;             // 32-wide column blocks of O^T
-    static constexpr int PS = kBN / 16;           // MFMA k-steps of P V
-    static constexpr int KST = D + 8;             // K row stride in LDS (bf16)
-    static constexpr int VST = kBN + 4;           // V^T row stride in LDS (bf16)
-    static constexpr int K_ELEMS = kBN * KST;
-    static constexpr int V_ELEMS = D * VST;
-    // global -> register staging of one tile
-    static constexpr int K_CHUNKS = D / 8;                      // 16-byte chunks per key row
-    static constexpr int K_PASSES = kBN * K_CHUNKS / 256;       // 16-byte loads per lane
-    static constexpr int V_UNITS = (kBN / 4) * (D / 4);         // 4 keys x 4 dims units
+    static constexpr int KS = D / 16;                    // MFMA k-steps of K Q^T
+    static constexpr int DB = D / 32;                    // 32-row blocks of O^T (dims)
+    static constexpr int CPR = D / 8;                    // 16-byte chunks per K row
+    static constexpr int K_STRIDE = D * 2 + 16;          // K row + 16-byte pad
+    static constexpr int K_BYTES = kBN * K_STRIDE;
+    static constexpr int VT_STRIDE = kBN * 2 + 16;       // V^T row (32 keys) + pad
+    static constexpr int V_BYTES = D * VT_STRIDE;
+    static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+    static constexpr int K_CHUNKS = kBN * CPR;           // 16-byte chunks per K tile
+    static constexpr int V_UNITS = (kBN / 4) * (D / 2);  // 4-key x 2-dim V units
 };
 
-template <int D>
-struct TileRegs {
-    u32x4 k[Cfg<D>::K_PASSES];
-    u32x2 v[4];
+// V^T position of key k (0..31) in its row: in each 16-key group the 4-key
+// blocks 1 and 2 trade places, so keys 16s + {0..3, 8..11} (MFMA lanes 0-31)
+// and 16s + {4..7, 12..15} (lanes 32-63) are each contiguous.
+__device__ __forceinline__ int vt_pos(int key) {
+    const int a = (key >> 2) & 3;
+    return (key & ~15) | ((((a & 1) << 1) | (a >> 1)) << 2) | (key & 3);
+}
+
+// One thread's share of a tile in flight: a 16-byte K chunk and a 4-key x
+// 2-dim V unit (4 dwords).
+struct Stage {
+    u32x4 k;
+    u32x4 v;
 };
 
-// Fetch one K/V tile (keys k0 .. k0+kBN-1) into registers; rows >= Tk are 0.
+// K of the tile at key k0k, V of the tile at key k0v.  Rows past Tk are
+// clamped to row Tk - 1 (valid memory): their K scores are masked to -inf and
+// their V rows meet P = 0, so they never change a result.  The clamp is only
+// evaluated on a tile that crosses Tk (a scalar branch).
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& t, const uint16_t* __restrict__ kp,
-                                          const uint16_t* __restrict__ vp, int k0, int Tk,
-                                          int tid) {
+__device__ __forceinline__ void load_stage(Stage& st, const uint16_t* __restrict__ kp,
+                                           const uint16_t* __restrict__ vp, int k0k, int k0v,
+                                           int Tk, int tid, bool do_k, bool do_v) {
     using C = Cfg<D>;
-#pragma unroll
-    for (int i = 0; i < C::K_PASSES; i++) {
-        const int e = tid + 256 * i;
-        const int row = e / C::K_CHUNKS, ch = e % C::K_CHUNKS;
-        t.k[i] = (k0 + row < Tk) ? *(const u32x4*)(kp + (size_t)(k0 + row) * D + 8 * ch)
-                                 : u32x4{0, 0, 0, 0};
+    if (do_k && tid < C::K_CHUNKS) {
+        const int row = tid / C::CPR, ch = tid % C::CPR;
+        const int r = (k0k + kBN <= Tk) ? k0k + row : min(k0k + row, Tk - 1);
+        st.k = *(const u32x4*)(kp + (size_t)r * D + 8 * ch);
     }
-    if (tid < C::V_UNITS) {
-        const int dg = tid % (D / 4), kg = tid / (D / 4);
+    if (do_v && tid < C::V_UNITS) {
+        const int dp = tid % (D / 2), kb4 = tid / (D / 2);   // dims 2dp, 2dp+1; keys 4kb4..+3
+        if (k0v + kBN <= Tk) {
+            const uint16_t* base = vp + (size_t)(k0v + 4 * kb4) * D + 2 * dp;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int row = k0 + 4 * kg + j;
-            t.v[j] = (row < Tk) ? *(const u32x2*)(vp + (size_t)row * D + 4 * dg) : u32x2{0, 0};
+            for (int j = 0; j < 4; j++) st.v[j] = *(const uint32_t*)(base + j * D);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                st.v[j] = *(const uint32_t*)(vp + (size_t)min(k0v + 4 * kb4 + j, Tk - 1) * D + 2 * dp);
         }
     }
 }
 
-// Write a staged tile to LDS: K row-major, V transposed (V^T[d][key]).
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& t, uint16_t* sK, uint16_t* sV,
-                                           int tid) {
+__device__ __forceinline__ void store_stage(const Stage& st, unsigned char* kbuf,
+                                            unsigned char* vbuf, int tid, bool do_k, bool do_v) {
     using C = Cfg<D>;
-#pragma unroll
-    for (int i = 0; i < C::K_PASSES; i++) {
-        const int e = tid + 256 * i;
-        const int row = e / C::K_CHUNKS, ch = e % C::K_CHUNKS;
-        *(u32x4*)(sK + row * C::KST + 8 * ch) = t.k[i];
+    if (do_k && tid < C::K_CHUNKS) {
+        const int row = tid / C::CPR, ch = tid % C::CPR;
+        *(u32x4*)(kbuf + row * C::K_STRIDE + 16 * ch) = st.k;
     }
-    if (tid < C::V_UNITS) {
-        const int dg = tid % (D / 4), kg = tid / (D / 4);
-        // t.v[j] holds dims 4dg..4dg+3 of key 4kg+j; V^T[d][4kg..4kg+3] per dim
-        u32x2 tr[4];
-        transpose4x4_bf16(t.v, tr);
-#pragma unroll
-        for (int i = 0; i < 4; i++) *(u32x2*)(sV + (4 * dg + i) * C::VST + 4 * kg) = tr[i];
+    if (do_v && tid < C::V_UNITS) {
+        const int dp = tid % (D / 2), kb4 = tid / (D / 2);
+        // st.v[j] = (dim 2dp, dim 2dp+1) of key 4kb4 + j -> two V^T rows of 4 keys
+        const uint32_t v0 = st.v[0], v1 = st.v[1], v2 = st.v[2], v3 = st.v[3];
+        const uint32_t e01 = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
+        const uint32_t e23 = __builtin_amdgcn_perm(v3, v2, 0x05040100u);
+        const uint32_t o01 = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
+        const uint32_t o23 = __builtin_amdgcn_perm(v3, v2, 0x07060302u);
+        unsigned char* row = vbuf + C::K_BYTES + (2 * dp) * C::VT_STRIDE + vt_pos(4 * kb4) * 2;
+        *(u32x2*)row = u32x2{e01, e23};
+        *(u32x2*)(row + C::VT_STRIDE) = u32x2{o01, o23};
     }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                          float* __restrict__ lse, int BH, int Hq, int Hkv, int Tq, int Tk,
                          int n_qtiles, float scale_log2) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][C::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][C::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF_BYTES];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
     const int li = lane & 31, hi = lane >> 5;
+    // Wavefront w runs on SIMD w % 4; group 1 (waves 4-7) runs one phase
+    // behind group 0.  Row blocks alternate between the groups so both see
+    // the same share of the causal diagonal.
+    const int grp = wave >> 2;
+    const int rb = 2 * (wave & 3) + grp;
 
     // Heaviest query tiles first; bh = id % BH keeps one (b, h) on one XCD
     // when BH is a multiple of 8 (workgroups are dealt to XCDs round-robin).
@@ -135,163 +165,182 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int qt = n_qtiles - 1 - id / BH;
     const int b = bh / Hq, h = bh % Hq, kvh = h / (Hq / Hkv);
     const int q0 = qt * kBM;
-    const int qw0 = q0 + wave * (kIB * 32);  // first row of this wavefront
+    const int qw0 = q0 + rb * 32;        // this wavefront's first row
+    const int qrow = qw0 + li;           // the query row of this lane
     const int diag = Tk - Tq;
 
     const uint16_t* qp = q + (size_t)bh * Tq * D;
     const uint16_t* kp = k + (size_t)(b * Hkv + kvh) * Tk * D;
     const uint16_t* vp = v + (size_t)(b * Hkv + kvh) * Tk * D;
 
-    // Q fragments (B operand of S^T = K Q^T): row li of each block, dims
-    // 16s + 8hi .. +7.
-    bf16x8 qf[kIB][C::KS];
-#pragma unroll
-    for (int ib = 0; ib < kIB; ib++) {
-        const int row = qw0 + ib * 32 + li;
+    // Q fragments (B operand of S^T = K Q^T): row qrow, dims 16s + 8hi .. +7.
+    // Loaded unconditionally (clamped row, zeroed past Tq) so that no
+    // exec-masked load is pending when the main loop starts.
+    bf16x8 qf[C::KS];
+    {
+        const int qr = min(qrow, max(Tq - 1, 0));
 #pragma unroll
         for (int s = 0; s < C::KS; s++) {
-            u32x4 w = (row < Tq) ? *(const u32x4*)(qp + (size_t)row * D + 16 * s + 8 * hi)
-                                 : u32x4{0, 0, 0, 0};
-            qf[ib][s] = __builtin_bit_cast(bf16x8, w);
+            u32x4 w = *(const u32x4*)(qp + (size_t)qr * D + 16 * s + 8 * hi);
+            if (qrow >= Tq) w = u32x4{0, 0, 0, 0};
+            qf[s] = __builtin_bit_cast(bf16x8, w);
         }
     }
 
-    // Key range of the workgroup and of this wavefront.
-    int kend = Tk;
-    if (CAUSAL) kend = max(0, min(Tk, q0 + kBM + diag));
-    int kend_w = Tk;
-    if (CAUSAL) kend_w = max(0, min(Tk, qw0 + kIB * 32 + diag));
+    // key range of the workgroup and of this wavefront
+    int kend = Tk, kend_w = Tk;
+    if (CAUSAL) {
+        kend = max(0, min(Tk, q0 + kBM + diag));
+        kend_w = max(0, min(Tk, qw0 + 32 + diag));
+    }
     const int n_tiles = (kend + kBN - 1) / kBN;
+    const int n_tiles_w = (kend_w + kBN - 1) / kBN;   // tiles with a visible key for this wavefront
 
-    f32x16 oacc[kIB][C::DB];
+    f32x16 oacc[C::DB];
 #pragma unroll
-    for (int ib = 0; ib < kIB; ib++)
+    for (int db = 0; db < C::DB; db++)
 #pragma unroll
-        for (int db = 0; db < C::DB; db++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) oacc[ib][db][r] = 0.f;
-    float m_run[kIB], l_run[kIB];
-#pragma unroll
-    for (int ib = 0; ib < kIB; ib++) {
-        m_run[ib] = -INFINITY;
-        l_run[ib] = 0.f;
-    }
+        for (int r = 0; r < 16; r++) oacc[db][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 sacc;
+    bf16x8 pf[2];
 
-    TileRegs<D> stage;
+    // Global phase p: group 0 runs its MFMA step t at p = 2t and its softmax
+    // step t at p = 2t + 1; group 1 runs each one phase later.  K(t) lives in
+    // buffer t % 2 during phases 2t and 2t+1 (the two groups' S(t)); V(t)
+    // lives in buffer t % 2 during phases 2t+2 and 2t+3 (their PV(t)).  The
+    // pair (K(t+1), V(t)) is loaded into register stage t % 2 at the start of
+    // phase 2t - 2 and written to LDS at the end of phase 2t + 1, so every
+    // load has four phases to arrive.
+    Stage st0, st1;
     if (n_tiles > 0) {
-        load_tile<D>(stage, kp, vp, 0, Tk, tid);
-        store_tile<D>(stage, sK[0], sV[0], tid);
+        load_stage<D>(st0, kp, vp, 0, 0, Tk, tid, true, false);
+        store_stage<D>(st0, smem, smem, tid, true, false);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // Q and the first K tile have landed
+
+    auto load_pair = [&](Stage& st, int t) {  // K(t+1), V(t)
+        if (t < n_tiles)
+            load_stage<D>(st, kp, vp, (t + 1) * kBN, t * kBN, Tk, tid, t + 1 < n_tiles, true);
+    };
+    auto store_pair = [&](const Stage& st, int t) {
+        if (t < n_tiles)
+            store_stage<D>(st, smem + ((t + 1) & 1) * C::BUF_BYTES, smem + (t & 1) * C::BUF_BYTES,
+                           tid, t + 1 < n_tiles, true);
+    };
+    load_pair(st0, 0);
     __syncthreads();
-
-    for (int kt = 0; kt < n_tiles; kt++) {
-        const int buf = kt & 1;
-        const int k0 = kt * kBN;
-        if (kt + 1 < n_tiles) load_tile<D>(stage, kp, vp, k0 + kBN, Tk, tid);
-
-        if (k0 < kend_w) {  // wavefront-uniform: some key of the tile is visible
-            const uint16_t* tK = sK[buf];
-            const uint16_t* tV = sV[buf];
-            // ---- S^T = K Q^T ------------------------------------------------
-            f32x16 sacc[kIB];
-#pragma unroll
-            for (int ib = 0; ib < kIB; ib++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) sacc[ib][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < C::KS; s++) {
-                const bf16x8 kf = *(const bf16x8*)(tK + li * C::KST + 16 * s + 8 * hi);
-#pragma unroll
-                for (int ib = 0; ib < kIB; ib++)
-                    sacc[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ib][s], sacc[ib],
-                                                                       0, 0, 0);
-            }
-            // ---- mask, online softmax ----------------------------------------
-            // sacc[ib][r] is the score of key k0 + 8(r/4) + 4hi + r%4 for
-            // query row qw0 + 32ib + li.
-            const bool need_mask = (k0 + kBN > Tk) || (CAUSAL && k0 + kBN - 1 > qw0 + diag);
-            bf16x8 pf[kIB][C::PS];
-#pragma unroll
-            for (int ib = 0; ib < kIB; ib++) {
-                if (need_mask) {
-                    const int qi = qw0 + ib * 32 + li;
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int kj = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        const bool vis = kj < Tk && (!CAUSAL || kj <= qi + diag);
-                        if (!vis) sacc[ib][r] = -INFINITY;
-                    }
-                }
-                float mx = sacc[ib][0];
-#pragma unroll
-                for (int r = 1; r < 16; r++) mx = fmaxf(mx, sacc[ib][r]);
-                mx = half_swap_max(mx) * scale_log2;
-                const float m_new = fmaxf(m_run[ib], mx);
-                if (__builtin_amdgcn_ballot_w64(m_new > m_run[ib] + kRescaleThresh)) {
-                    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[ib] - m_new);
-                    l_run[ib] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < C::DB; db++) oacc[ib][db] *= alpha;
-                    m_run[ib] = m_new;
-                }
-                const float m_eff = (m_run[ib] == -INFINITY) ? 0.f : m_run[ib];
-#pragma unroll
-                for (int ps = 0; ps < C::PS; ps++) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const float p0 = fast_exp2(__builtin_fmaf(sacc[ib][8 * ps + 2 * e], scale_log2, -m_eff));
-                        const float p1 = fast_exp2(__builtin_fmaf(sacc[ib][8 * ps + 2 * e + 1], scale_log2, -m_eff));
-                        w[e] = pack_bf16x2(p0, p1);
-                        l_run[ib] = __builtin_amdgcn_fdot2_f32_bf16(
-                            __builtin_bit_cast(bf16x2, w[e]),
-                            __builtin_bit_cast(bf16x2, 0x3f803f80u), l_run[ib], false);
-                    }
-                    pf[ib][ps] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-                }
-            }
-            // ---- O^T += V^T P^T -------------------------------------------------
-#pragma unroll
-            for (int ps = 0; ps < C::PS; ps++) {
-#pragma unroll
-                for (int db = 0; db < C::DB; db++) {
-                    const uint16_t* vrow = tV + (32 * db + li) * C::VST + 16 * ps + 4 * hi;
-                    const u32x2 lo = *(const u32x2*)(vrow);
-                    const u32x2 hi8 = *(const u32x2*)(vrow + 8);
-                    const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi8[0], hi8[1]});
-#pragma unroll
-                    for (int ib = 0; ib < kIB; ib++)
-                        oacc[ib][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ib][ps],
-                                                                               oacc[ib][db], 0, 0, 0);
-                }
-            }
-        }
-
-        if (kt + 1 < n_tiles) store_tile<D>(stage, sK[buf ^ 1], sV[buf ^ 1], tid);
+    if (grp == 1) {  // phase 0: group 0 computes S(0); group 1 only loads
+        load_pair(st1, 1);
         __syncthreads();
     }
 
-    // ---- epilogue: O = O / l, lse = m ln2 + ln l ----------------------------
+    // cur = stage t % 2 (pair t), nxt = stage (t + 1) % 2 (pair t + 1)
+    auto step = [&](int t, Stage& cur, Stage& nxt) {
+        // ---- MFMA step t (phase 2t for group 0, 2t+1 for group 1):
+        //      O^T += V^T P^T for tile t-1 and S^T = K Q^T for tile t.  All 16
+        //      LDS operands are requested before the first MFMA.
+        if (grp == 0) load_pair(nxt, t + 1);
+        const bool do_pv = t >= 1 && t - 1 < n_tiles_w;
+        const bool do_s = t < n_tiles_w;
+        bf16x8 vf[2][C::DB], kf[C::KS];
+        if (do_pv) {
+            // V^T rows 32db + li; keys key(hi, 0..7) of step ps at positions 16ps + 8hi
+            const unsigned char* sV = smem + ((t - 1) & 1) * C::BUF_BYTES + C::K_BYTES +
+                                      li * C::VT_STRIDE + 16 * hi;
 #pragma unroll
-    for (int ib = 0; ib < kIB; ib++) {
-        const int row = qw0 + ib * 32 + li;
-        const float l_tot = half_swap_sum(l_run[ib]);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (row < Tq) {
-            uint16_t* op = o + ((size_t)bh * Tq + row) * D;
+            for (int ps = 0; ps < 2; ps++)
 #pragma unroll
-            for (int db = 0; db < C::DB; db++)
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    const int d0 = 32 * db + 8 * g + 4 * hi;
-                    *(u32x2*)(op + d0) = u32x2{
-                        pack_bf16x2(oacc[ib][db][4 * g] * inv, oacc[ib][db][4 * g + 1] * inv),
-                        pack_bf16x2(oacc[ib][db][4 * g + 2] * inv, oacc[ib][db][4 * g + 3] * inv)};
-                }
-            if (lse && hi == 0)
-                lse[(size_t)bh * Tq + row] =
-                    l_tot > 0.f ? (m_run[ib] + __log2f(l_tot)) * kLn2 : -INFINITY;
+                for (int db = 0; db < C::DB; db++)
+                    vf[ps][db] = *(const bf16x8*)(sV + 32 * db * C::VT_STRIDE + 32 * ps);
         }
+        if (do_s) {
+            const unsigned char* sK = smem + (t & 1) * C::BUF_BYTES + li * C::K_STRIDE + 16 * hi;
+#pragma unroll
+            for (int s = 0; s < C::KS; s++) kf[s] = *(const bf16x8*)(sK + 32 * s);
+        }
+        if (do_pv) {
+#pragma unroll
+            for (int ps = 0; ps < 2; ps++)
+#pragma unroll
+                for (int db = 0; db < C::DB; db++)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ps][db], pf[ps], oacc[db],
+                                                                       0, 0, 0);
+        }
+        if (do_s) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+            for (int s = 1; s < C::KS; s++)
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+        }
+        if (grp == 1) store_pair(cur, t);
+        __syncthreads();
+
+        // ---- softmax step t (phase 2t+1 for group 0, 2t+2 for group 1)
+        if (grp == 1) load_pair(cur, t + 2);
+        if (t < n_tiles_w) {
+            const int k0 = t * kBN;
+            // sacc[r] is the score of key k0 + 8(r/4) + 4hi + r%4
+            if (k0 + kBN > Tk || (CAUSAL && k0 + kBN - 1 > qw0 + diag)) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int kj = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (kj >= Tk || (CAUSAL && kj > qrow + diag)) sacc[r] = -INFINITY;
+                }
+            }
+            float mx = sacc[0];
+#pragma unroll
+            for (int r = 1; r < 16; r++) mx = fmaxf(mx, sacc[r]);
+            mx = half_swap_max(mx);
+            mx = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
+            const float m_new = fmaxf(m_run, mx);
+            if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThresh)) {
+                const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < C::DB; db++) oacc[db] *= alpha;
+                m_run = m_new;
+            }
+            const float m_eff = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+            for (int ps = 0; ps < 2; ps++) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const float p0 = fast_exp2(__builtin_fmaf(sacc[8 * ps + 2 * e], scale_log2, -m_eff));
+                    const float p1 = fast_exp2(__builtin_fmaf(sacc[8 * ps + 2 * e + 1], scale_log2, -m_eff));
+                    w[e] = pack_bf16x2(p0, p1);
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]),
+                                                            __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                                            l_run, false);
+                }
+                pf[ps] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+            }
+        }
+        if (grp == 0) store_pair(cur, t);
+        __syncthreads();
+    };
+    for (int t = 0; t <= n_tiles; t += 2) {
+        step(t, st0, st1);
+        if (t + 1 <= n_tiles) step(t + 1, st1, st0);
+    }
+    if (grp == 0) __syncthreads();  // group 1's last phase
+
+    // ---- epilogue: O = O / l, lse = m ln2 + ln l ----------------------------
+    const float l_tot = half_swap_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < Tq) {
+        uint16_t* op = o + ((size_t)bh * Tq + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; db++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int d0 = 32 * db + 8 * g + 4 * hi;
+                *(u32x2*)(op + d0) = u32x2{pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                                           pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+            }
+        if (lse && hi == 0)
+            lse[(size_t)bh * Tq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 
@@ -305,9 +354,9 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
     const dim3 grid(BH * n_qtiles);
     const float sl2 = scale * kLog2e;
     auto go = [&](auto kern) {
-        kern<<<grid, 256, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k,
-                                       (const uint16_t*)v, (uint16_t*)o, lse, BH, Hq, Hkv, Tq,
-                                       Tk, n_qtiles, sl2);
+        kern<<<grid, kThreads, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k,
+                                            (const uint16_t*)v, (uint16_t*)o, lse, BH, Hq, Hkv,
+                                            Tq, Tk, n_qtiles, sl2);
     };
     if (D == 64)
         causal ? go(prefill_bf16_kernel<64, true>) : go(prefill_bf16_kernel<64, false>);

@@ -47,6 +47,8 @@
 // rows are skipped.  Workgroups are issued heaviest (longest key range)
 // first, and all query tiles of one (b, h) land on one XCD so their shared
 // K/V stay in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -89,32 +91,41 @@ struct Stage {
     u32x4 v;
 };
 
-// K of the tile at key k0k, V of the tile at key k0v.  Rows past Tk are
-// clamped to row Tk - 1 (valid memory): their K scores are masked to -inf and
-// their V rows meet P = 0, so they never change a result.  The clamp is only
-// evaluated on a tile that crosses Tk (a scalar branch).
+// Raw buffer resource over the rows [k0, min(k0 + kBN, Tk)) of one (b, h) K or
+// V slice.  Buffer loads past its end return 0 without touching memory, so
+// tail tiles, tiles past the key range and the idle threads of D = 64 need no
+// branch and no address clamp; the descriptor is built with scalar ALU only.
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data, no swizzle
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int k0, int Tk) {
+    // (the clamp lowers to a vector op; readfirstlane keeps the descriptor scalar)
+    const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(kBN, Tk - k0)) * D * 2);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * D), (short)0, bytes,
+                                             kRsrcWord3);
+}
+
+// Byte offsets of this thread's K chunk and V unit inside a tile (fixed for
+// the whole kernel).  Threads past the tile's chunk count land past the
+// descriptor's end and read zeros.
+template <int D>
+struct LoadOffsets {
+    int k, v;
+    __device__ explicit LoadOffsets(int tid) {
+        constexpr int CPR = Cfg<D>::CPR;
+        k = (tid / CPR) * D * 2 + 16 * (tid % CPR);
+        v = 4 * (tid / (D / 2)) * D * 2 + 4 * (tid % (D / 2));   // keys 4kb4.., dims 2dp, 2dp+1
+    }
+};
+
 template <int D>
 __device__ __forceinline__ void load_stage(Stage& st, const uint16_t* __restrict__ kp,
                                            const uint16_t* __restrict__ vp, int k0k, int k0v,
-                                           int Tk, int tid, bool do_k, bool do_v) {
-    using C = Cfg<D>;
-    if (do_k && tid < C::K_CHUNKS) {
-        const int row = tid / C::CPR, ch = tid % C::CPR;
-        const int r = (k0k + kBN <= Tk) ? k0k + row : min(k0k + row, Tk - 1);
-        st.k = *(const u32x4*)(kp + (size_t)r * D + 8 * ch);
-    }
-    if (do_v && tid < C::V_UNITS) {
-        const int dp = tid % (D / 2), kb4 = tid / (D / 2);   // dims 2dp, 2dp+1; keys 4kb4..+3
-        if (k0v + kBN <= Tk) {
-            const uint16_t* base = vp + (size_t)(k0v + 4 * kb4) * D + 2 * dp;
+                                           int Tk, const LoadOffsets<D>& off) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kp, k0k, Tk);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vp, k0v, Tk);
+    st.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k, 0, 0);
 #pragma unroll
-            for (int j = 0; j < 4; j++) st.v[j] = *(const uint32_t*)(base + j * D);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                st.v[j] = *(const uint32_t*)(vp + (size_t)min(k0v + 4 * kb4 + j, Tk - 1) * D + 2 * dp);
-        }
-    }
+    for (int j = 0; j < 4; j++) st.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, off.v + j * D * 2, 0, 0);
 }
 
 template <int D>
@@ -212,72 +223,71 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     // pair (K(t+1), V(t)) is loaded into register stage t % 2 at the start of
     // phase 2t - 2 and written to LDS at the end of phase 2t + 1, so every
     // load has four phases to arrive.
+    // PV at t = 0 multiplies P = 0 with the V region of buffer 1: zero both so
+    // that it adds exact zeros.
+    pf[0] = pf[1] = bf16x8{};
+    for (int i = tid; i < C::V_BYTES / 16; i += kThreads)
+        *(u32x4*)(smem + C::BUF_BYTES + C::K_BYTES + 16 * i) = u32x4{0, 0, 0, 0};
+    const LoadOffsets<D> off(tid);
     Stage st0, st1;
-    if (n_tiles > 0) {
-        load_stage<D>(st0, kp, vp, 0, 0, Tk, tid, true, false);
-        store_stage<D>(st0, smem, smem, tid, true, false);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // Q and the first K tile have landed
-
     auto load_pair = [&](Stage& st, int t) {  // K(t+1), V(t)
-        if (t < n_tiles)
-            load_stage<D>(st, kp, vp, (t + 1) * kBN, t * kBN, Tk, tid, t + 1 < n_tiles, true);
+        load_stage<D>(st, kp, vp, (t + 1) * kBN, t * kBN, Tk, off);
     };
     auto store_pair = [&](const Stage& st, int t) {
         if (t < n_tiles)
             store_stage<D>(st, smem + ((t + 1) & 1) * C::BUF_BYTES, smem + (t & 1) * C::BUF_BYTES,
                            tid, t + 1 < n_tiles, true);
     };
+    if (n_tiles > 0) {
+        load_stage<D>(st0, kp, vp, 0, 0, Tk, off);
+        store_stage<D>(st0, smem, smem, tid, true, false);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // Q and the first K tile have landed
     load_pair(st0, 0);
     __syncthreads();
-    if (grp == 1) {  // phase 0: group 0 computes S(0); group 1 only loads
-        load_pair(st1, 1);
-        __syncthreads();
-    }
 
-    // cur = stage t % 2 (pair t), nxt = stage (t + 1) % 2 (pair t + 1)
-    auto step = [&](int t, Stage& cur, Stage& nxt) {
+    // One step t of group G: its MFMA phase, then its softmax phase.  Every
+    // global load is unconditional, so the wait before each LDS store covers
+    // only the stage being stored, not the loads issued after it.
+    // cur = stage t % 2 (pair t), nxt = stage (t + 1) % 2 (pair t + 1).
+    auto step = [&](int t, Stage& cur, Stage& nxt, auto G) {
+        constexpr int g = decltype(G)::value;
         // ---- MFMA step t (phase 2t for group 0, 2t+1 for group 1):
-        //      O^T += V^T P^T for tile t-1 and S^T = K Q^T for tile t.  All 16
-        //      LDS operands are requested before the first MFMA.
-        if (grp == 0) load_pair(nxt, t + 1);
-        const bool do_pv = t >= 1 && t - 1 < n_tiles_w;
-        const bool do_s = t < n_tiles_w;
-        bf16x8 vf[2][C::DB], kf[C::KS];
-        if (do_pv) {
-            // V^T rows 32db + li; keys key(hi, 0..7) of step ps at positions 16ps + 8hi
+        //      O^T += V^T P^T for tile t-1 and S^T = K Q^T for tile t.
+        if (g == 0) load_pair(nxt, t + 1);
+        if (t <= n_tiles_w) {
+            // All 16 LDS operands are requested first, V and K alternating in
+            // the order the MFMAs consume them; PV(t-1) and S(t) MFMAs then
+            // alternate too, so each waits only for its own operand and the S
+            // chain's dependences are covered by PV MFMAs.  At t = 0 PV adds
+            // P = 0 times the zeroed V buffer; at t = n_tiles_w S is computed
+            // and not used.
+            bf16x8 vf[C::KS], kf[C::KS];
             const unsigned char* sV = smem + ((t - 1) & 1) * C::BUF_BYTES + C::K_BYTES +
                                       li * C::VT_STRIDE + 16 * hi;
-#pragma unroll
-            for (int ps = 0; ps < 2; ps++)
-#pragma unroll
-                for (int db = 0; db < C::DB; db++)
-                    vf[ps][db] = *(const bf16x8*)(sV + 32 * db * C::VT_STRIDE + 32 * ps);
-        }
-        if (do_s) {
             const unsigned char* sK = smem + (t & 1) * C::BUF_BYTES + li * C::K_STRIDE + 16 * hi;
 #pragma unroll
-            for (int s = 0; s < C::KS; s++) kf[s] = *(const bf16x8*)(sK + 32 * s);
-        }
-        if (do_pv) {
+            for (int s = 0; s < C::KS; s++) {
+                // V^T rows 32db + li; keys key(hi, 0..7) of step ps at positions 16ps + 8hi
+                const int ps = s / C::DB, db = s % C::DB;
+                vf[s] = *(const bf16x8*)(sV + 32 * db * C::VT_STRIDE + 32 * ps);
+                kf[s] = *(const bf16x8*)(sK + 32 * s);
+            }
 #pragma unroll
-            for (int ps = 0; ps < 2; ps++)
-#pragma unroll
-                for (int db = 0; db < C::DB; db++)
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ps][db], pf[ps], oacc[db],
-                                                                       0, 0, 0);
+            for (int s = 0; s < C::KS; s++) {
+                const int ps = s / C::DB, db = s % C::DB;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], pf[ps], oacc[db], 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], s == 0 ? f32x16{} : sacc,
+                                                               0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::KS, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KS, 0);  // then MFMAs
         }
-        if (do_s) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-            for (int s = 1; s < C::KS; s++)
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
-        }
-        if (grp == 1) store_pair(cur, t);
+        if (g == 1) store_pair(cur, t);
         __syncthreads();
 
         // ---- softmax step t (phase 2t+1 for group 0, 2t+2 for group 1)
-        if (grp == 1) load_pair(cur, t + 2);
+        if (g == 1) load_pair(cur, t + 2);
         if (t < n_tiles_w) {
             const int k0 = t * kBN;
             // sacc[r] is the score of key k0 + 8(r/4) + 4hi + r%4
@@ -317,14 +327,34 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                 pf[ps] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
             }
         }
-        if (grp == 0) store_pair(cur, t);
+        if (g == 0) store_pair(cur, t);
         __syncthreads();
     };
-    for (int t = 0; t <= n_tiles; t += 2) {
-        step(t, st0, st1);
-        if (t + 1 <= n_tiles) step(t + 1, st1, st0);
+    // The two groups run separate copies of the loop (the branch on grp is
+    // wave-uniform); both pass the same number of barriers.
+    // Steps run t = 0 .. n_tiles; the loop takes them in pairs (the stages
+    // swap roles) and an odd last step runs after it, so that inside the
+    // loop both steps are unconditional and the waits stay exact.
+    if (grp == 0) {
+        const std::integral_constant<int, 0> G0;
+        int t = 0;
+        for (; t + 1 <= n_tiles; t += 2) {
+            step(t, st0, st1, G0);
+            step(t + 1, st1, st0, G0);
+        }
+        if (t == n_tiles) step(t, st0, st1, G0);
+        __syncthreads();  // group 1's last phase
+    } else {
+        const std::integral_constant<int, 1> G1;
+        load_pair(st1, 1);  // phase 0: group 0 computes S(0); group 1 only loads
+        __syncthreads();
+        int t = 0;
+        for (; t + 1 <= n_tiles; t += 2) {
+            step(t, st0, st1, G1);
+            step(t + 1, st1, st0, G1);
+        }
+        if (t == n_tiles) step(t, st0, st1, G1);
     }
-    if (grp == 0) __syncthreads();  // group 1's last phase
 
     // ---- epilogue: O = O / l, lse = m ln2 + ln l ----------------------------
     const float l_tot = half_swap_sum(l_run);

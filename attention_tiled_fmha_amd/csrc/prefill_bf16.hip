@@ -298,10 +298,17 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                     if (kj >= Tk || (CAUSAL && kj > qrow + diag)) sacc[r] = -INFINITY;
                 }
             }
-            float mx = sacc[0];
-#pragma unroll
-            for (int r = 1; r < 16; r++) mx = fmaxf(mx, sacc[r]);
-            mx = half_swap_max(mx);
+            float mx;
+            {   // max tree of depth 4 (v_max3)
+                float t0 = __builtin_fmaxf(__builtin_fmaxf(sacc[0], sacc[1]), sacc[2]);
+                float t1 = __builtin_fmaxf(__builtin_fmaxf(sacc[3], sacc[4]), sacc[5]);
+                float t2 = __builtin_fmaxf(__builtin_fmaxf(sacc[6], sacc[7]), sacc[8]);
+                float t3 = __builtin_fmaxf(__builtin_fmaxf(sacc[9], sacc[10]), sacc[11]);
+                float t4 = __builtin_fmaxf(__builtin_fmaxf(sacc[12], sacc[13]), sacc[14]);
+                t0 = __builtin_fmaxf(__builtin_fmaxf(t0, t1), t2);
+                t3 = __builtin_fmaxf(__builtin_fmaxf(t3, t4), sacc[15]);
+                mx = half_swap_max(__builtin_fmaxf(t0, t3));
+            }
             mx = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
             const float m_new = fmaxf(m_run, mx);
             if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThresh)) {
@@ -312,6 +319,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                 m_run = m_new;
             }
             const float m_eff = (m_run == -INFINITY) ? 0.f : m_run;
+            float l0 = l_run, l1 = 0.f;   // two row-sum chains
 #pragma unroll
             for (int ps = 0; ps < 2; ps++) {
                 uint32_t w[4];
@@ -320,12 +328,13 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                     const float p0 = fast_exp2(__builtin_fmaf(sacc[8 * ps + 2 * e], scale_log2, -m_eff));
                     const float p1 = fast_exp2(__builtin_fmaf(sacc[8 * ps + 2 * e + 1], scale_log2, -m_eff));
                     w[e] = pack_bf16x2(p0, p1);
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]),
-                                                            __builtin_bit_cast(bf16x2, 0x3f803f80u),
-                                                            l_run, false);
+                    float& acc = (e & 1) ? l1 : l0;
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]),
+                                                          __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
                 }
                 pf[ps] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
             }
+            l_run = l0 + l1;
         }
         if (g == 0) store_pair(cur, t);
         __syncthreads();

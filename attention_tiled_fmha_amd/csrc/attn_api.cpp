@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kPageSize = 16;
 constexpr int kPlanCUs = 256;      // MI355X compute units (planning only)
-constexpr int kMaxSplit = 512;     // longest chunk one workgroup takes
+constexpr int kMaxSplit = 1024;    // longest chunk one workgroup takes
 constexpr int kMinSplit = 64;      // 4 wavefronts x one 16-token page
 constexpr int kGridYZ = 65535;
 
@@ -33,7 +33,7 @@ int plan(int batch, int heads_kv, int max_kv_len, int num_cus, int requested, in
         s = (requested + kMinSplit - 1) / kMinSplit * kMinSplit;
     } else {
         // Aim for ~8 chunks per compute unit over the batch's worst case, in
-        // power-of-two chunks between 64 and 512 tokens: long contexts and
+        // power-of-two chunks between 64 and 1024 tokens: long contexts and
         // big batches get long chunks (less combine traffic), small batches
         // get short ones (enough workgroups to fill the GPU).
         const double per_item =
@@ -117,6 +117,9 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
     a.in_f32 = dtype == ATTN_F32;
     a.out_f32 = o_dtype == ATTN_F32;
     a.scale = scale;
+    // bf16 caches go to the matrix-core kernel; fp32 and chunks longer than
+    // it takes go to the vector kernel
+    if (attn::decode_mfma_supported(a)) return check_hip(attn::launch_decode_mfma(a, (hipStream_t)stream));
     return check_hip(attn::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -42,6 +42,12 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// The same decode on the matrix core (bf16 cache, G <= 16 query heads per kv
+// head, chunks of at most 1024 tokens); decode_mfma_supported says whether
+// launch_decode_mfma accepts the arguments.
+bool decode_mfma_supported(const DecodeArgs& a);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+
 // Log-sum-exp combine of per-chunk partial states in the workspace into the
 // output (rows = B*Hq, chunks = ceil(length / split_tokens)).
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);

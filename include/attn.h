@@ -94,7 +94,7 @@ int attn_prefill(const void *q, const void *k, const void *v, void *o, float *ls
  *
  * attn_decode_plan: host-only.  Given the shape, the host-side upper bound
  * max_kv_len and the device's compute-unit count (num_cus <= 0: 256),
- * returns in *split_tokens the chunk length (a multiple of 64, at most 512)
+ * returns in *split_tokens the chunk length (a multiple of 64, at most 1024)
  * and in *max_splits the number of chunks of the longest sequence.
  * requested_split > 0 forces that chunk length (rounded up to a multiple of
  * 64).  Returns ATTN_OK or ATTN_E_SHAPE.

@@ -130,9 +130,9 @@ def test_shared_prefix_checks(lib):
 
 
 def test_decode_plan(lib):
-    # workload shapes: long contexts over many sequences get 512-token chunks
-    assert attn.attn_decode_plan(32, 32, 8192) == (512, 16)
-    assert attn.attn_decode_plan(128, 8, 32768) == (512, 64)
+    # workload shapes: long contexts over many sequences get 1024-token chunks
+    assert attn.attn_decode_plan(32, 32, 8192) == (1024, 8)
+    assert attn.attn_decode_plan(128, 8, 32768) == (1024, 32)
     # a small batch gets short chunks, so there are enough workgroups
     s, n = attn.attn_decode_plan(1, 8, 4096)
     assert s == 64 and n == 64
@@ -141,7 +141,7 @@ def test_decode_plan(lib):
     assert attn.attn_decode_plan(4, 4, 1000, requested_split=100) == (128, 8)
     for B, H, L in ((1, 1, 1), (3, 5, 777), (64, 32, 1024), (256, 8, 131072)):
         s, n = attn.attn_decode_plan(B, H, L)
-        assert s % 64 == 0 and 64 <= s <= 512
+        assert s % 64 == 0 and 64 <= s <= 1024
         assert (n - 1) * s < max(L, 1) <= n * s
     with pytest.raises(attn.AttnError):
         attn.attn_decode_plan(1, 0, 10)

@@ -54,19 +54,17 @@ size_t decode_ws_bytes(int batch, int heads_q, int head_dim, int max_splits) {
 
 int check_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
 
-// Shared-prefix chunking: a workgroup covers 4 wavefronts x tpw tiles of 32
-// keys; aim for about two workgroups per compute unit over all kv heads and
-// 64-row query blocks.
-void prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int* chunk, int* tpw,
-                 int* n_chunks) {
+// Shared-prefix chunking: an item is (chunk, kv head, block of 32 query rows),
+// one 4-wavefront workgroup each; aim for about two items per compute unit,
+// in chunks of 64 .. 1024 tokens.
+void prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int* chunk, int* n_chunks) {
     const long rows = (long)batch * (heads_q / heads_kv);
-    const long base = (long)heads_kv * ((rows + 63) / 64);
-    const long want = std::max(1L, (2L * kPlanCUs + base - 1) / base);
-    const long tiles = (prefix_len + 31) / 32;
-    const long t = std::max(1L, (tiles + 4 * want - 1) / (4 * want));
-    *tpw = (int)t;
-    *chunk = (int)(128 * t);
-    *n_chunks = (int)((prefix_len + *chunk - 1) / *chunk);
+    const long per_chunk = (long)heads_kv * ((rows + 31) / 32);
+    const long want = std::max(1L, (2L * kPlanCUs + per_chunk - 1) / per_chunk);
+    long c = (prefix_len + want - 1) / want;
+    c = std::min(1024L, std::max(64L, (c + 63) / 64 * 64));
+    *chunk = (int)c;
+    *n_chunks = (int)((prefix_len + c - 1) / c);
 }
 
 int decode_common(const void* q, const void* k_pages, const void* v_pages,
@@ -221,8 +219,8 @@ size_t attn_shared_prefix_workspace_bytes(int batch, int heads_q, int heads_kv, 
         prefix_len < 0)
         return 0;
     if (dtype == ATTN_BF16 && prefix_len > 0) {
-        int chunk = 0, tpw = 0, n_chunks = 0;
-        prefix_plan(batch, heads_q, heads_kv, prefix_len, &chunk, &tpw, &n_chunks);
+        int chunk = 0, n_chunks = 0;
+        prefix_plan(batch, heads_q, heads_kv, prefix_len, &chunk, &n_chunks);
         return decode_ws_bytes(batch, heads_q, head_dim, n_chunks);
     }
     int split = 0, max_splits = 0;
@@ -252,8 +250,8 @@ int attn_decode_shared_prefix(const void* q, const void* k_pages, const void* v_
     if (!q || !k_pages || !v_pages || !prefix_pages || !o) return ATTN_E_NULL;
     const long rows = (long)batch * (heads_q / heads_kv);
     if ((rows + 63) / 64 > kGridYZ || heads_kv > kGridYZ) return ATTN_E_UNSUPPORTED;
-    int chunk = 0, tpw = 0, n_chunks = 0;
-    prefix_plan(batch, heads_q, heads_kv, prefix_len, &chunk, &tpw, &n_chunks);
+    int chunk = 0, n_chunks = 0;
+    prefix_plan(batch, heads_q, heads_kv, prefix_len, &chunk, &n_chunks);
     const size_t need = decode_ws_bytes(batch, heads_q, head_dim, n_chunks);
     if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
     const size_t nrow = (size_t)batch * heads_q * n_chunks;
@@ -276,7 +274,6 @@ int attn_decode_shared_prefix(const void* q, const void* k_pages, const void* v_
     a.Hkv = heads_kv;
     a.D = head_dim;
     a.chunk = chunk;
-    a.tiles_per_wave = tpw;
     a.out_f32 = o_dtype == ATTN_F32;
     a.scale = scale;
     hipError_t e = attn::launch_prefix(a, (hipStream_t)stream);

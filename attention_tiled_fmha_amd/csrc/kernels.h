@@ -52,11 +52,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // output (rows = B*Hq, chunks = ceil(length / split_tokens)).
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 
-// Shared-prefix stage of cascade decode (bf16 MFMA).  Grid: one workgroup
-// per (prefix chunk, kv head, block of 64 query rows); each chunk is
-// 4 wavefronts x tiles_per_wave x 32 keys long.  With more than one chunk the
-// per-chunk states go to ws_o / ws_lse ([R*Hq][n_chunks][D], [R*Hq][n_chunks])
-// and must be combined with launch_decode_combine.
+// Shared-prefix stage of cascade decode (bf16 MFMA).  Work items are
+// (prefix chunk of `chunk` tokens, kv head, block of 32 query rows), walked by
+// a persistent grid; chunk is a multiple of 16 and at most 1024.  With more
+// than one chunk the per-chunk states go to ws_o / ws_lse ([R*Hq][n_chunks][D],
+// [R*Hq][n_chunks]) and must be combined with launch_decode_combine.
 struct PrefixArgs {
     const void* q;           // [R, Hq, D] bf16
     const void* k_pages;     // [P, Hkv, 16, D] bf16
@@ -68,7 +68,7 @@ struct PrefixArgs {
     float* ws_o;
     float* ws_lse;
     int R, Hq, Hkv, D;
-    int chunk, tiles_per_wave;
+    int chunk;
     bool out_f32;
     float scale;
 };

@@ -176,10 +176,13 @@ def bench_cascade(steps, warmup):
                        dtype=torch.uint8, device="cuda")
     ws_s = torch.empty(max(1, attn.attn_decode_workspace_bytes(R, H, c["Hkv"], D, maxlen)),
                        dtype=torch.uint8, device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
 
     def before(i):
-        flush.fill_(i & 0xFF)   # evict the last-level cache between repetitions
+        # evict the last-level cache (256 MB) between repetitions by reading
+        # 512 MB; a write would leave dirty lines whose write-back then
+        # competes with the timed reads
+        flush.sum()
 
     def step(i):
         attn.attn_decode_shared_prefix(q, kp, vp, pp, c["prefix_len"], o_p, l_p, scale=c["scale"],

@@ -43,7 +43,9 @@ class AttnError(RuntimeError):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("split_tokens", ctypes.c_int), ("reserved", ctypes.c_int * 7)]
+    _fields_ = [("split_tokens", ctypes.c_int), ("use_unified_max", ctypes.c_int),
+                ("phi", ctypes.c_float), ("reserved0", ctypes.c_int),
+                ("fallback_count", ctypes.c_void_p), ("reserved", ctypes.c_int * 4)]
 
 
 def load(path=LIB_PATH):
@@ -130,11 +132,15 @@ def attn_decode_workspace_bytes(batch, heads_q, heads_kv, head_dim, max_kv_len, 
 
 
 def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse=None, max_kv_len=None,
-                      scale=None, workspace=None, split_tokens=0, stream=None):
+                      scale=None, workspace=None, split_tokens=0, stream=None,
+                      unified_max=False, phi=0.0, fallback_count=None):
     """q, o [B,Hq,D]; k_pages, v_pages [P,Hkv,16,D]; block_table int32 [B,maxp];
     kv_lens int32 [B]; lse fp32 [B,Hq] or None.  max_kv_len is the host-side
     bound of kv_lens (required).  A workspace of the needed size is allocated
-    with torch when none is given."""
+    with torch when none is given.  unified_max selects the unified-max
+    softmax with value phi; fallback_count (a device int32 tensor of one
+    element, or None) receives the number of (row, chunk) pairs that fell
+    back to the exact path, added to its value."""
     for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"),
                  (block_table, "block_table"), (kv_lens, "kv_lens"), (o, "o")):
         _dense(t, n)
@@ -160,7 +166,12 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse=None, ma
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    opts = DecodeOpts(split_tokens=int(split_tokens))
+    if fallback_count is not None:
+        _dense(fallback_count, "fallback_count")
+        if fallback_count.dtype != torch.int32 or fallback_count.numel() != 1:
+            raise TypeError("fallback_count must be one int32 element")
+    opts = DecodeOpts(split_tokens=int(split_tokens), use_unified_max=int(bool(unified_max)),
+                      phi=float(phi), fallback_count=_p(fallback_count))
     _check(load().attn_decode_paged_ex(
         _p(q), _p(k_pages), _p(v_pages), _p(block_table), _p(kv_lens), _p(o), _p(lse),
         B, Hq, Hkv, D, page, block_table.shape[1], int(max_kv_len), dt, _dtype(o),

@@ -72,7 +72,8 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
                   int fixed_len, void* o, float* lse, int batch, int heads_q, int heads_kv,
                   int head_dim, int page_size, int max_pages_per_seq, int max_kv_len, int dtype,
                   int o_dtype, float scale, void* workspace, size_t workspace_bytes,
-                  void* stream, int requested_split) {
+                  void* stream, int requested_split, bool unified = false, float phi = 0.f,
+                  int* fallback_count = nullptr) {
     if (!dtype_ok(dtype) || !dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
     if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || max_kv_len < 0 || max_pages_per_seq < 0)
         return ATTN_E_SHAPE;
@@ -115,9 +116,13 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
     a.in_f32 = dtype == ATTN_F32;
     a.out_f32 = o_dtype == ATTN_F32;
     a.scale = scale;
+    a.unified = unified;
+    a.phi = phi;
+    a.fallback_count = fallback_count;
     // bf16 caches go to the matrix-core kernel; fp32 and chunks longer than
-    // it takes go to the vector kernel
+    // it takes go to the vector kernel (which has no unified-max mode)
     if (attn::decode_mfma_supported(a)) return check_hip(attn::launch_decode_mfma(a, (hipStream_t)stream));
+    if (unified) return ATTN_E_UNSUPPORTED;
     return check_hip(attn::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -185,10 +190,13 @@ int attn_decode_paged_ex(const void* q, const void* k_pages, const void* v_pages
     if (batch > 0 && !kv_lens) return ATTN_E_NULL;
     const int requested = opts ? opts->split_tokens : 0;
     if (requested < 0) return ATTN_E_ARG;
+    const bool unified = opts && opts->use_unified_max;
+    const float phi = opts ? opts->phi : 0.f;
+    if (unified && !std::isfinite(phi)) return ATTN_E_ARG;
     return decode_common(q, k_pages, v_pages, block_table, max_pages_per_seq, kv_lens, 0, o,
                          lse, batch, heads_q, heads_kv, head_dim, page_size, max_pages_per_seq,
                          max_kv_len, dtype, o_dtype, scale, workspace, workspace_bytes, stream,
-                         requested);
+                         requested, unified, phi, opts ? opts->fallback_count : nullptr);
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,

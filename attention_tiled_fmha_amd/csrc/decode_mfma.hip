@@ -42,6 +42,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace attn {
 
@@ -50,6 +51,7 @@ namespace {
 constexpr int kPage = 16;
 constexpr int kMaxG = 16;
 constexpr float kRescaleThresh = 8.0f;   // log2 units, as in the vector kernel
+constexpr float kUnifiedWindow = 60.0f;  // |max scaled score - phi| bound of the unified max
 constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit data, no swizzle
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -88,7 +90,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int G = a.Hq / a.Hkv;
     __shared__ float s_m[4][kMaxG];
     __shared__ float s_l[4][kMaxG];
+    __shared__ float s_x[4][kMaxG];     // unified max: largest raw score per row
     __shared__ float s_o[4][kMaxG][D];
+    const float phi_l2 = a.phi * kLog2e;
     auto item = [&](const int c, const int kvh, const int b) {
     // lengths past the host bound are clamped, so no index leaves the planned
     // split range or the block-table row
@@ -158,79 +162,123 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D * 2 + 64 * cc, 0, 0);
     };
 
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f, smax = -INFINITY;
     f32x4 oacc[NB];
-#pragma unroll
-    for (int i = 0; i < NB; i++) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const PageBuf<D>& pb, int j) {
-        const int pg = pg0 + j;
-        f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[0]), qf[0],
-                                                           f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    // One pass over the chunk's pages, with the result published to LDS.
+    // EXACT: online softmax against the running max (raised lazily).  Else
+    // the unified-max softmax: every exponential is taken against the
+    // caller's phi, with no running max, no rescale and no cross-lane max;
+    // smax only tracks the lane's largest raw score, so that a row leaving
+    // the safe window around phi can be detected after the pass.
+    auto pass = [&](auto EXACT) {
+        constexpr bool exact = decltype(EXACT)::value;
+        m_run = exact ? -INFINITY : phi_l2;
+        l_run = 0.f;
+        smax = -INFINITY;
 #pragma unroll
-        for (int ks = 1; ks < KS; ks++)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[ks]), qf[ks], s, 0, 0, 0);
-        // s[r] is the score of token pg*16 + 4grp + r for head col
-        if (pg * kPage + kPage > tok1) {
+        for (int i = 0; i < NB; i++) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        auto compute = [&](const PageBuf<D>& pb, int j) {
+            const int pg = pg0 + j;
+            f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[0]), qf[0],
+                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; r++)
-                if (pg * kPage + 4 * grp + r >= tok1) s[r] = -INFINITY;
+            for (int ks = 1; ks < KS; ks++)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[ks]), qf[ks], s, 0, 0, 0);
+            // s[r] is the score of token pg*16 + 4grp + r for head col
+            if (pg * kPage + kPage > tok1) {
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if (pg * kPage + 4 * grp + r >= tok1) s[r] = -INFINITY;
+            }
+            float m_eff;
+            if (exact) {
+                float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+                mx = max_xor32(max_xor16(mx));
+                const float m_new = fmaxf(m_run, mx * sl2);
+                if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThresh)) {
+                    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+                    l_run *= alpha;
+#pragma unroll
+                    for (int i = 0; i < NB; i++) oacc[i] *= alpha;
+                    m_run = m_new;
+                }
+                m_eff = (m_run == -INFINITY) ? 0.f : m_run;
+            } else {
+                smax = fmaxf(smax, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+                m_eff = phi_l2;
+            }
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m_eff));
+            const uint32_t p01 = pack_bf16x2(p[0], p[1]), p23 = pack_bf16x2(p[2], p[3]);
+            // the row sum adds the bf16-rounded P that meets V
+            l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+            const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+#pragma unroll
+            for (int cc = 0; cc < D / 32; cc++) {
+                const uint32_t v0 = pb.v[0][cc], v1 = pb.v[1][cc], v2 = pb.v[2][cc], v3 = pb.v[3][cc];
+                const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x05040100u),
+                                                                 __builtin_amdgcn_perm(v3, v2, 0x05040100u)});
+                const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x07060302u),
+                                                                 __builtin_amdgcn_perm(v3, v2, 0x07060302u)});
+                oacc[2 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pt, oacc[2 * cc], 0, 0, 0);
+                oacc[2 * cc + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pt, oacc[2 * cc + 1], 0, 0, 0);
+            }
+        };
+
+        // pages j = wave, wave + 4, ... with the next page's loads in flight;
+        // the loads are unconditional so that each wait covers exactly one page
+        const int nj = npg > wave ? (npg - wave + 3) / 4 : 0;
+        PageBuf<D> ba, bb;
+        load(ba, wave);
+        for (int n = 0; n < nj; n += 2) {
+            load(bb, wave + 4 * (n + 1));
+            compute(ba, wave + 4 * n);
+            if (n + 1 >= nj) break;
+            load(ba, wave + 4 * (n + 2));
+            compute(bb, wave + 4 * (n + 1));
         }
-        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        mx = max_xor32(max_xor16(mx));
-        const float m_new = fmaxf(m_run, mx * sl2);
-        if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThresh)) {
-            const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < NB; i++) oacc[i] *= alpha;
-            m_run = m_new;
+        l_run = sum_xor32(sum_xor16(l_run));   // tokens of the four lane groups
+        if (!exact) smax = max_xor32(max_xor16(smax));
+
+        // publish this wavefront's state
+        if (grp == 0) {
+            s_m[wave][col] = m_run;
+            s_l[wave][col] = l_run;
+            s_x[wave][col] = smax;
         }
-        const float m_eff = (m_run == -INFINITY) ? 0.f : m_run;
-        float p[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m_eff));
-        const uint32_t p01 = pack_bf16x2(p[0], p[1]), p23 = pack_bf16x2(p[2], p[3]);
-        // the row sum adds the bf16-rounded P that meets V
-        l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-        const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+        for (int i = 0; i < NB; i++)
 #pragma unroll
-        for (int cc = 0; cc < D / 32; cc++) {
-            const uint32_t v0 = pb.v[0][cc], v1 = pb.v[1][cc], v2 = pb.v[2][cc], v3 = pb.v[3][cc];
-            const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x05040100u),
-                                                             __builtin_amdgcn_perm(v3, v2, 0x05040100u)});
-            const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x07060302u),
-                                                             __builtin_amdgcn_perm(v3, v2, 0x07060302u)});
-            oacc[2 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pt, oacc[2 * cc], 0, 0, 0);
-            oacc[2 * cc + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pt, oacc[2 * cc + 1], 0, 0, 0);
-        }
+            for (int r = 0; r < 4; r++)   // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2
+                s_o[wave][col][32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1)] = oacc[i][r];
+        __syncthreads();
     };
 
-    // pages j = wave, wave + 4, ... with the next page's loads in flight; the
-    // loads are unconditional so that each wait covers exactly one page
-    const int nj = npg > wave ? (npg - wave + 3) / 4 : 0;
-    PageBuf<D> ba, bb;
-    load(ba, wave);
-    for (int n = 0; n < nj; n += 2) {
-        load(bb, wave + 4 * (n + 1));
-        compute(ba, wave + 4 * n);
-        if (n + 1 >= nj) break;
-        load(ba, wave + 4 * (n + 2));
-        compute(bb, wave + 4 * (n + 1));
+    if (a.unified) {
+        pass(std::false_type{});
+        // Rows (heads < G) whose largest scaled score leaves [phi - 60,
+        // phi + 60] are recomputed with the exact pass: outside it a term
+        // exp(s - phi) can overflow the fp32 sums (or the largest one
+        // underflow).  Every thread reads the same LDS values, so the
+        // decision is uniform across the workgroup.
+        int n_out = 0;
+        for (int g = 0; g < G; g++) {
+            float M = -INFINITY;
+            for (int w = 0; w < 4; w++) M = fmaxf(M, s_x[w][g]);
+            const float z = M * a.scale - a.phi;
+            if (z > kUnifiedWindow || z < -kUnifiedWindow) n_out++;
+        }
+        if (n_out > 0) {
+            if (threadIdx.x == 0 && a.fallback_count) atomicAdd(a.fallback_count, n_out);
+            __syncthreads();   // the LDS state is rewritten by the exact pass
+            pass(std::true_type{});
+        }
+    } else {
+        pass(std::true_type{});
     }
-    l_run = sum_xor32(sum_xor16(l_run));   // tokens of the four lane groups
-
-    // ---- merge the four wavefronts through LDS ----------------------------
-    if (grp == 0) {
-        s_m[wave][col] = m_run;
-        s_l[wave][col] = l_run;
-    }
-#pragma unroll
-    for (int i = 0; i < NB; i++)
-#pragma unroll
-        for (int r = 0; r < 4; r++)   // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2
-            s_o[wave][col][32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1)] = oacc[i][r];
-    __syncthreads();
 
     for (int idx = threadIdx.x; idx < G * D; idx += 256) {
         const int g = idx / D, d = idx % D;

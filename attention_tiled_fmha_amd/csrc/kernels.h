@@ -39,6 +39,12 @@ struct DecodeArgs {
     int split_tokens, max_splits;
     bool in_f32, out_f32;
     float scale;
+    // unified-max softmax (matrix-core kernel only): exponentials against phi,
+    // exact recompute of the chunks whose rows leave the window; the number of
+    // such (row, chunk) pairs is added to *fallback_count when it is not null
+    bool unified;
+    float phi;
+    int* fallback_count;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -152,11 +152,34 @@ int attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
 
 /*
  * Options of attn_decode_paged_ex (zero-initialise, then set what you need).
- *   split_tokens : 0 = planner's choice; > 0 forces the chunk length.
+ *   split_tokens    : 0 = planner's choice; > 0 forces the chunk length.
+ *   use_unified_max : 1 = asynchronous softmax with a unified max value
+ *                     (FlashDecoding++ summary, wenjunhu.com/d/2311396.html,
+ *                     sections 1 and 3): within every chunk each exponential
+ *                     is taken against the fixed scalar phi instead of a
+ *                     running maximum, so partial sums need no rescaling and
+ *                     no exchange of maxima.  A (query row, chunk) pair whose
+ *                     largest scaled score s = scale * q.k leaves the window
+ *                     phi - 60 <= max s <= phi + 60 (outside it exp(s - phi)
+ *                     could overflow an fp32 sum or the largest term
+ *                     underflow) falls back: its chunk is recomputed with the
+ *                     exact online softmax.  Results equal the plain path's
+ *                     within the same tolerance.  bf16 caches with
+ *                     heads_q / heads_kv <= 16 only (else ATTN_E_UNSUPPORTED).
+ *   phi             : the unified max, in units of scaled scores (finite,
+ *                     else ATTN_E_ARG); 0 suits scores of order one.
+ *   fallback_count  : device int, or NULL.  The number of (query row, chunk)
+ *                     pairs that fell back is added to it (atomically; the
+ *                     caller zeroes it); a sequence shorter than one chunk is
+ *                     one chunk.
  */
 typedef struct {
     int split_tokens;
-    int reserved[7];
+    int use_unified_max;
+    float phi;
+    int reserved0;
+    int *fallback_count;
+    int reserved[4];
 } attn_decode_opts;
 
 /* attn_decode_paged with options (opts may be NULL = defaults). */

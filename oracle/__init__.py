@@ -52,6 +52,10 @@ def load(path=_LIB_PATH):
                                         ctypes.c_double, ip]
     lib.oracle_merge_states.restype = None
     lib.oracle_merge_states.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_long, ip]
+    lib.oracle_unified_fallback_count.restype = ctypes.c_long
+    lib.oracle_unified_fallback_count.argtypes = [vp, vp, ip, vp, vp, ip, ip, ip, ip, ip, ip,
+                                                  ctypes.c_double, ip, ctypes.c_double,
+                                                  ctypes.c_double]
     return lib
 
 
@@ -141,6 +145,31 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale, threads=None,
     if rc != 0:
         raise RuntimeError(f"oracle_decode_paged failed ({rc})")
     return o, lse
+
+
+def unified_fallback_count(q, k_pages, block_table, kv_lens, scale, split_tokens, phi,
+                           window=60.0, lib=None):
+    """Number of (query row, chunk) pairs whose largest scaled score leaves
+    [phi - window, phi + window]: the fallback model of the unified-max
+    softmax.  Same input layout as decode_paged."""
+    lib = lib or _get()
+    q = np.ascontiguousarray(q)
+    k_pages = np.ascontiguousarray(k_pages)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    kl = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    dt = _dtype_code(q)
+    if _dtype_code(k_pages) != dt:
+        raise TypeError("q and the pages must share one element type")
+    B, Hq, D = q.shape
+    P, Hkv, page, Dk = k_pages.shape
+    if Dk != D or bt.shape[0] != B or kl.shape != (B,):
+        raise ValueError("shape mismatch")
+    n = lib.oracle_unified_fallback_count(_ptr(q), _ptr(k_pages), dt, _ptr(bt), _ptr(kl),
+                                          B, Hq, Hkv, D, page, bt.shape[1], float(scale),
+                                          int(split_tokens), float(phi), float(window))
+    if n < 0:
+        raise RuntimeError("oracle_unified_fallback_count: bad arguments")
+    return int(n)
 
 
 def merge_states(o_a, lse_a, o_b, lse_b, lib=None):

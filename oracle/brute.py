@@ -55,3 +55,24 @@ def attention(q, k, v, causal, scale):
         o.append(ob)
         lse.append(lb)
     return o, lse
+
+
+def unified_fallback_count(q, keys, lengths, scale, split_tokens, phi, window=60.0):
+    """Fallback pairs of the unified-max softmax, by brute force.
+
+    q[b][h] is a query row, keys[b][kvh][t] the t-th key of sequence b (no
+    paging), lengths[b] the number of keys; head h reads kv head
+    h // (len(q[b]) // len(keys[b])).  A (row, chunk of split_tokens keys) pair
+    counts when its largest scaled score is more than window away from phi.
+    """
+    count = 0
+    for b in range(len(q)):
+        group = len(q[b]) // len(keys[b])
+        for h in range(len(q[b])):
+            ks = keys[b][h // group]
+            for c0 in range(0, lengths[b], split_tokens):
+                s = [scale * math.fsum(x * y for x, y in zip(q[b][h], ks[t]))
+                     for t in range(c0, min(lengths[b], c0 + split_tokens))]
+                if abs(max(s) - phi) > window:
+                    count += 1
+    return count

@@ -267,3 +267,53 @@ void oracle_merge_states(const double *o_a, const double *lse_a,
         lse_out[r] = M + log(wa + wb);
     }
 }
+
+/*
+ * Fallback model of the unified-max softmax (FlashDecoding++ summary,
+ * wenjunhu.com/d/2311396.html, sections 1 and 3: every partial softmax uses
+ * one fixed maximum phi; a partial whose values leave the range the fixed
+ * maximum can serve is recomputed).  The pages fix neither phi nor the test;
+ * the reading adopted: with s = scale * q.k, the pair (query row, chunk of
+ * split_tokens keys) falls back when max_chunk(s) - phi > window or
+ * max_chunk(s) - phi < -window.  Returns the number of such pairs over all
+ * (b, hq) rows and chunks c < ceil(kv_lens[b] / split_tokens), scores in
+ * fp64, or a negative value on bad arguments.
+ */
+long oracle_unified_fallback_count(const void *q, const void *k_pages, int dtype,
+                                   const int32_t *block_table, const int32_t *kv_lens,
+                                   int B, int Hq, int Hkv, int D, int page_size,
+                                   int max_pages, double scale, int split_tokens,
+                                   double phi, double window)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || page_size <= 0 ||
+        split_tokens <= 0)
+        return -1;
+    const int group = Hq / Hkv;
+    long count = 0;
+    for (int b = 0; b < B; b++) {
+        const int L = kv_lens[b];
+        if (L < 0 || (L + page_size - 1) / page_size > max_pages)
+            return -1;
+        for (int h = 0; h < Hq; h++) {
+            const int kvh = h / group;
+            for (int c0 = 0; c0 < L; c0 += split_tokens) {
+                const int c1 = c0 + split_tokens < L ? c0 + split_tokens : L;
+                double m = -INFINITY;
+                for (int t = c0; t < c1; t++) {
+                    const size_t page = (size_t)block_table[(size_t)b * max_pages + t / page_size];
+                    const size_t src = ((page * Hkv + kvh) * page_size + t % page_size) * D;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; d++)
+                        dot += load_elem(q, dtype, ((size_t)b * Hq + h) * D + d) *
+                               load_elem(k_pages, dtype, src + d);
+                    const double s = scale * dot;
+                    if (s > m)
+                        m = s;
+                }
+                if (m - phi > window || m - phi < -window)
+                    count++;
+            }
+        }
+    }
+    return count;
+}

@@ -406,10 +406,49 @@ def check_bf16_widening(lib):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "bf16 widening"
 
 
+# --- 17. fallback model of the unified-max softmax ----------------------------
+
+def check_unified_fallback(lib):
+    """The (row, chunk) pairs that leave phi +- 60 (the reading of the unified
+    max of the FlashDecoding++ summary, sections 1 and 3): closed forms from
+    constant and one-hot scores, and the brute force on random tiny cases."""
+    D, split, Hq, Hkv = 8, 32, 4, 2
+    lens = [40, 16, 100]                        # 2 + 1 + 4 chunks of 32
+    d = wl.paged_decode_inputs(len(lens), Hq, Hkv, D, "f32", 21, lengths=lens)
+    bt, kl = d["block_table"], d["kv_lens"]
+    pairs = Hq * sum((L + split - 1) // split for L in lens)
+    # every score s = 1 * (2 e0) . (5 e0) = 10 exactly
+    k = np.zeros_like(d["k_pages"]); k[..., 0] = 5.0
+    q = np.zeros_like(d["q"]); q[..., 0] = 2.0
+    for phi, expect in ((0.0, 0), (100.0, pairs), (-55.0, pairs), (-45.0, 0), (69.0, 0), (71.0, pairs)):
+        n = oracle.unified_fallback_count(q, k, bt, kl, 1.0, split, phi, lib=lib)
+        assert n == expect, f"constant scores, phi {phi}: {n} != {expect}"
+    # one key with score 100 (sequence 2, token 37 = chunk 1, kv head 1) and
+    # every other score 0: only heads 2 and 3 of that chunk fall back
+    k = np.zeros_like(d["k_pages"])
+    k[bt[2][37 // 16], 1, 37 % 16, 0] = 100.0
+    q = np.zeros_like(d["q"]); q[..., 0] = 1.0
+    n = oracle.unified_fallback_count(q, k, bt, kl, 1.0, split, 0.0, lib=lib)
+    assert n == 2, f"one dominant key: {n} != 2"
+    # brute force: random scores spread over a few hundred around phi
+    g = _rng(22)
+    for case in range(3):
+        lens = [int(x) for x in g.integers(1, 70, size=3)]
+        d = wl.paged_decode_inputs(3, Hq, Hkv, D, "f32", 30 + case, lengths=lens)
+        scale, phi = float(g.uniform(20, 60)), float(g.uniform(-50, 50))
+        n = oracle.unified_fallback_count(d["q"], d["k_pages"], d["block_table"], d["kv_lens"],
+                                          scale, 16, phi, lib=lib)
+        keys = [[[d["k_pages"][d["block_table"][b][t // 16], kvh, t % 16].tolist()
+                  for t in range(lens[b])] for kvh in range(Hkv)] for b in range(3)]
+        ref = brute.unified_fallback_count(d["q"].tolist(), keys, lens, scale, 16, phi)
+        assert n == ref, f"brute force case {case}: {n} != {ref}"
+        assert 0 < ref < Hq * sum((L + 15) // 16 for L in lens), "case should mix in and out"
+
+
 ALL_CHECKS = [
     check_hand_2x2, check_identical_keys, check_dominant_score,
     check_single_key_and_row0, check_scale_zero, check_brute_force, check_scipy,
     check_rows_sum_to_one, check_permutation, check_merge_split, check_merge_algebra,
     check_cascade, check_decode_vs_prefill, check_gqa_mapping, check_token_set,
-    check_lse_dropped_page, check_tail_garbage, check_bf16_widening,
+    check_lse_dropped_page, check_tail_garbage, check_bf16_widening, check_unified_fallback,
 ]

@@ -270,3 +270,79 @@ def test_shared_prefix_bf16(R, H, Hkv, plen, D, o_dtype):
                                  np.full(R, plen, np.int32), c["scale"])
     assert_close(host(o), ro, "bf16", "prefix O")
     assert_close(host(lse), rl, "bf16", "prefix lse")
+
+
+# --- unified-max softmax (asynchronous softmax with recompute fallback) -------
+
+def run_decode_unified(d, phi, split_tokens):
+    q = dev(d["q"])
+    o = empty_like_out(q.shape, d["dtype"])
+    lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+    count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    attn.attn_decode_paged(q, dev(d["k_pages"]), dev(d["v_pages"]), dev(d["block_table"]),
+                           dev(d["kv_lens"]), o, lse, max_kv_len=int(d["kv_lens"].max(initial=0)),
+                           scale=d["scale"], split_tokens=split_tokens, unified_max=True, phi=phi,
+                           fallback_count=count)
+    torch.cuda.synchronize()
+    return host(o), host(lse), int(count.item())
+
+
+def model_count(d, split, phi):
+    """The fp64 fallback model; the case must not sit within 0.01 of the
+    window edge, where fp32 and fp64 scores could decide differently."""
+    args = (d["q"], d["k_pages"], d["block_table"], d["kv_lens"], d["scale"], split, phi)
+    n = oracle.unified_fallback_count(*args)
+    assert n == oracle.unified_fallback_count(*args, window=59.99) == \
+        oracle.unified_fallback_count(*args, window=60.01), "case too close to the window edge"
+    return n
+
+
+UNI_LENS = [0, 1, 16, 17, 300, 512, 513, 1000, 2049]
+
+
+@pytest.mark.parametrize("phi", [0.0, 100.0, -100.0])
+@pytest.mark.parametrize("heads", [(8, 8), (32, 8)])
+def test_unified_max(phi, heads):
+    """With phi = 0 no (row, chunk) pair of N(0,1) scores leaves the window
+    and none falls back; with phi = +-100 every pair does.  Either way the
+    result is the plain attention, and the GPU's fallback count is the fp64
+    model's."""
+    require_gpu()
+    Hq, Hkv = heads
+    split = 256
+    d = wl.paged_decode_inputs(len(UNI_LENS), Hq, Hkv, 128, "bf16", 40 + Hq, lengths=UNI_LENS)
+    o, lse, n = run_decode_unified(d, phi, split)
+    ro, rl = oracle_decode(d)
+    assert_close(o, ro, "bf16", "O")
+    assert_close(lse, rl, "bf16", "lse")
+    pairs = Hq * sum((L + split - 1) // split for L in UNI_LENS)
+    assert n == model_count(d, split, phi) == (0 if phi == 0.0 else pairs)
+
+
+def test_unified_max_mixed_fallback():
+    """Queries of half the sequences scaled by 50: their (row, chunk) pairs
+    leave the window around phi = 0 (the others stay inside) and are
+    recomputed; the count matches the model and the result the oracle."""
+    require_gpu()
+    split = 128
+    lens = [33, 200, 700, 1500, 64, 129, 900, 2000]
+    d = wl.paged_decode_inputs(len(lens), 16, 4, 128, "bf16", 47, lengths=lens)
+    q = wl.bf16_to_f32(d["q"])
+    q[::2] *= 50.0
+    d["q"] = wl.bf16_bits(q)
+    o, lse, n = run_decode_unified(d, 0.0, split)
+    ro, rl = oracle_decode(d)
+    assert_close(o, ro, "bf16", "O")
+    assert_close(lse, rl, "bf16", "lse")
+    assert n == model_count(d, split, 0.0)
+    assert 0 < n < 16 * sum((L + split - 1) // split for L in lens)
+
+
+def test_unified_max_default_split():
+    """Planner-chosen chunks, GQA 4, fp32 output: same result as the plain path."""
+    require_gpu()
+    d = wl.paged_decode_inputs(6, 32, 8, 128, "bf16", 48, lengths=[5, 600, 1100, 3000, 64, 4096])
+    o, lse, n = run_decode_unified(d, 0.0, 0)
+    ro, rl = oracle_decode(d)
+    assert_close(o, ro, "bf16", "O")
+    assert n == 0

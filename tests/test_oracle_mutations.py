@@ -33,6 +33,10 @@ MUTATIONS = {
                               "const double ta = wa > 0.0 ? wb * o_a[r * D + c] : 0.0;"),
     "merge lse without max": ("lse_out[r] = M + log(wa + wb);", "lse_out[r] = log(wa + wb);"),
     "bf16 widened as low half": ("<< 16;\n    float f;", ";\n    float f;"),
+    "fallback lower bound dropped": ("if (m - phi > window || m - phi < -window)", "if (m - phi > window)"),
+    "fallback score unscaled": ("const double s = scale * dot;", "const double s = dot;"),
+    "fallback over the whole sequence": ("const int c1 = c0 + split_tokens < L ? c0 + split_tokens : L;",
+                                         "const int c1 = L;"),
 }
 
 

@@ -55,26 +55,38 @@ def log(msg):
 
 def time_launches(fn, steps, warmup, before=None):
     """Per-launch durations (ms) from HIP events on the current stream, plus
-    the wall span of the K timed steps."""
+    the span of the K timed steps and its wall time.
+
+    Without a per-step ``before`` the K steps are enqueued back to back
+    between one pair of events (per-step events would add their own gaps), so
+    every duration is span / K.  With ``before`` (e.g. a cache flush) each step
+    gets its own event pair and ``before`` stays outside the timed spans."""
     for i in range(warmup):
         if before:
             before(i)
         fn(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if before is None:
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        span = start.elapsed_time(end)
+        return [span / steps] * steps, span, time.perf_counter() - t0
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
-        if before:
-            before(i)
+        before(i)
         starts[i].record()
         fn(i)
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    span = starts[0].elapsed_time(ends[-1])
-    return durs, span, wall
+    return durs, float(np.sum(durs)), wall
 
 
 def source_digest(*names):

@@ -94,218 +94,218 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ float s_o[4][kMaxG][D];
     const float phi_l2 = a.phi * kLog2e;
     auto item = [&](const int c, const int kvh, const int b) {
-    // lengths past the host bound are clamped, so no index leaves the planned
-    // split range or the block-table row
-    const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
-    const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
+        // lengths past the host bound are clamped, so no index leaves the planned
+        // split range or the block-table row
+        const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
+        const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
 
-    if (L <= 0) {  // nothing to attend: O = 0, lse = -inf
-        if (c == 0 && wave == 0) {
-            for (int g = 0; g < G; g++) {
-                const size_t row = (size_t)b * a.Hq + kvh * G + g;
-                for (int d = lane; d < D; d += kWave) {
-                    if (a.out_f32) ((float*)a.o)[row * D + d] = 0.f;
-                    else ((uint16_t*)a.o)[row * D + d] = 0;
+        if (L <= 0) {  // nothing to attend: O = 0, lse = -inf
+            if (c == 0 && wave == 0) {
+                for (int g = 0; g < G; g++) {
+                    const size_t row = (size_t)b * a.Hq + kvh * G + g;
+                    for (int d = lane; d < D; d += kWave) {
+                        if (a.out_f32) ((float*)a.o)[row * D + d] = 0.f;
+                        else ((uint16_t*)a.o)[row * D + d] = 0;
+                    }
+                    if (a.lse && lane == 0) a.lse[row] = -INFINITY;
                 }
-                if (a.lse && lane == 0) a.lse[row] = -INFINITY;
+            }
+            return;
+        }
+        if (c >= nsplit) return;
+
+        const int tok0 = c * a.split_tokens;
+        const int tok1 = min(L, tok0 + a.split_tokens);
+        const int pg0 = tok0 / kPage, pg1 = (tok1 + kPage - 1) / kPage;
+        const int npg = pg1 - pg0;
+        const int32_t* table = a.block_table + (size_t)b * a.bt_stride;
+        const float sl2 = a.scale * kLog2e;
+        const uint16_t* kbase = (const uint16_t*)a.k_pages;
+        const uint16_t* vbase = (const uint16_t*)a.v_pages;
+
+        // Q^T (B operand): head col (zero for col >= G), dims 32s + 8grp .. +7
+        bf16x8 qf[KS];
+        {
+            const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.Hq + kvh * G + min(col, G - 1)) * D;
+    #pragma unroll
+            for (int s = 0; s < KS; s++) {
+                u32x4 w = *(const u32x4*)(qrow + 32 * s + 8 * grp);
+                if (col >= G) w = u32x4{0, 0, 0, 0};
+                qf[s] = __builtin_bit_cast(bf16x8, w);
             }
         }
-        return;
-    }
-    if (c >= nsplit) return;
 
-    const int tok0 = c * a.split_tokens;
-    const int tok1 = min(L, tok0 + a.split_tokens);
-    const int pg0 = tok0 / kPage, pg1 = (tok1 + kPage - 1) / kPage;
-    const int npg = pg1 - pg0;
-    const int32_t* table = a.block_table + (size_t)b * a.bt_stride;
-    const float sl2 = a.scale * kLog2e;
-    const uint16_t* kbase = (const uint16_t*)a.k_pages;
-    const uint16_t* vbase = (const uint16_t*)a.v_pages;
+        // the chunk's block-table entries (at most 64 pages): entry pg0 + lane,
+        // picked with v_readlane
+        const int tblv = lane < npg ? table[pg0 + lane] : 0;
+        auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(tblv, j); };
 
-    // Q^T (B operand): head col (zero for col >= G), dims 32s + 8grp .. +7
-    bf16x8 qf[KS];
-    {
-        const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.Hq + kvh * G + min(col, G - 1)) * D;
-#pragma unroll
-        for (int s = 0; s < KS; s++) {
-            u32x4 w = *(const u32x4*)(qrow + 32 * s + 8 * grp);
-            if (col >= G) w = u32x4{0, 0, 0, 0};
-            qf[s] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-
-    // the chunk's block-table entries (at most 64 pages): entry pg0 + lane,
-    // picked with v_readlane
-    const int tblv = lane < npg ? table[pg0 + lane] : 0;
-    auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(tblv, j); };
-
-    const int voff_k = col * D * 2 + 16 * grp;
-    const int voff_v = 4 * grp * D * 2 + 4 * col;
-    // page j of the chunk; past the chunk the descriptor is empty and the
-    // loads return zeros without touching memory
-    auto load = [&](PageBuf<D>& pb, int j) {
-        const int pg = pg0 + j;
-        const int phys = phys_of(min(j, npg - 1));
-        const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(kPage, tok1 - pg * kPage)) * D * 2);
-        const size_t off = ((size_t)phys * a.Hkv + kvh) * kPage * D;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, bytes, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, bytes, kRsrcWord3);
-#pragma unroll
-        for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + 64 * s, 0, 0);
-#pragma unroll
-        for (int t = 0; t < 4; t++)
-#pragma unroll
-            for (int cc = 0; cc < D / 32; cc++)
-                pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D * 2 + 64 * cc, 0, 0);
-    };
-
-    float m_run = -INFINITY, l_run = 0.f, smax = -INFINITY;
-    f32x4 oacc[NB];
-
-    // One pass over the chunk's pages, with the result published to LDS.
-    // EXACT: online softmax against the running max (raised lazily).  Else
-    // the unified-max softmax: every exponential is taken against the
-    // caller's phi, with no running max, no rescale and no cross-lane max;
-    // smax only tracks the lane's largest raw score, so that a row leaving
-    // the safe window around phi can be detected after the pass.
-    auto pass = [&](auto EXACT) {
-        constexpr bool exact = decltype(EXACT)::value;
-        m_run = exact ? -INFINITY : phi_l2;
-        l_run = 0.f;
-        smax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NB; i++) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        auto compute = [&](const PageBuf<D>& pb, int j) {
+        const int voff_k = col * D * 2 + 16 * grp;
+        const int voff_v = 4 * grp * D * 2 + 4 * col;
+        // page j of the chunk; past the chunk the descriptor is empty and the
+        // loads return zeros without touching memory
+        auto load = [&](PageBuf<D>& pb, int j) {
             const int pg = pg0 + j;
-            f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[0]), qf[0],
-                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-            for (int ks = 1; ks < KS; ks++)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[ks]), qf[ks], s, 0, 0, 0);
-            // s[r] is the score of token pg*16 + 4grp + r for head col
-            if (pg * kPage + kPage > tok1) {
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    if (pg * kPage + 4 * grp + r >= tok1) s[r] = -INFINITY;
-            }
-            float m_eff;
-            if (exact) {
-                float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-                mx = max_xor32(max_xor16(mx));
-                const float m_new = fmaxf(m_run, mx * sl2);
-                if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThresh)) {
-                    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-                    l_run *= alpha;
-#pragma unroll
-                    for (int i = 0; i < NB; i++) oacc[i] *= alpha;
-                    m_run = m_new;
-                }
-                m_eff = (m_run == -INFINITY) ? 0.f : m_run;
-            } else {
-                smax = fmaxf(smax, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-                m_eff = phi_l2;
-            }
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m_eff));
-            const uint32_t p01 = pack_bf16x2(p[0], p[1]), p23 = pack_bf16x2(p[2], p[3]);
-            // the row sum adds the bf16-rounded P that meets V
-            l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-            const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
-#pragma unroll
-            for (int cc = 0; cc < D / 32; cc++) {
-                const uint32_t v0 = pb.v[0][cc], v1 = pb.v[1][cc], v2 = pb.v[2][cc], v3 = pb.v[3][cc];
-                const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x05040100u),
-                                                                 __builtin_amdgcn_perm(v3, v2, 0x05040100u)});
-                const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x07060302u),
-                                                                 __builtin_amdgcn_perm(v3, v2, 0x07060302u)});
-                oacc[2 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pt, oacc[2 * cc], 0, 0, 0);
-                oacc[2 * cc + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pt, oacc[2 * cc + 1], 0, 0, 0);
-            }
+            const int phys = phys_of(min(j, npg - 1));
+            const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(kPage, tok1 - pg * kPage)) * D * 2);
+            const size_t off = ((size_t)phys * a.Hkv + kvh) * kPage * D;
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, bytes, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, bytes, kRsrcWord3);
+    #pragma unroll
+            for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + 64 * s, 0, 0);
+    #pragma unroll
+            for (int t = 0; t < 4; t++)
+    #pragma unroll
+                for (int cc = 0; cc < D / 32; cc++)
+                    pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D * 2 + 64 * cc, 0, 0);
         };
 
-        // pages j = wave, wave + 4, ... with the next page's loads in flight;
-        // the loads are unconditional so that each wait covers exactly one page
-        const int nj = npg > wave ? (npg - wave + 3) / 4 : 0;
-        PageBuf<D> ba, bb;
-        load(ba, wave);
-        for (int n = 0; n < nj; n += 2) {
-            load(bb, wave + 4 * (n + 1));
-            compute(ba, wave + 4 * n);
-            if (n + 1 >= nj) break;
-            load(ba, wave + 4 * (n + 2));
-            compute(bb, wave + 4 * (n + 1));
-        }
-        l_run = sum_xor32(sum_xor16(l_run));   // tokens of the four lane groups
-        if (!exact) smax = max_xor32(max_xor16(smax));
+        float m_run = -INFINITY, l_run = 0.f, smax = -INFINITY;
+        f32x4 oacc[NB];
 
-        // publish this wavefront's state
-        if (grp == 0) {
-            s_m[wave][col] = m_run;
-            s_l[wave][col] = l_run;
-            s_x[wave][col] = smax;
-        }
-#pragma unroll
-        for (int i = 0; i < NB; i++)
-#pragma unroll
-            for (int r = 0; r < 4; r++)   // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2
-                s_o[wave][col][32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1)] = oacc[i][r];
-        __syncthreads();
-    };
+        // One pass over the chunk's pages, with the result published to LDS.
+        // EXACT: online softmax against the running max (raised lazily).  Else
+        // the unified-max softmax: every exponential is taken against the
+        // caller's phi, with no running max, no rescale and no cross-lane max;
+        // smax only tracks the lane's largest raw score, so that a row leaving
+        // the safe window around phi can be detected after the pass.
+        auto pass = [&](auto EXACT) {
+            constexpr bool exact = decltype(EXACT)::value;
+            m_run = exact ? -INFINITY : phi_l2;
+            l_run = 0.f;
+            smax = -INFINITY;
+    #pragma unroll
+            for (int i = 0; i < NB; i++) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (a.unified) {
-        pass(std::false_type{});
-        // Rows (heads < G) whose largest scaled score leaves [phi - 60,
-        // phi + 60] are recomputed with the exact pass: outside it a term
-        // exp(s - phi) can overflow the fp32 sums (or the largest one
-        // underflow).  Every thread reads the same LDS values, so the
-        // decision is uniform across the workgroup.
-        int n_out = 0;
-        for (int g = 0; g < G; g++) {
-            float M = -INFINITY;
-            for (int w = 0; w < 4; w++) M = fmaxf(M, s_x[w][g]);
-            const float z = M * a.scale - a.phi;
-            if (z > kUnifiedWindow || z < -kUnifiedWindow) n_out++;
-        }
-        if (n_out > 0) {
-            if (threadIdx.x == 0 && a.fallback_count) atomicAdd(a.fallback_count, n_out);
-            __syncthreads();   // the LDS state is rewritten by the exact pass
+            auto compute = [&](const PageBuf<D>& pb, int j) {
+                const int pg = pg0 + j;
+                f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[0]), qf[0],
+                                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    #pragma unroll
+                for (int ks = 1; ks < KS; ks++)
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[ks]), qf[ks], s, 0, 0, 0);
+                // s[r] is the score of token pg*16 + 4grp + r for head col
+                if (pg * kPage + kPage > tok1) {
+    #pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        if (pg * kPage + 4 * grp + r >= tok1) s[r] = -INFINITY;
+                }
+                float m_eff;
+                if (exact) {
+                    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+                    mx = max_xor32(max_xor16(mx));
+                    const float m_new = fmaxf(m_run, mx * sl2);
+                    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThresh)) {
+                        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+                        l_run *= alpha;
+    #pragma unroll
+                        for (int i = 0; i < NB; i++) oacc[i] *= alpha;
+                        m_run = m_new;
+                    }
+                    m_eff = (m_run == -INFINITY) ? 0.f : m_run;
+                } else {
+                    smax = fmaxf(smax, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+                    m_eff = phi_l2;
+                }
+                float p[4];
+    #pragma unroll
+                for (int r = 0; r < 4; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m_eff));
+                const uint32_t p01 = pack_bf16x2(p[0], p[1]), p23 = pack_bf16x2(p[2], p[3]);
+                // the row sum adds the bf16-rounded P that meets V
+                l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+                const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+    #pragma unroll
+                for (int cc = 0; cc < D / 32; cc++) {
+                    const uint32_t v0 = pb.v[0][cc], v1 = pb.v[1][cc], v2 = pb.v[2][cc], v3 = pb.v[3][cc];
+                    const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x05040100u),
+                                                                     __builtin_amdgcn_perm(v3, v2, 0x05040100u)});
+                    const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x07060302u),
+                                                                     __builtin_amdgcn_perm(v3, v2, 0x07060302u)});
+                    oacc[2 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pt, oacc[2 * cc], 0, 0, 0);
+                    oacc[2 * cc + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pt, oacc[2 * cc + 1], 0, 0, 0);
+                }
+            };
+
+            // pages j = wave, wave + 4, ... with the next page's loads in flight;
+            // the loads are unconditional so that each wait covers exactly one page
+            const int nj = npg > wave ? (npg - wave + 3) / 4 : 0;
+            PageBuf<D> ba, bb;
+            load(ba, wave);
+            for (int n = 0; n < nj; n += 2) {
+                load(bb, wave + 4 * (n + 1));
+                compute(ba, wave + 4 * n);
+                if (n + 1 >= nj) break;
+                load(ba, wave + 4 * (n + 2));
+                compute(bb, wave + 4 * (n + 1));
+            }
+            l_run = sum_xor32(sum_xor16(l_run));   // tokens of the four lane groups
+            if (!exact) smax = max_xor32(max_xor16(smax));
+
+            // publish this wavefront's state
+            if (grp == 0) {
+                s_m[wave][col] = m_run;
+                s_l[wave][col] = l_run;
+                s_x[wave][col] = smax;
+            }
+    #pragma unroll
+            for (int i = 0; i < NB; i++)
+    #pragma unroll
+                for (int r = 0; r < 4; r++)   // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2
+                    s_o[wave][col][32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1)] = oacc[i][r];
+            __syncthreads();
+        };
+
+        if (a.unified) {
+            pass(std::false_type{});
+            // Rows (heads < G) whose largest scaled score leaves [phi - 60,
+            // phi + 60] are recomputed with the exact pass: outside it a term
+            // exp(s - phi) can overflow the fp32 sums (or the largest one
+            // underflow).  Every thread reads the same LDS values, so the
+            // decision is uniform across the workgroup.
+            int n_out = 0;
+            for (int g = 0; g < G; g++) {
+                float M = -INFINITY;
+                for (int w = 0; w < 4; w++) M = fmaxf(M, s_x[w][g]);
+                const float z = M * a.scale - a.phi;
+                if (z > kUnifiedWindow || z < -kUnifiedWindow) n_out++;
+            }
+            if (n_out > 0) {
+                if (threadIdx.x == 0 && a.fallback_count) atomicAdd(a.fallback_count, n_out);
+                __syncthreads();   // the LDS state is rewritten by the exact pass
+                pass(std::true_type{});
+            }
+        } else {
             pass(std::true_type{});
         }
-    } else {
-        pass(std::true_type{});
-    }
 
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int g = idx / D, d = idx % D;
-        float M = -INFINITY;
-        for (int w = 0; w < 4; w++) M = fmaxf(M, s_m[w][g]);
-        float lt = 0.f, ot = 0.f;
-        if (M != -INFINITY) {
-            for (int w = 0; w < 4; w++) {
-                const float wt = (s_m[w][g] == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
-                lt = fmaf(wt, s_l[w][g], lt);
-                ot = fmaf(wt, s_o[w][g][d], ot);
+        for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+            const int g = idx / D, d = idx % D;
+            float M = -INFINITY;
+            for (int w = 0; w < 4; w++) M = fmaxf(M, s_m[w][g]);
+            float lt = 0.f, ot = 0.f;
+            if (M != -INFINITY) {
+                for (int w = 0; w < 4; w++) {
+                    const float wt = (s_m[w][g] == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
+                    lt = fmaf(wt, s_l[w][g], lt);
+                    ot = fmaf(wt, s_o[w][g][d], ot);
+                }
+            }
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const float ov = ot * inv;
+            const float lse = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
+            const size_t row = (size_t)b * a.Hq + kvh * G + g;
+            if (nsplit == 1) {
+                if (a.out_f32) ((float*)a.o)[row * D + d] = ov;
+                else ((uint16_t*)a.o)[row * D + d] = f32_to_bf16(ov);
+                if (a.lse && d == 0) a.lse[row] = lse;
+            } else {
+                a.ws_o[(row * a.max_splits + c) * D + d] = ov;
+                if (d == 0) a.ws_lse[row * a.max_splits + c] = lse;
             }
         }
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const float ov = ot * inv;
-        const float lse = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
-        const size_t row = (size_t)b * a.Hq + kvh * G + g;
-        if (nsplit == 1) {
-            if (a.out_f32) ((float*)a.o)[row * D + d] = ov;
-            else ((uint16_t*)a.o)[row * D + d] = f32_to_bf16(ov);
-            if (a.lse && d == 0) a.lse[row] = lse;
-        } else {
-            a.ws_o[(row * a.max_splits + c) * D + d] = ov;
-            if (d == 0) a.ws_lse[row * a.max_splits + c] = lse;
-        }
-    }
-    __syncthreads();   // s_o is rewritten by the next item
+        __syncthreads();   // s_o is rewritten by the next item
     };
     // persistent workgroups walk the (chunk, kv head, sequence) items; empty
     // chunks of short sequences cost a few scalar instructions

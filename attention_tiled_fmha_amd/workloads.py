@@ -12,7 +12,8 @@ Storage conventions (see ``include/attn.h``):
   (page, kv head) contiguous in memory;
 * block tables are int32 [B, max_pages]; entries past a sequence's last page
   hold 0 (a valid page, never read);
-* bf16 tensors are carried on the host as uint16 bit patterns.
+* bf16 tensors are carried on the host as uint16 bit patterns;
+* FP8 caches are OCP E4M3 bytes (uint8) with one scale per tensor.
 
 Draw order for a workload (one ``numpy.random.Generator(PCG64(seed))``):
 lengths, page permutation, Q, K pool, V pool.  Large pools are drawn in
@@ -49,6 +50,28 @@ def bf16_bits(x):
     if nan.any():
         out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
     return out
+
+
+def e4m3_bits(x, scale=1.0):
+    """Quantise x / scale to OCP FP8 E4M3 bytes (uint8): round to nearest,
+    ties to even, saturating at +-448; the stored value is scale * e4m3(byte).
+    E4M3 keeps 3 mantissa bits; its exponent field (bias 7) spans 2^-6 .. 2^8,
+    with subnormals in steps of 2^-9 below 2^-6."""
+    y = np.asarray(x, np.float64) / float(scale)
+    a = np.minimum(np.abs(y), 448.0)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    step = np.exp2(e - 3)                       # spacing of E4M3 values in that binade
+    r = np.minimum(np.rint(a / step) * step, 448.0)   # rint: ties to even
+    with np.errstate(divide="ignore"):
+        er = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    normal = r >= 2.0 ** -6
+    exp_field = np.where(normal, er + 7, 0)
+    mant = np.where(normal, (r / np.exp2(er) - 1.0) * 8.0, r / 2.0 ** -9)
+    code = (exp_field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(np.signbit(y) & (r > 0), code | 0x80, code)
+    return code.astype(np.uint8)
 
 
 def bf16_to_f32(bits):
@@ -171,6 +194,30 @@ def paged_decode_inputs(B, Hq, Hkv, D, dtype, seed, lengths=None,
                 kv_lens=lengths, B=B, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype,
                 page_size=page_size, scale=1.0 / math.sqrt(D), seed=seed,
                 max_kv_len=int(lengths.max(initial=0)))
+
+
+def paged_decode_fp8_inputs(B, Hq, Hkv, D, seed, lengths=None, length_range=(512, 8192),
+                            length_dist="uniform", kv_scale=1.0 / 32, page_size=PAGE_SIZE,
+                            tail_garbage=True):
+    """Paged decode over an FP8 (OCP E4M3) cache: bf16 queries; K and V are
+    N(0,1) draws quantised to E4M3 bytes with one per-tensor scale each
+    (``kv_scale``: stored value = kv_scale * e4m3(byte)).  Same draw order and
+    layout as ``paged_decode_inputs``; the unused slots of each last page hold
+    the largest code (448 * kv_scale) so that any read past kv_len shows."""
+    d = paged_decode_inputs(B, Hq, Hkv, D, "bf16", seed, lengths=lengths,
+                            length_range=length_range, length_dist=length_dist,
+                            page_size=page_size, tail_garbage=False)
+    gen = generator(seed + 7919)
+    pool = d["k_pages"].shape[0]
+    k = e4m3_bits(normal(gen, (pool, Hkv, page_size, D), "f32"), kv_scale)
+    v = e4m3_bits(normal(gen, (pool, Hkv, page_size, D), "f32"), kv_scale)
+    if tail_garbage:
+        for b, L in enumerate(np.asarray(d["kv_lens"])):
+            if L % page_size:
+                pg = d["block_table"][b, (L - 1) // page_size]
+                k[pg, :, L % page_size:, :] = 0x7E
+                v[pg, :, L % page_size:, :] = 0x7E
+    return d | dict(k_pages=k, v_pages=v, dtype="fp8", k_scale=kv_scale, v_scale=kv_scale)
 
 
 def cascade_inputs(R, H, D, dtype, seed, prefix_len=4096, suffix_range=(128, 1024),

@@ -50,6 +50,12 @@ def load(path=_LIB_PATH):
     lib.oracle_decode_paged.argtypes = [vp, vp, vp, ip, vp, vp, dp, dp, ip, ip,
                                         ip, ip, ip, ip, ctypes.c_long,
                                         ctypes.c_double, ip]
+    lib.oracle_decode_paged_fp8.restype = ip
+    cd = ctypes.c_double
+    lib.oracle_decode_paged_fp8.argtypes = [vp, ip, vp, vp, cd, cd, vp, vp, dp, dp, ip, ip, ip,
+                                            ip, ip, ip, ctypes.c_long, cd, ip]
+    lib.oracle_e4m3_value.restype = cd
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_merge_states.restype = None
     lib.oracle_merge_states.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_long, ip]
     lib.oracle_unified_fallback_count.restype = ctypes.c_long
@@ -144,6 +150,41 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale, threads=None,
                                  float(scale), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_decode_paged failed ({rc})")
+    return o, lse
+
+
+def e4m3_value(byte, lib=None):
+    """Value of one OCP FP8 E4M3 byte (NaN for S.1111.111), from oracle.c."""
+    lib = lib or _get()
+    return lib.oracle_e4m3_value(int(byte) & 0xFF)
+
+
+def decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, kv_lens, scale,
+                     threads=None, lib=None):
+    """Paged decode over an FP8 (OCP E4M3) cache with per-tensor scales.
+
+    q [B,Hq,D] (bf16 bits as uint16, or fp32/fp64); k_pages, v_pages uint8
+    [P,Hkv,page,D] holding E4M3 bytes, dequantised as scale * e4m3(byte);
+    block_table int32 [B,maxp]; kv_lens int32 [B].  Returns (o, lse) in fp64.
+    """
+    lib = lib or _get()
+    q = np.ascontiguousarray(q)
+    k_pages = np.ascontiguousarray(k_pages, dtype=np.uint8)
+    v_pages = np.ascontiguousarray(v_pages, dtype=np.uint8)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    kl = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    B, Hq, D = q.shape
+    P, Hkv, page, Dk = k_pages.shape
+    if Dk != D or v_pages.shape != k_pages.shape or bt.shape[0] != B or kl.shape != (B,):
+        raise ValueError("shape mismatch")
+    o = np.zeros((B, Hq, D), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    rc = lib.oracle_decode_paged_fp8(_ptr(q), _dtype_code(q), _ptr(k_pages), _ptr(v_pages),
+                                     float(k_scale), float(v_scale), _ptr(bt), _ptr(kl),
+                                     _dptr(o), _dptr(lse), B, Hq, Hkv, D, page, bt.shape[1], P,
+                                     float(scale), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_decode_paged_fp8 failed ({rc})")
     return o, lse
 
 

@@ -44,7 +44,12 @@
  *     results are combined at the end; the formula is not printed there.)
  *
  * Element types: inputs may be fp64, fp32 or bf16 (given as raw 16-bit
- * patterns); every element is widened to fp64 exactly before use.
+ * patterns); every element is widened to fp64 exactly before use.  A paged
+ * cache may also hold 8-bit floats (OCP FP8 E4M3, one byte per element) with
+ * one scale per tensor: the element's value is scale * e4m3(byte), and
+ * attention is the plain definition on those values (quantised caches are
+ * named as an inference optimisation on the TensorRT-LLM FMHA page,
+ * sections 3, 4 and 7; the format is the OCP 8-bit floating point one).
  */
 #include <math.h>
 #include <stdint.h>
@@ -69,6 +74,25 @@ static double load_elem(const void *base, int dtype, size_t idx)
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/*
+ * OCP FP8 E4M3 byte -> fp64, from the format's definition: 1 sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m/8 * 2^-6; the pattern S.1111.111 is NaN (there is no
+ * infinity), so the largest finite magnitude is 1.75 * 2^8 = 448.
+ */
+double oracle_e4m3_value(uint8_t byte)
+{
+    const int sign = byte >> 7, e = (byte >> 3) & 15, m = byte & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
 }
 
 /*
@@ -231,6 +255,68 @@ int oracle_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                 const size_t row = (size_t)b * Hq + h;
                 for (int c = 0; c < D; c++)
                     Q[c] = load_elem(q, dtype, row * D + c);
+                attend_rows(Q, K, V, 1, L, D, 0, scale, S, o + row * D, lse + row);
+            }
+        }
+        free(K); free(V); free(Q); free(S);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Paged decode over an FP8 cache: k_pages and v_pages are E4M3 bytes
+ * [num_pages][Hkv][page_size][D], dequantised as k_scale * e4m3(byte) and
+ * v_scale * e4m3(byte); q is in dtype q_dtype.  Everything else as
+ * oracle_decode_paged (the same gather, then the plain attention of one
+ * query row over the dequantised keys and values).
+ */
+int oracle_decode_paged_fp8(const void *q, int q_dtype, const uint8_t *k_pages,
+                            const uint8_t *v_pages, double k_scale, double v_scale,
+                            const int32_t *block_table, const int32_t *kv_lens,
+                            double *o, double *lse, int B, int Hq, int Hkv, int D,
+                            int page_size, int max_pages, long num_pages, double scale,
+                            int nthreads)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || page_size <= 0)
+        return -1;
+    for (int b = 0; b < B; b++) {
+        const int L = kv_lens[b];
+        if (L < 0 || (L + page_size - 1) / page_size > max_pages)
+            return -1;
+        for (int p = 0; p < (L + page_size - 1) / page_size; p++) {
+            const int32_t pg = block_table[(size_t)b * max_pages + p];
+            if (pg < 0 || pg >= num_pages)
+                return -1;
+        }
+    }
+    const int group = Hq / Hkv;
+    int failed = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic)
+    for (long bk = 0; bk < (long)B * Hkv; bk++) {
+        const int b = (int)(bk / Hkv), kvh = (int)(bk % Hkv);
+        const int L = kv_lens[b];
+        double *K = malloc(sizeof(double) * ((size_t)L * D + 1));
+        double *V = malloc(sizeof(double) * ((size_t)L * D + 1));
+        double *Q = malloc(sizeof(double) * ((size_t)D + 1));
+        double *S = malloc(sizeof(double) * ((size_t)L + 1));
+        if (!K || !V || !Q || !S) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            for (int t = 0; t < L; t++) {
+                const size_t page = (size_t)block_table[(size_t)b * max_pages + t / page_size];
+                const size_t src = ((page * Hkv + kvh) * page_size + t % page_size) * D;
+                for (int c = 0; c < D; c++) {
+                    K[(size_t)t * D + c] = k_scale * oracle_e4m3_value(k_pages[src + c]);
+                    V[(size_t)t * D + c] = v_scale * oracle_e4m3_value(v_pages[src + c]);
+                }
+            }
+            for (int g = 0; g < group; g++) {
+                const int h = kvh * group + g;
+                const size_t row = (size_t)b * Hq + h;
+                for (int c = 0; c < D; c++)
+                    Q[c] = load_elem(q, q_dtype, row * D + c);
                 attend_rows(Q, K, V, 1, L, D, 0, scale, S, o + row * D, lse + row);
             }
         }

@@ -445,10 +445,65 @@ def check_unified_fallback(lib):
         assert 0 < ref < Hq * sum((L + 15) // 16 for L in lens), "case should mix in and out"
 
 
+# --- 18. FP8 (OCP E4M3) caches ------------------------------------------------
+
+def check_e4m3_values(lib):
+    """Values that the OCP 8-bit floating point format fixes for E4M3: 1.0 is
+    0x38, the largest finite value 448 is 0x7E, the smallest normal 2^-6 is
+    0x08, the smallest subnormal 2^-9 is 0x01, S.1111.111 is NaN, the top bit
+    is the sign; the positive codes increase strictly; the generator's own
+    round-to-nearest encoder inverts the decoder on every finite nonzero code;
+    every value is exact in bf16."""
+    v = [oracle.e4m3_value(b, lib=lib) for b in range(256)]
+    assert v[0x00] == 0.0 and math.copysign(1.0, v[0x80]) == -1.0, "zeros"
+    assert v[0x38] == 1.0 and v[0x40] == 2.0 and v[0x30] == 0.5, "one, two, half"
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0, "largest finite"
+    assert v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9, \
+        "normal / subnormal boundary"
+    assert math.isnan(v[0x7F]) and math.isnan(v[0xFF]), "NaN codes"
+    pos = v[0x00:0x7F]
+    assert all(a < b for a, b in zip(pos, pos[1:])), "positive codes not increasing"
+    assert all(v[b | 0x80] == -v[b] for b in range(0x7F)), "sign bit"
+    fin = [b for b in range(256) if not math.isnan(v[b]) and v[b] != 0.0]
+    assert list(wl.e4m3_bits(np.array([v[b] for b in fin]))) == fin, "encoder round trip"
+    x = np.array([v[b] for b in fin], np.float32)
+    assert np.array_equal(wl.bf16_to_f32(wl.bf16_bits(x)), x), "E4M3 values exact in bf16"
+
+
+def check_decode_fp8(lib):
+    """The FP8 decode is the plain decode of the dequantised cache: it equals
+    oracle.decode_paged on scale * value arrays (built here from the pinned
+    value table) for GQA, ragged lengths and unequal k / v scales; and with
+    every key equal the weights are uniform (closed form for O and lse)."""
+    table = np.array([oracle.e4m3_value(b, lib=lib) for b in range(256)])
+    lens = [1, 15, 16, 17, 70]
+    Hq, Hkv, D = 4, 2, 16
+    d = wl.paged_decode_fp8_inputs(len(lens), Hq, Hkv, D, 31, lengths=lens)
+    ks, vs = 0.75, 1.0 / 16
+    bt, kl, sc = d["block_table"], d["kv_lens"], d["scale"]
+    o8, l8 = oracle.decode_paged_fp8(d["q"], d["k_pages"], d["v_pages"], ks, vs, bt, kl, sc,
+                                     lib=lib)
+    qf = wl.bf16_to_f32(d["q"]).astype(np.float64)
+    o, l = oracle.decode_paged(qf, ks * table[d["k_pages"]], vs * table[d["v_pages"]], bt, kl,
+                               sc, lib=lib)
+    _close(o8, o, 1e-14, "fp8 decode vs dequantised decode")
+    _close(l8, l, 1e-13, "fp8 decode lse")
+    k1 = np.full_like(d["k_pages"], 0x38)          # every key = 1.0 * 2.0
+    o1, l1 = oracle.decode_paged_fp8(d["q"], k1, d["v_pages"], 2.0, vs, bt, kl, sc, lib=lib)
+    for b, L in enumerate(lens):
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            vals = [vs * table[d["v_pages"][bt[b, t // 16], kvh, t % 16]] for t in range(L)]
+            _close(o1[b, h], np.mean(vals, axis=0), 1e-14, f"fp8 uniform O L={L}")
+            s = sc * 2.0 * math.fsum(qf[b, h])
+            _close(l1[b, h], s + math.log(L), 1e-13, f"fp8 uniform lse L={L}")
+
+
 ALL_CHECKS = [
     check_hand_2x2, check_identical_keys, check_dominant_score,
     check_single_key_and_row0, check_scale_zero, check_brute_force, check_scipy,
     check_rows_sum_to_one, check_permutation, check_merge_split, check_merge_algebra,
     check_cascade, check_decode_vs_prefill, check_gqa_mapping, check_token_set,
     check_lse_dropped_page, check_tail_garbage, check_bf16_widening, check_unified_fallback,
+    check_e4m3_values, check_decode_fp8,
 ]

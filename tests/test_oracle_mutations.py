@@ -37,6 +37,16 @@ MUTATIONS = {
     "fallback score unscaled": ("const double s = scale * dot;", "const double s = dot;"),
     "fallback over the whole sequence": ("const int c1 = c0 + split_tokens < L ? c0 + split_tokens : L;",
                                          "const int c1 = L;"),
+    "e4m3 exponent bias 8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+                             "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "e4m3 subnormals flushed": ("v = ldexp((double)m / 8.0, -6);", "v = 0.0;"),
+    "e4m3 subnormal exponent": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
+    "e4m3 sign dropped": ("return sign ? -v : v;", "return v;"),
+    "e4m3 no NaN code": ("if (e == 15 && m == 7)\n        return NAN;", ""),
+    "fp8 key scale ignored": ("K[(size_t)t * D + c] = k_scale * oracle_e4m3_value",
+                              "K[(size_t)t * D + c] = oracle_e4m3_value"),
+    "fp8 scales swapped": ("V[(size_t)t * D + c] = v_scale * oracle_e4m3_value",
+                           "V[(size_t)t * D + c] = k_scale * oracle_e4m3_value"),
 }
 
 

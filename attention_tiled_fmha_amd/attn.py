@@ -14,7 +14,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
 
-BF16, F32 = 0, 1
+BF16, F32, FP8_E4M3 = 0, 1, 2
 _lib = None
 
 # Every symbol include/attn.h declares, with (restype, argtypes).
@@ -29,6 +29,8 @@ SIGNATURES = {
                                _i, _i, _f, _vp, _sz, _vp]),
     "attn_decode_paged_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                   _i, _i, _i, _f, _vp, _sz, _vp, _vp]),
+    "attn_decode_paged_fp8": (_i, [_vp, _vp, _vp, _f, _f, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                   _i, _i, _i, _i, _f, _vp, _sz, _vp, _vp]),
     "attn_merge_states": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp]),
     "attn_shared_prefix_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_decode_shared_prefix": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
@@ -177,6 +179,44 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse=None, ma
         B, Hq, Hkv, D, page, block_table.shape[1], int(max_kv_len), dt, _dtype(o),
         float(scale), _p(workspace), ws_bytes, _stream(stream), ctypes.byref(opts)),
         "attn_decode_paged")
+
+
+def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, kv_lens, o,
+                          lse=None, max_kv_len=None, scale=None, workspace=None, split_tokens=0,
+                          stream=None):
+    """attn_decode_paged over an FP8 cache: q bf16 [B,Hq,D]; k_pages, v_pages
+    uint8 [P,Hkv,16,D] holding OCP E4M3 bytes, the cached values being
+    k_scale * e4m3 and v_scale * e4m3; o bf16 or fp32 [B,Hq,D]."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"),
+                 (block_table, "block_table"), (kv_lens, "kv_lens"), (o, "o")):
+        _dense(t, n)
+    if max_kv_len is None:
+        raise ValueError("max_kv_len (host-side bound of kv_lens) is required")
+    B, Hq, D = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    if o.shape != q.shape or v_pages.shape != k_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if q.dtype != torch.bfloat16 or k_pages.dtype != torch.uint8 or v_pages.dtype != torch.uint8:
+        raise TypeError("q must be bf16 and the pages uint8 (E4M3 bytes)")
+    if block_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
+        raise TypeError("block_table and kv_lens must be int32")
+    if block_table.shape[0] != B or kv_lens.shape != (B,):
+        raise ValueError("block_table / kv_lens shape mismatch")
+    if lse is not None:
+        _dense(lse, "lse")
+        if lse.shape != (B, Hq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, Hq]")
+    scale = D ** -0.5 if scale is None else scale
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, D, max_kv_len, split_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    opts = DecodeOpts(split_tokens=int(split_tokens))
+    _check(load().attn_decode_paged_fp8(
+        _p(q), _p(k_pages), _p(v_pages), float(k_scale), float(v_scale), _p(block_table),
+        _p(kv_lens), _p(o), _p(lse), B, Hq, Hkv, D, page, block_table.shape[1], int(max_kv_len),
+        _dtype(o), float(scale), _p(workspace), ws_bytes, _stream(stream), ctypes.byref(opts)),
+        "attn_decode_paged_fp8")
 
 
 def attn_merge_states(o_a, lse_a, o_b, lse_b, stream=None):

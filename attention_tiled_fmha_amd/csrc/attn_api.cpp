@@ -73,16 +73,18 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
                   int head_dim, int page_size, int max_pages_per_seq, int max_kv_len, int dtype,
                   int o_dtype, float scale, void* workspace, size_t workspace_bytes,
                   void* stream, int requested_split, bool unified = false, float phi = 0.f,
-                  int* fallback_count = nullptr) {
-    if (!dtype_ok(dtype) || !dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
+                  int* fallback_count = nullptr, float k_scale = 1.f, float v_scale = 1.f) {
+    // dtype ATTN_FP8_E4M3: bf16 queries over an FP8 cache (matrix-core kernel only)
+    const bool fp8 = dtype == ATTN_FP8_E4M3;
+    if ((!fp8 && !dtype_ok(dtype)) || !dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
     if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || max_kv_len < 0 || max_pages_per_seq < 0)
         return ATTN_E_SHAPE;
     if (heads_q % heads_kv) return ATTN_E_SHAPE;
     if (!dim_ok(head_dim) || page_size != kPageSize) return ATTN_E_UNSUPPORTED;
     const int G = heads_q / heads_kv;
-    if (G != 1 && G != 2 && G != 4 && G != 8) return ATTN_E_UNSUPPORTED;
+    if (G > 16) return ATTN_E_UNSUPPORTED;
     if ((long)max_pages_per_seq * page_size < max_kv_len) return ATTN_E_SHAPE;
-    if (!scale_ok(scale)) return ATTN_E_ARG;
+    if (!scale_ok(scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return ATTN_E_ARG;
     if (batch == 0) return ATTN_OK;
     if (!q || !k_pages || !v_pages || !o || (!block_table && max_kv_len > 0))
         return ATTN_E_NULL;
@@ -115,14 +117,18 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
     a.max_splits = max_splits;
     a.in_f32 = dtype == ATTN_F32;
     a.out_f32 = o_dtype == ATTN_F32;
+    a.in_fp8 = fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     a.scale = scale;
     a.unified = unified;
     a.phi = phi;
     a.fallback_count = fallback_count;
-    // bf16 caches go to the matrix-core kernel; fp32 and chunks longer than
-    // it takes go to the vector kernel (which has no unified-max mode)
+    // bf16 and FP8 caches go to the matrix-core kernel; fp32 caches and
+    // chunks longer than it takes go to the vector kernel (no unified-max
+    // mode, no FP8, G in {1, 2, 4, 8})
     if (attn::decode_mfma_supported(a)) return check_hip(attn::launch_decode_mfma(a, (hipStream_t)stream));
-    if (unified) return ATTN_E_UNSUPPORTED;
+    if (unified || fp8 || (G != 1 && G != 2 && G != 4 && G != 8)) return ATTN_E_UNSUPPORTED;
     return check_hip(attn::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -187,6 +193,7 @@ int attn_decode_paged_ex(const void* q, const void* k_pages, const void* v_pages
                          int max_pages_per_seq, int max_kv_len, int dtype, int o_dtype,
                          float scale, void* workspace, size_t workspace_bytes, void* stream,
                          const attn_decode_opts* opts) {
+    if (!dtype_ok(dtype)) return ATTN_E_UNSUPPORTED;   // FP8 caches: attn_decode_paged_fp8
     if (batch > 0 && !kv_lens) return ATTN_E_NULL;
     const int requested = opts ? opts->split_tokens : 0;
     if (requested < 0) return ATTN_E_ARG;
@@ -197,6 +204,22 @@ int attn_decode_paged_ex(const void* q, const void* k_pages, const void* v_pages
                          lse, batch, heads_q, heads_kv, head_dim, page_size, max_pages_per_seq,
                          max_kv_len, dtype, o_dtype, scale, workspace, workspace_bytes, stream,
                          requested, unified, phi, opts ? opts->fallback_count : nullptr);
+}
+
+int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_pages,
+                          float k_scale, float v_scale, const int32_t* block_table,
+                          const int32_t* kv_lens, void* o, float* lse, int batch, int heads_q,
+                          int heads_kv, int head_dim, int page_size, int max_pages_per_seq,
+                          int max_kv_len, int o_dtype, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream, const attn_decode_opts* opts) {
+    if (batch > 0 && !kv_lens) return ATTN_E_NULL;
+    const int requested = opts ? opts->split_tokens : 0;
+    if (requested < 0) return ATTN_E_ARG;
+    if (opts && opts->use_unified_max) return ATTN_E_UNSUPPORTED;
+    return decode_common(q, k_pages, v_pages, block_table, max_pages_per_seq, kv_lens, 0, o,
+                         lse, batch, heads_q, heads_kv, head_dim, page_size, max_pages_per_seq,
+                         max_kv_len, ATTN_FP8_E4M3, o_dtype, scale, workspace, workspace_bytes,
+                         stream, requested, false, 0.f, nullptr, k_scale, v_scale);
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -241,6 +264,7 @@ int attn_decode_shared_prefix(const void* q, const void* k_pages, const void* v_
                               int batch, int heads_q, int heads_kv, int head_dim, int page_size,
                               int dtype, int o_dtype, float scale, void* workspace,
                               size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return ATTN_E_UNSUPPORTED;
     if (prefix_len < 0) return ATTN_E_SHAPE;
     const int npages = (prefix_len + kPageSize - 1) / kPageSize;
     if (dtype != ATTN_BF16 || prefix_len == 0) {

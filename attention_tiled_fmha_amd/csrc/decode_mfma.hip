@@ -56,11 +56,24 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit data, no swizzle
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+// One page's operands in flight, per lane.
+template <int D, bool FP8>
 struct PageBuf {
-    u32x4 k[D / 32];          // K A operand of k-step s
+    u32x4 k[D / 32];          // K A operand of k-step s (8 bf16)
     uint32_t v[4][D / 32];    // V: token 4(l/16) + t, dims 32c + 2(l%16), +1
 };
+template <int D>
+struct PageBuf<D, true> {
+    u32x2 k[D / 32];          // K of k-step s: 8 E4M3 bytes, dims 32s + 8(l/16) ..
+    uint32_t v[4][D / 64];    // V: token 4(l/16) + t, dims 64c + 4(l%16) .. +3
+};
+
+// Two E4M3 bytes (the low or high half of w) -> two bf16, exactly (every
+// E4M3 value is a bf16 value; the conversion's scale is 1).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
 
 // (own value, value of lane ^ 16 or lane ^ 32); only used symmetrically
 __device__ __forceinline__ float max_xor16(float x) {
@@ -80,8 +93,9 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+    constexpr int EB = FP8 ? 1 : 2;   // bytes per cached element
     constexpr int KS = D / 32;   // k-steps of S^T, and 32-dim V columns
     constexpr int NB = D / 16;   // 16-dim blocks of O^T
     const int lane = threadIdx.x & 63;
@@ -119,9 +133,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         const int pg0 = tok0 / kPage, pg1 = (tok1 + kPage - 1) / kPage;
         const int npg = pg1 - pg0;
         const int32_t* table = a.block_table + (size_t)b * a.bt_stride;
-        const float sl2 = a.scale * kLog2e;
-        const uint16_t* kbase = (const uint16_t*)a.k_pages;
-        const uint16_t* vbase = (const uint16_t*)a.v_pages;
+        // an FP8 cache holds k_scale * e4m3: the key scale joins the softmax
+        // scale, the value scale multiplies the output
+        const float sl2 = a.scale * a.k_scale * kLog2e;
+        const unsigned char* kbase = (const unsigned char*)a.k_pages;
+        const unsigned char* vbase = (const unsigned char*)a.v_pages;
 
         // Q^T (B operand): head col (zero for col >= G), dims 32s + 8grp .. +7
         bf16x8 qf[KS];
@@ -140,26 +156,37 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         const int tblv = lane < npg ? table[pg0 + lane] : 0;
         auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(tblv, j); };
 
-        const int voff_k = col * D * 2 + 16 * grp;
-        const int voff_v = 4 * grp * D * 2 + 4 * col;
+        // byte offsets of this lane's K and V elements in a page tile
+        const int voff_k = col * D * EB + 8 * EB * grp;
+        const int voff_v = 4 * grp * D * EB + 4 * col;
         // page j of the chunk; past the chunk the descriptor is empty and the
         // loads return zeros without touching memory
-        auto load = [&](PageBuf<D>& pb, int j) {
+        auto load = [&](PageBuf<D, FP8>& pb, int j) {
             const int pg = pg0 + j;
             const int phys = phys_of(min(j, npg - 1));
-            const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(kPage, tok1 - pg * kPage)) * D * 2);
-            const size_t off = ((size_t)phys * a.Hkv + kvh) * kPage * D;
+            const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(kPage, tok1 - pg * kPage)) * D * EB);
+            const size_t off = (((size_t)phys * a.Hkv + kvh) * kPage * D) * EB;
             const __amdgpu_buffer_rsrc_t rk =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, bytes, kRsrcWord3);
             const __amdgpu_buffer_rsrc_t rv =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, bytes, kRsrcWord3);
+            if constexpr (FP8) {
     #pragma unroll
-            for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + 64 * s, 0, 0);
+                for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b64(rk, voff_k + 32 * s, 0, 0);
     #pragma unroll
-            for (int t = 0; t < 4; t++)
+                for (int t = 0; t < 4; t++)
     #pragma unroll
-                for (int cc = 0; cc < D / 32; cc++)
-                    pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D * 2 + 64 * cc, 0, 0);
+                    for (int cc = 0; cc < D / 64; cc++)
+                        pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D + 64 * cc, 0, 0);
+            } else {
+    #pragma unroll
+                for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + 64 * s, 0, 0);
+    #pragma unroll
+                for (int t = 0; t < 4; t++)
+    #pragma unroll
+                    for (int cc = 0; cc < D / 32; cc++)
+                        pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D * 2 + 64 * cc, 0, 0);
+            }
         };
 
         float m_run = -INFINITY, l_run = 0.f, smax = -INFINITY;
@@ -179,13 +206,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     #pragma unroll
             for (int i = 0; i < NB; i++) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-            auto compute = [&](const PageBuf<D>& pb, int j) {
+            auto compute = [&](const PageBuf<D, FP8>& pb, int j) {
                 const int pg = pg0 + j;
-                f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[0]), qf[0],
-                                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                // K A operand of k-step ks (FP8: 8 bytes widened to bf16)
+                auto kop = [&](int ks) -> bf16x8 {
+                    if constexpr (FP8) {
+                        const uint32_t w0 = pb.k[ks][0], w1 = pb.k[ks][1];
+                        return __builtin_bit_cast(bf16x8, u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                                                e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)});
+                    } else {
+                        return __builtin_bit_cast(bf16x8, pb.k[ks]);
+                    }
+                };
+                f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(0), qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     #pragma unroll
                 for (int ks = 1; ks < KS; ks++)
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[ks]), qf[ks], s, 0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(ks), qf[ks], s, 0, 0, 0);
                 // s[r] is the score of token pg*16 + 4grp + r for head col
                 if (pg * kPage + kPage > tok1) {
     #pragma unroll
@@ -216,22 +252,48 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 // the row sum adds the bf16-rounded P that meets V
                 l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
                 const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+                if constexpr (FP8) {
+                    // per 64-dim column c: lane holds dims 64c + 4(l%16) + {0..3} of its 4
+                    // tokens; block 4c + i gathers dim offset i of the 4 tokens
     #pragma unroll
-                for (int cc = 0; cc < D / 32; cc++) {
-                    const uint32_t v0 = pb.v[0][cc], v1 = pb.v[1][cc], v2 = pb.v[2][cc], v3 = pb.v[3][cc];
-                    const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x05040100u),
-                                                                     __builtin_amdgcn_perm(v3, v2, 0x05040100u)});
-                    const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x07060302u),
-                                                                     __builtin_amdgcn_perm(v3, v2, 0x07060302u)});
-                    oacc[2 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pt, oacc[2 * cc], 0, 0, 0);
-                    oacc[2 * cc + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pt, oacc[2 * cc + 1], 0, 0, 0);
+                    for (int cc = 0; cc < D / 64; cc++) {
+                        uint32_t lo[4], hi[4];
+    #pragma unroll
+                        for (int t = 0; t < 4; t++) {
+                            lo[t] = e4m3x2_to_bf16x2<false>(pb.v[t][cc]);   // dims +0, +1
+                            hi[t] = e4m3x2_to_bf16x2<true>(pb.v[t][cc]);    // dims +2, +3
+                        }
+                        const s16x4 a0 = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u),
+                                                                         __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u)});
+                        const s16x4 a1 = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u),
+                                                                         __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)});
+                        const s16x4 a2 = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u),
+                                                                         __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u)});
+                        const s16x4 a3 = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u),
+                                                                         __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)});
+                        oacc[4 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, pt, oacc[4 * cc], 0, 0, 0);
+                        oacc[4 * cc + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, pt, oacc[4 * cc + 1], 0, 0, 0);
+                        oacc[4 * cc + 2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a2, pt, oacc[4 * cc + 2], 0, 0, 0);
+                        oacc[4 * cc + 3] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a3, pt, oacc[4 * cc + 3], 0, 0, 0);
+                    }
+                } else {
+    #pragma unroll
+                    for (int cc = 0; cc < D / 32; cc++) {
+                        const uint32_t v0 = pb.v[0][cc], v1 = pb.v[1][cc], v2 = pb.v[2][cc], v3 = pb.v[3][cc];
+                        const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x05040100u),
+                                                                         __builtin_amdgcn_perm(v3, v2, 0x05040100u)});
+                        const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x07060302u),
+                                                                         __builtin_amdgcn_perm(v3, v2, 0x07060302u)});
+                        oacc[2 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pt, oacc[2 * cc], 0, 0, 0);
+                        oacc[2 * cc + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pt, oacc[2 * cc + 1], 0, 0, 0);
+                    }
                 }
             };
 
             // pages j = wave, wave + 4, ... with the next page's loads in flight;
             // the loads are unconditional so that each wait covers exactly one page
             const int nj = npg > wave ? (npg - wave + 3) / 4 : 0;
-            PageBuf<D> ba, bb;
+            PageBuf<D, FP8> ba, bb;
             load(ba, wave);
             for (int n = 0; n < nj; n += 2) {
                 load(bb, wave + 4 * (n + 1));
@@ -252,8 +314,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     #pragma unroll
             for (int i = 0; i < NB; i++)
     #pragma unroll
-                for (int r = 0; r < 4; r++)   // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2
-                    s_o[wave][col][32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1)] = oacc[i][r];
+                for (int r = 0; r < 4; r++) {
+                    // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2 (bf16),
+                    // 64(i/4) + 4(4grp + r) + i%4 (FP8)
+                    const int dim = FP8 ? 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3)
+                                        : 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
+                    s_o[wave][col][dim] = oacc[i][r];
+                }
             __syncthreads();
         };
 
@@ -292,7 +359,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                     ot = fmaf(wt, s_o[w][g][d], ot);
                 }
             }
-            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
             const float ov = ot * inv;
             const float lse = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
             const size_t row = (size_t)b * a.Hq + kvh * G + g;
@@ -321,14 +388,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
 bool decode_mfma_supported(const DecodeArgs& a) {
     return !a.in_f32 && (a.D == 64 || a.D == 128) && a.Hq / a.Hkv <= kMaxG &&
-           a.split_tokens <= 64 * kPage;
+           a.split_tokens <= 64 * kPage && !(a.in_fp8 && a.unified);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
     const long n_items = (long)a.max_splits * a.Hkv * a.B;
     const dim3 grid((unsigned)std::min<long>(n_items, 8192));
-    if (a.D == 64) decode_mfma_kernel<64><<<grid, 256, 0, stream>>>(a);
-    else decode_mfma_kernel<128><<<grid, 256, 0, stream>>>(a);
+    if (a.in_fp8) {
+        if (a.D == 64) decode_mfma_kernel<64, true><<<grid, 256, 0, stream>>>(a);
+        else decode_mfma_kernel<128, true><<<grid, 256, 0, stream>>>(a);
+    } else {
+        if (a.D == 64) decode_mfma_kernel<64, false><<<grid, 256, 0, stream>>>(a);
+        else decode_mfma_kernel<128, false><<<grid, 256, 0, stream>>>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_splits <= 1) return e;
     return launch_decode_combine(a, stream);

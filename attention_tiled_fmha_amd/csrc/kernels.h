@@ -38,6 +38,11 @@ struct DecodeArgs {
     int B, Hq, Hkv, D;
     int split_tokens, max_splits;
     bool in_f32, out_f32;
+    // FP8 cache (matrix-core kernel only): OCP E4M3 bytes, the cached value
+    // being k_scale * e4m3 (keys) and v_scale * e4m3 (values); both scales
+    // are 1 for bf16 / fp32 caches
+    bool in_fp8;
+    float k_scale, v_scale;
     float scale;
     // unified-max softmax (matrix-core kernel only): exponentials against phi,
     // exact recompute of the chunks whose rows leave the window; the number of
@@ -48,9 +53,9 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
-// The same decode on the matrix core (bf16 cache, G <= 16 query heads per kv
-// head, chunks of at most 1024 tokens); decode_mfma_supported says whether
-// launch_decode_mfma accepts the arguments.
+// The same decode on the matrix core (bf16 or FP8 cache, G <= 16 query heads
+// per kv head, chunks of at most 1024 tokens); decode_mfma_supported says
+// whether launch_decode_mfma accepts the arguments.
 bool decode_mfma_supported(const DecodeArgs& a);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 

@@ -53,23 +53,23 @@ def bf16_bits(x):
 
 
 def e4m3_bits(x, scale=1.0):
-    """Quantise x / scale to OCP FP8 E4M3 bytes (uint8): round to nearest,
-    ties to even, saturating at +-448; the stored value is scale * e4m3(byte).
-    E4M3 keeps 3 mantissa bits; its exponent field (bias 7) spans 2^-6 .. 2^8,
-    with subnormals in steps of 2^-9 below 2^-6."""
-    y = np.asarray(x, np.float64) / float(scale)
-    a = np.minimum(np.abs(y), 448.0)
-    with np.errstate(divide="ignore"):
-        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.clip(e, -6, 8)
-    step = np.exp2(e - 3)                       # spacing of E4M3 values in that binade
-    r = np.minimum(np.rint(a / step) * step, 448.0)   # rint: ties to even
-    with np.errstate(divide="ignore"):
-        er = np.floor(np.log2(np.where(r > 0, r, 1.0)))
-    normal = r >= 2.0 ** -6
+    """Quantise x / scale (computed in float32) to OCP FP8 E4M3 bytes (uint8):
+    round to nearest, ties to even, saturating at +-448; the stored value is
+    scale * e4m3(byte).  E4M3 keeps 3 mantissa bits; its exponent field
+    (bias 7) spans 2^-6 .. 2^8, with subnormals in steps of 2^-9 below 2^-6."""
+    one = np.float32(1.0)
+    y = np.asarray(x, np.float32) / np.float32(scale)
+    a = np.minimum(np.abs(y), np.float32(448.0))
+    _, e = np.frexp(a)                          # a = f * 2^e, f in [0.5, 1)
+    e = np.clip(e - 1, -6, 8)
+    step = np.ldexp(one, e - 3).astype(np.float32)   # spacing of E4M3 values there
+    r = np.minimum(np.rint(a / step) * step, np.float32(448.0))   # rint: ties to even
+    _, er = np.frexp(r)
+    er = er - 1
+    normal = r >= np.float32(2.0 ** -6)
     exp_field = np.where(normal, er + 7, 0)
-    mant = np.where(normal, (r / np.exp2(er) - 1.0) * 8.0, r / 2.0 ** -9)
-    code = (exp_field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    mant = np.where(normal, r / np.ldexp(one, er).astype(np.float32) * 8 - 8, r * np.float32(512.0))
+    code = (exp_field.astype(np.int32) << 3) | np.rint(mant).astype(np.int32)
     code = np.where(np.signbit(y) & (r > 0), code | 0x80, code)
     return code.astype(np.uint8)
 
@@ -84,18 +84,24 @@ def _threads():
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def normal(gen, shape, dtype):
+def normal(gen, shape, dtype, e4m3_scale=1.0):
     """N(0,1) draws of ``shape`` in storage ``dtype`` ('bf16' -> uint16 bits,
-    'f32' -> float32).  Drawn in fixed chunks from child streams."""
+    'f32' -> float32, 'e4m3' -> uint8 E4M3 bytes of x / e4m3_scale).  Drawn in
+    fixed chunks from child streams."""
     n = int(np.prod(shape)) if len(shape) else 1
     nchunks = max(1, (n + _CHUNK - 1) // _CHUNK)
     seeds = gen.integers(0, 2**63 - 1, size=nchunks, dtype=np.int64)
-    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    out = np.empty(n, dtype={"bf16": np.uint16, "e4m3": np.uint8}.get(dtype, np.float32))
 
     def fill(c):
         lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
         x = generator(int(seeds[c])).standard_normal(hi - lo, dtype=np.float32)
-        out[lo:hi] = bf16_bits(x) if dtype == "bf16" else x
+        if dtype == "bf16":
+            out[lo:hi] = bf16_bits(x)
+        elif dtype == "e4m3":
+            out[lo:hi] = e4m3_bits(x, e4m3_scale)
+        else:
+            out[lo:hi] = x
 
     if nchunks == 1:
         fill(0)
@@ -204,20 +210,28 @@ def paged_decode_fp8_inputs(B, Hq, Hkv, D, seed, lengths=None, length_range=(512
     (``kv_scale``: stored value = kv_scale * e4m3(byte)).  Same draw order and
     layout as ``paged_decode_inputs``; the unused slots of each last page hold
     the largest code (448 * kv_scale) so that any read past kv_len shows."""
-    d = paged_decode_inputs(B, Hq, Hkv, D, "bf16", seed, lengths=lengths,
-                            length_range=length_range, length_dist=length_dist,
-                            page_size=page_size, tail_garbage=False)
-    gen = generator(seed + 7919)
-    pool = d["k_pages"].shape[0]
-    k = e4m3_bits(normal(gen, (pool, Hkv, page_size, D), "f32"), kv_scale)
-    v = e4m3_bits(normal(gen, (pool, Hkv, page_size, D), "f32"), kv_scale)
+    gen = generator(seed)
+    if lengths is None:
+        lo, hi = length_range
+        draw = uniform_lengths if length_dist == "uniform" else log_uniform_lengths
+        lengths = draw(gen, B, lo, hi)
+    lengths = np.asarray(lengths, np.int32)
+    pool = max(1, int(pages_for(lengths, page_size).sum()))
+    physical = gen.permutation(pool).astype(np.int32)
+    table = _tables(lengths, physical, page_size)
+    q = normal(gen, (B, Hq, D), "bf16")
+    k = normal(gen, (pool, Hkv, page_size, D), "e4m3", kv_scale)
+    v = normal(gen, (pool, Hkv, page_size, D), "e4m3", kv_scale)
     if tail_garbage:
-        for b, L in enumerate(np.asarray(d["kv_lens"])):
+        for b, L in enumerate(lengths):
             if L % page_size:
-                pg = d["block_table"][b, (L - 1) // page_size]
+                pg = table[b, (L - 1) // page_size]
                 k[pg, :, L % page_size:, :] = 0x7E
                 v[pg, :, L % page_size:, :] = 0x7E
-    return d | dict(k_pages=k, v_pages=v, dtype="fp8", k_scale=kv_scale, v_scale=kv_scale)
+    return dict(q=q, k_pages=k, v_pages=v, block_table=table, kv_lens=lengths, B=B, Hq=Hq,
+                Hkv=Hkv, D=D, dtype="fp8", page_size=page_size, scale=1.0 / math.sqrt(D),
+                seed=seed, max_kv_len=int(lengths.max(initial=0)), k_scale=kv_scale,
+                v_scale=kv_scale)
 
 
 def cascade_inputs(R, H, D, dtype, seed, prefix_len=4096, suffix_range=(128, 1024),
@@ -264,6 +278,26 @@ WORKLOADS = {
     5: "shared-prefix cascade decode, 64 requests, prefix 4096, suffix U[128,1024], "
        "H32 D128 bf16, page 16",
 }
+
+
+FP8_WORKLOADS = {
+    3: "paged decode MHA B32 H32 D128, FP8 E4M3 cache (scale 1/32), bf16 q/o, L~U[512,8192], "
+       "page 16",
+    4: "paged decode GQA B128 Hq32 Hkv8 D128, FP8 E4M3 cache (scale 1/32), bf16 q/o, "
+       "L~logU[1024,32768], page 16, split <= 512",
+}
+
+
+def fp8_workload(n, seed=None):
+    """Workloads 3 and 4 over an FP8 cache (same shapes and length draws)."""
+    seed = 1000 + n if seed is None else seed
+    if n == 3:
+        return paged_decode_fp8_inputs(32, 32, 32, 128, seed, length_range=(512, 8192),
+                                       length_dist="uniform")
+    if n == 4:
+        return paged_decode_fp8_inputs(128, 32, 8, 128, seed, length_range=(1024, 32768),
+                                       length_dist="log-uniform") | dict(split_tokens=512)
+    raise ValueError(f"no FP8 workload {n}")
 
 
 def workload(n, seed=None):

@@ -53,7 +53,9 @@ typedef enum {
     ATTN_E_ARG = 6          /* a value outside its domain (scale <= 0 or NaN)   */
 } attn_status;
 
-typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+/* ATTN_FP8_E4M3 names an FP8 KV cache (OCP E4M3 bytes); it is accepted only
+ * by attn_decode_paged_fp8, whose queries and outputs are bf16 / fp32. */
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1, ATTN_FP8_E4M3 = 2 } attn_dtype;
 
 /* Text for a status code (static storage; never NULL). */
 const char *attn_status_str(int status);
@@ -139,8 +141,8 @@ size_t attn_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int hea
  * A sequence with kv_lens[b] == 0 gets O = 0 and lse = -inf.
  * Page slots past kv_lens[b] are never used, whatever they hold.
  * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_UNSUPPORTED (page_size != 16,
- * head_dim, dtype, heads_q / heads_kv not in {1,2,4,8}), ATTN_E_WORKSPACE,
- * ATTN_E_HIP.
+ * head_dim, dtype, heads_q / heads_kv above 16 -- or, for fp32 caches, not
+ * in {1,2,4,8}), ATTN_E_WORKSPACE, ATTN_E_HIP.
  */
 int attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                       const int32_t *block_table, const int32_t *kv_lens,
@@ -191,6 +193,42 @@ int attn_decode_paged_ex(const void *q, const void *k_pages, const void *v_pages
                          int dtype, int o_dtype, float scale,
                          void *workspace, size_t workspace_bytes, void *stream,
                          const attn_decode_opts *opts);
+
+/*
+ * attn_decode_paged_fp8 -- attn_decode_paged over an FP8 KV cache.
+ *
+ * Quantised KV caches are the inference optimisation the TensorRT-LLM FMHA
+ * page (zyxy.net/?p=24414) lists in sections 3, 4 and 7; decode is bound by
+ * reading the cache, so one byte per element halves the traffic.  The cache
+ * holds OCP FP8 E4M3 bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; largest finite value 448) with one scale per tensor:
+ *     key element = k_scale * e4m3(byte),  value element = v_scale * e4m3(byte),
+ * and the result is attention over those values, exactly as
+ * attn_decode_paged computes it (the bytes are widened in registers; every
+ * E4M3 value is a bf16 value, so nothing is rounded on the way).
+ *
+ *   q, o        : [batch, heads_q, head_dim], q bf16, o `o_dtype`
+ *                 (ATTN_BF16 or ATTN_F32)
+ *   k_pages,
+ *   v_pages     : uint8 [num_pages, heads_kv, page_size, head_dim], E4M3
+ *   k_scale,
+ *   v_scale     : the per-tensor scales (finite and > 0, else ATTN_E_ARG)
+ *   opts        : as for attn_decode_paged_ex (may be NULL); only
+ *                 split_tokens is used; use_unified_max gives
+ *                 ATTN_E_UNSUPPORTED
+ *   everything else, the workspace size (attn_decode_workspace_bytes), the
+ *   preconditions and the errors: as attn_decode_paged.  heads_q / heads_kv
+ *   <= 16; chunks of at most 1024 tokens.
+ */
+int attn_decode_paged_fp8(const void *q, const void *k_pages, const void *v_pages,
+                          float k_scale, float v_scale,
+                          const int32_t *block_table, const int32_t *kv_lens,
+                          void *o, float *lse,
+                          int batch, int heads_q, int heads_kv, int head_dim,
+                          int page_size, int max_pages_per_seq, int max_kv_len,
+                          int o_dtype, float scale,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          const attn_decode_opts *opts);
 
 /*
  * attn_merge_states -- combine two partial attention states in place.

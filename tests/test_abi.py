@@ -90,7 +90,8 @@ def test_decode_checks(lib):
     assert decode(lib, maxlen=-1) == E_SHAPE
     assert decode(lib, page=32) == E_UNSUP
     assert decode(lib, D=80) == E_UNSUP
-    assert decode(lib, Hq=32, Hkv=2) == E_UNSUP       # group of 16
+    assert decode(lib, Hq=34, Hkv=2) == E_UNSUP       # group of 17
+    assert decode(lib, Hq=32, Hkv=2, dt=1) == E_UNSUP  # fp32 cache: groups of 1, 2, 4, 8 only
     assert decode(lib, odt=5) == E_UNSUP
     assert decode(lib, scale=0.0) == E_ARG
     opts = attn.DecodeOpts(split_tokens=-5)
@@ -101,6 +102,41 @@ def test_decode_checks(lib):
     assert decode(lib, maxlen=100000, maxp=6250) == E_WS
     assert decode(lib, maxlen=100000, maxp=6250, ws=FAKE, ws_bytes=need - 1) == E_WS
     assert decode(lib, B=0, q=None, k=None, v=None, bt=None, kl=None, o=None) == OK
+
+
+def decode_fp8(lib, ws=None, ws_bytes=0, opts=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.5, vs=0.25, bt=FAKE, kl=FAKE, o=FAKE, lse=None, B=2,
+             Hq=8, Hkv=2, D=128, page=16, maxp=4, maxlen=64, odt=0, scale=0.1)
+    a.update(kw)
+    return lib.attn_decode_paged_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["kl"],
+                                     a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                     a["page"], a["maxp"], a["maxlen"], a["odt"], a["scale"], ws,
+                                     ws_bytes, None, opts)
+
+
+def test_decode_fp8_checks(lib):
+    # every case here is rejected on the host, before anything is launched
+    assert decode_fp8(lib, q=None) == E_NULL
+    assert decode_fp8(lib, kl=None) == E_NULL
+    assert decode_fp8(lib, Hq=6, Hkv=4) == E_SHAPE
+    assert decode_fp8(lib, page=32) == E_UNSUP
+    assert decode_fp8(lib, D=96) == E_UNSUP
+    assert decode_fp8(lib, Hq=34, Hkv=2) == E_UNSUP
+    assert decode_fp8(lib, odt=2) == E_UNSUP          # outputs are bf16 or fp32
+    assert decode_fp8(lib, ks=0.0) == E_ARG
+    assert decode_fp8(lib, vs=float("nan")) == E_ARG
+    assert decode_fp8(lib, ks=-1.0) == E_ARG
+    assert decode_fp8(lib, scale=float("inf")) == E_ARG
+    uni = attn.DecodeOpts(use_unified_max=1)
+    assert decode_fp8(lib, opts=ctypes.byref(uni)) == E_UNSUP
+    neg = attn.DecodeOpts(split_tokens=-1)
+    assert decode_fp8(lib, opts=ctypes.byref(neg)) == E_ARG
+    need = lib.attn_decode_workspace_bytes(2, 8, 2, 128, 100000, 0)
+    assert decode_fp8(lib, maxlen=100000, maxp=6250, ws=FAKE, ws_bytes=need - 1) == E_WS
+    assert decode_fp8(lib, B=0, q=None, k=None, v=None, bt=None, kl=None, o=None) == OK
+    # the FP8 cache type is not a q / o type of the other calls
+    assert decode(lib, dt=2) == E_UNSUP
+    assert prefill(lib, dt=2) == E_UNSUP
 
 
 def test_merge_checks(lib):

@@ -290,17 +290,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 }
             };
 
-            // pages j = wave, wave + 4, ... with the next page's loads in flight;
-            // the loads are unconditional so that each wait covers exactly one page
-            const int nj = npg > wave ? (npg - wave + 3) / 4 : 0;
-            PageBuf<D, FP8> ba, bb;
-            load(ba, wave);
+            // units of PU pages (two for FP8, whose pages are half the bytes, so
+            // that as many bytes are in flight as for bf16): units j = wave,
+            // wave + 4, ... with the next unit's loads in flight; the loads are
+            // unconditional so that each wait covers exactly one unit (a page
+            // past the chunk loads zeros and is masked)
+            constexpr int PU = FP8 ? 2 : 1;
+            struct Unit {
+                PageBuf<D, FP8> p[PU];
+            };
+            auto load_u = [&](Unit& u, int j) {
+    #pragma unroll
+                for (int i = 0; i < PU; i++) load(u.p[i], PU * j + i);
+            };
+            auto compute_u = [&](const Unit& u, int j) {
+    #pragma unroll
+                for (int i = 0; i < PU; i++) compute(u.p[i], PU * j + i);
+            };
+            const int nunits = (npg + PU - 1) / PU;
+            const int nj = nunits > wave ? (nunits - wave + 3) / 4 : 0;
+            Unit ba, bb;
+            load_u(ba, wave);
             for (int n = 0; n < nj; n += 2) {
-                load(bb, wave + 4 * (n + 1));
-                compute(ba, wave + 4 * n);
+                load_u(bb, wave + 4 * (n + 1));
+                compute_u(ba, wave + 4 * n);
                 if (n + 1 >= nj) break;
-                load(ba, wave + 4 * (n + 2));
-                compute(bb, wave + 4 * (n + 1));
+                load_u(ba, wave + 4 * (n + 2));
+                compute_u(bb, wave + 4 * (n + 1));
             }
             l_run = sum_xor32(sum_xor16(l_run));   // tokens of the four lane groups
             if (!exact) smax = max_xor32(max_xor16(smax));

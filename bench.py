@@ -8,9 +8,10 @@ The bench line's workload is causal prefill in the Llama2-7B attention shape
 is its throughput in algorithmic TFLOP/s: 4*D flop per attended
 (query, key) pair, T(T+1)/2 pairs per (b, h) under the causal mask.
 
-The paged-decode workloads (MHA B32, GQA 32/8 B128, shared-prefix cascade)
-are timed in the same run and reported under "decode" in KV GB/s: unique
-K+V bytes read, the shared prefix counted once.
+The paged-decode workloads (MHA B32, GQA 32/8 B128, the same two over an
+FP8 E4M3 cache, shared-prefix cascade) are timed in the same run and reported
+under "decode" in KV GB/s: unique K+V bytes read (one byte per element for
+FP8), the shared prefix counted once.
 
 Timing: W untimed warm-up steps, then K steps bracketed by a device
 synchronisation on both sides; HIP events on the launch stream give each
@@ -174,6 +175,35 @@ def bench_decode(n, steps, warmup):
                 split_tokens=split_used, max_splits=nsplit)
 
 
+def bench_decode_fp8(n, steps, warmup):
+    """Workload n's shapes and lengths over an FP8 (OCP E4M3) cache; KV bytes
+    are one byte per element."""
+    d = wl.fp8_workload(n)
+    q = dev(d["q"])
+    kp, vp = dev(d["k_pages"]), dev(d["v_pages"])
+    bt, kl = dev(d["block_table"]), dev(d["kv_lens"])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], device="cuda")
+    maxlen = int(d["kv_lens"].max())
+    split = d.get("split_tokens", 0)
+    ws_bytes = attn.attn_decode_workspace_bytes(d["B"], d["Hq"], d["Hkv"], d["D"], maxlen, split)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        attn.attn_decode_paged_fp8(q, kp, vp, d["k_scale"], d["v_scale"], bt, kl, o, lse,
+                                   max_kv_len=maxlen, scale=d["scale"], workspace=ws,
+                                   split_tokens=split)
+
+    durs, span, _ = time_launches(step, steps, warmup)
+    nbytes = kv_bytes(d["kv_lens"], d["Hkv"], d["D"], elem=1)
+    mean_ms = float(np.mean(durs))
+    del kp, vp
+    return dict(workload=wl.FP8_WORKLOADS[n], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
+                mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
+                frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                tokens_per_s=int(d["kv_lens"].sum()) * d["Hkv"] / (mean_ms * 1e-3))
+
+
 def bench_cascade(steps, warmup):
     c = wl.workload(5)
     q = dev(c["q"])
@@ -271,6 +301,11 @@ def main():
             log(f"decode workload {n} ...")
             decode[f"workload{n}"] = bench_decode(n, args.steps, args.warmup)
             log(f"  {decode[f'workload{n}']['gbs']:.0f} GB/s")
+            torch.cuda.empty_cache()
+        for n in (3, 4):
+            log(f"decode workload {n}, FP8 cache ...")
+            decode[f"workload{n}_fp8"] = bench_decode_fp8(n, args.steps, args.warmup)
+            log(f"  {decode[f'workload{n}_fp8']['gbs']:.0f} GB/s")
             torch.cuda.empty_cache()
         log("cascade workload 5 ...")
         decode["workload5"] = bench_cascade(args.steps, args.warmup)

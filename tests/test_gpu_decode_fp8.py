@@ -102,24 +102,27 @@ def test_fp8_every_code():
 
 def test_fp8_equals_bf16_decode_of_the_dequantised_cache():
     """With power-of-two scales the dequantised cache is exact in bf16, and
-    the FP8 path computes the same scores and weighted sums as the bf16 path
-    on that cache: the two results are bit-identical."""
+    the FP8 path computes the same scores and weights as the bf16 path on
+    that cache; only the order in which pages reach the wavefronts differs
+    (FP8 pages go in pairs), which changes each wavefront's softmax reference
+    and so the bf16 rounding of P: the outputs agree to the bf16 tolerance
+    (a wrong widening or scale would be far outside it)."""
     require_gpu()
     d = wl.paged_decode_fp8_inputs(8, 32, 8, 128, 10, lengths=[1, 17, 300, 511, 512, 1025, 2000, 64])
     table = np.array([oracle.e4m3_value(b) for b in range(256)])
     kb = wl.bf16_bits((d["k_scale"] * table[d["k_pages"]]).astype(np.float32))
     vb = wl.bf16_bits((d["v_scale"] * table[d["v_pages"]]).astype(np.float32))
     for split in (0, 128):
-        o8, l8 = run_fp8(d, split_tokens=split)
+        o8, l8 = run_fp8(d, split_tokens=split, o_dtype="f32")
         q = dev(d["q"])
-        o = empty_like_out(q.shape, "bf16")
+        o = empty_like_out(q.shape, "f32")
         lse = torch.empty(q.shape[:2], device="cuda")
         attn.attn_decode_paged(q, dev(kb), dev(vb), dev(d["block_table"]), dev(d["kv_lens"]),
                                o, lse, max_kv_len=int(d["kv_lens"].max()), scale=d["scale"],
                                split_tokens=split)
         torch.cuda.synchronize()
-        assert np.array_equal(o8, host(o)), f"O differs from the bf16 path (split {split})"
-        assert np.array_equal(l8, host(lse)), f"lse differs from the bf16 path (split {split})"
+        assert_close(o8, host(o), "bf16", f"O vs the bf16 path (split {split})")
+        assert_close(l8, host(lse), "bf16", f"lse vs the bf16 path (split {split})")
 
 
 def test_fp8_page_placement_invariance():

@@ -35,6 +35,8 @@ SIGNATURES = {
     "attn_shared_prefix_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_decode_shared_prefix": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
                                        _i, _i, _f, _vp, _sz, _vp]),
+    "attn_decode_shared_prefix_fp8": (_i, [_vp, _vp, _vp, _f, _f, _vp, _i, _vp, _vp, _i, _i, _i,
+                                           _i, _i, _i, _f, _vp, _sz, _vp]),
 }
 
 
@@ -264,3 +266,32 @@ def attn_decode_shared_prefix(q, k_pages, v_pages, prefix_pages, prefix_len, o, 
         _p(q), _p(k_pages), _p(v_pages), _p(prefix_pages), int(prefix_len), _p(o), _p(lse),
         B, Hq, Hkv, D, page, dt, _dtype(o), float(scale), _p(workspace), ws_bytes,
         _stream(stream)), "attn_decode_shared_prefix")
+
+
+def attn_decode_shared_prefix_fp8(q, k_pages, v_pages, k_scale, v_scale, prefix_pages,
+                                  prefix_len, o, lse=None, scale=None, workspace=None,
+                                  stream=None):
+    """attn_decode_shared_prefix over an FP8 cache: q bf16 [B,Hq,D]; k_pages,
+    v_pages uint8 [P,Hkv,16,D] (E4M3 bytes, values k_scale * e4m3 and
+    v_scale * e4m3); o bf16 or fp32 [B,Hq,D]."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (o, "o")):
+        _dense(t, n)
+    if q.dtype != torch.bfloat16 or k_pages.dtype != torch.uint8 or v_pages.dtype != torch.uint8:
+        raise TypeError("q must be bf16 and the pages uint8 (E4M3 bytes)")
+    B, Hq, D = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    if prefix_len > 0:
+        _dense(prefix_pages, "prefix_pages")
+        if prefix_pages.dtype != torch.int32 or prefix_pages.numel() * page < prefix_len:
+            raise ValueError("prefix_pages must be int32 covering prefix_len tokens")
+    if lse is not None:
+        _dense(lse, "lse")
+    scale = D ** -0.5 if scale is None else scale
+    need = attn_shared_prefix_workspace_bytes(B, Hq, Hkv, D, prefix_len, FP8_E4M3)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().attn_decode_shared_prefix_fp8(
+        _p(q), _p(k_pages), _p(v_pages), float(k_scale), float(v_scale), _p(prefix_pages),
+        int(prefix_len), _p(o), _p(lse), B, Hq, Hkv, D, page, _dtype(o), float(scale),
+        _p(workspace), ws_bytes, _stream(stream)), "attn_decode_shared_prefix_fp8")

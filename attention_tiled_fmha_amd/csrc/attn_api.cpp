@@ -249,7 +249,7 @@ size_t attn_shared_prefix_workspace_bytes(int batch, int heads_q, int heads_kv, 
     if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || heads_q % heads_kv || head_dim <= 0 ||
         prefix_len < 0)
         return 0;
-    if (dtype == ATTN_BF16 && prefix_len > 0) {
+    if ((dtype == ATTN_BF16 || dtype == ATTN_FP8_E4M3) && prefix_len > 0) {
         int chunk = 0, n_chunks = 0;
         prefix_plan(batch, heads_q, heads_kv, prefix_len, &chunk, &n_chunks);
         return decode_ws_bytes(batch, heads_q, head_dim, n_chunks);
@@ -259,25 +259,26 @@ size_t attn_shared_prefix_workspace_bytes(int batch, int heads_q, int heads_kv, 
     return decode_ws_bytes(batch, heads_q, head_dim, max_splits);
 }
 
-int attn_decode_shared_prefix(const void* q, const void* k_pages, const void* v_pages,
-                              const int32_t* prefix_pages, int prefix_len, void* o, float* lse,
-                              int batch, int heads_q, int heads_kv, int head_dim, int page_size,
-                              int dtype, int o_dtype, float scale, void* workspace,
-                              size_t workspace_bytes, void* stream) {
-    if (!dtype_ok(dtype)) return ATTN_E_UNSUPPORTED;
+static int shared_prefix_common(const void* q, const void* k_pages, const void* v_pages,
+                         const int32_t* prefix_pages, int prefix_len, void* o, float* lse,
+                         int batch, int heads_q, int heads_kv, int head_dim, int page_size,
+                         int dtype, int o_dtype, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream, float k_scale, float v_scale) {
+    const bool fp8 = dtype == ATTN_FP8_E4M3;
     if (prefix_len < 0) return ATTN_E_SHAPE;
     const int npages = (prefix_len + kPageSize - 1) / kPageSize;
-    if (dtype != ATTN_BF16 || prefix_len == 0) {
+    if (dtype == ATTN_F32 || prefix_len == 0) {
         // fp32 test mode (and the empty prefix): every request runs the paged
         // decode over the one shared table.
         return decode_common(q, k_pages, v_pages, prefix_pages, 0, nullptr, prefix_len, o, lse,
                              batch, heads_q, heads_kv, head_dim, page_size, npages, prefix_len,
-                             dtype, o_dtype, scale, workspace, workspace_bytes, stream, 0);
+                             dtype, o_dtype, scale, workspace, workspace_bytes, stream, 0, false,
+                             0.f, nullptr, k_scale, v_scale);
     }
     if (!dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
     if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || heads_q % heads_kv) return ATTN_E_SHAPE;
     if (!dim_ok(head_dim) || page_size != kPageSize) return ATTN_E_UNSUPPORTED;
-    if (!scale_ok(scale)) return ATTN_E_ARG;
+    if (!scale_ok(scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return ATTN_E_ARG;
     if (batch == 0) return ATTN_OK;
     if (!q || !k_pages || !v_pages || !prefix_pages || !o) return ATTN_E_NULL;
     const long rows = (long)batch * (heads_q / heads_kv);
@@ -307,6 +308,9 @@ int attn_decode_shared_prefix(const void* q, const void* k_pages, const void* v_
     a.D = head_dim;
     a.chunk = chunk;
     a.out_f32 = o_dtype == ATTN_F32;
+    a.in_fp8 = fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     a.scale = scale;
     hipError_t e = attn::launch_prefix(a, (hipStream_t)stream);
     if (e != hipSuccess || n_chunks <= 1) return check_hip(e);
@@ -327,6 +331,28 @@ int attn_decode_shared_prefix(const void* q, const void* k_pages, const void* v_
     c.max_splits = n_chunks;
     c.out_f32 = a.out_f32;
     return check_hip(attn::launch_decode_combine(c, (hipStream_t)stream));
+}
+
+int attn_decode_shared_prefix(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* prefix_pages, int prefix_len, void* o, float* lse,
+                              int batch, int heads_q, int heads_kv, int head_dim, int page_size,
+                              int dtype, int o_dtype, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return ATTN_E_UNSUPPORTED;   // FP8 caches: the _fp8 entry
+    return shared_prefix_common(q, k_pages, v_pages, prefix_pages, prefix_len, o, lse, batch,
+                                heads_q, heads_kv, head_dim, page_size, dtype, o_dtype, scale,
+                                workspace, workspace_bytes, stream, 1.f, 1.f);
+}
+
+int attn_decode_shared_prefix_fp8(const void* q, const void* k_pages, const void* v_pages,
+                                  float k_scale, float v_scale, const int32_t* prefix_pages,
+                                  int prefix_len, void* o, float* lse, int batch, int heads_q,
+                                  int heads_kv, int head_dim, int page_size, int o_dtype,
+                                  float scale, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    return shared_prefix_common(q, k_pages, v_pages, prefix_pages, prefix_len, o, lse, batch,
+                                heads_q, heads_kv, head_dim, page_size, ATTN_FP8_E4M3, o_dtype,
+                                scale, workspace, workspace_bytes, stream, k_scale, v_scale);
 }
 
 }  // extern "C"

@@ -70,7 +70,7 @@ hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 // [R*Hq][n_chunks]) and must be combined with launch_decode_combine.
 struct PrefixArgs {
     const void* q;           // [R, Hq, D] bf16
-    const void* k_pages;     // [P, Hkv, 16, D] bf16
+    const void* k_pages;     // [P, Hkv, 16, D] bf16 or E4M3 bytes
     const void* v_pages;
     const int32_t* pages;    // prefix pages
     int prefix_len;
@@ -81,6 +81,10 @@ struct PrefixArgs {
     int R, Hq, Hkv, D;
     int chunk;
     bool out_f32;
+    // FP8 cache: E4M3 bytes, cached values k_scale * e4m3 and v_scale * e4m3
+    // (both scales 1 for bf16)
+    bool in_fp8;
+    float k_scale, v_scale;
     float scale;
 };
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);

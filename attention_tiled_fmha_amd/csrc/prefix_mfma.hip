@@ -62,11 +62,30 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+template <int D, bool FP8>
 struct PrefixPage {
     u32x4 k[D / 32];          // K A operand of k-step s: token l % 16, dims 32s + 8(l/16) .. +7
     uint32_t v[4][D / 32];    // V: token 4(l/16) + t, dims 32c + 2(l%16), +1
 };
+template <int D>
+struct PrefixPage<D, true> {
+    u32x2 k[D / 32];          // K of k-step s: 8 E4M3 bytes, dims 32s + 8(l/16) ..
+    uint32_t v[4][D / 64];    // V: token 4(l/16) + t, dims 64c + 4(l%16) .. +3
+};
+
+// Two E4M3 bytes (the low or high half of w) -> two bf16, exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Head dimension of register r of O^T block i for lane group grp: bf16 pages
+// give blocks of even / odd dims of each 32-dim column, FP8 pages blocks of
+// dims 4k + i%4 of each 64-dim column.
+template <bool FP8>
+__device__ __forceinline__ int ot_dim(int i, int grp, int r) {
+    return FP8 ? 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3) : 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
+}
 
 template <int D>
 struct PrefixLds {
@@ -75,9 +94,11 @@ struct PrefixLds {
     static constexpr size_t BYTES = (2 * SLOT + 4 * kRows) * sizeof(float);
 };
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefix_mfma_kernel(PrefixArgs a) {
+    constexpr int EB = FP8 ? 1 : 2;            // bytes per cached element
+    constexpr int NBUF = FP8 ? 2 * kBufs : kBufs;   // as many bytes in flight for FP8
     constexpr int KS = D / 32;   // k-steps of S^T, and 32-dim V columns
     constexpr int NB = D / 16;   // 16-dim blocks of O^T
     using LD = PrefixLds<D>;
@@ -93,11 +114,13 @@ void prefix_mfma_kernel(PrefixArgs a) {
     const int N = a.R * G;                    // query rows of one kv head
     const int n_rb = (N + kRows - 1) / kRows;
     const int n_chunks = (a.prefix_len + a.chunk - 1) / a.chunk;
-    const float sl2 = a.scale * kLog2e;
-    const uint16_t* kbase = (const uint16_t*)a.k_pages;
-    const uint16_t* vbase = (const uint16_t*)a.v_pages;
-    const int voff_k = col * D * 2 + 16 * grp;
-    const int voff_v = 4 * grp * D * 2 + 4 * col;
+    // an FP8 cache holds k_scale * e4m3: the key scale joins the softmax scale,
+    // the value scale multiplies the output (both are 1 for bf16)
+    const float sl2 = a.scale * a.k_scale * kLog2e;
+    const unsigned char* kbase = (const unsigned char*)a.k_pages;
+    const unsigned char* vbase = (const unsigned char*)a.v_pages;
+    const int voff_k = col * D * EB + 8 * EB * grp;
+    const int voff_v = 4 * grp * D * EB + 4 * col;
 
     // query row n of kv head kvh: request n / G, head kvh*G + n % G
     auto qrow_of = [&](int kvh, int n) { return (size_t)(n / G) * a.Hq + kvh * G + n % G; };
@@ -124,22 +147,32 @@ void prefix_mfma_kernel(PrefixArgs a) {
         }
         const int tblv = lane < npg ? a.pages[pg0 + lane] : 0;
 
-        auto load = [&](PrefixPage<D>& pb, int j) {
+        auto load = [&](PrefixPage<D, FP8>& pb, int j) {
             const int pg = pg0 + j;
             const int phys = __builtin_amdgcn_readlane(tblv, min(j, npg - 1));
-            const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(kPage, tok1 - pg * kPage)) * D * 2);
-            const size_t off = ((size_t)phys * a.Hkv + kvh) * kPage * D;
+            const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(kPage, tok1 - pg * kPage)) * D * EB);
+            const size_t off = (((size_t)phys * a.Hkv + kvh) * kPage * D) * EB;
             const __amdgpu_buffer_rsrc_t rk =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, bytes, kRsrcWord3);
             const __amdgpu_buffer_rsrc_t rv =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, bytes, kRsrcWord3);
+            if constexpr (FP8) {
 #pragma unroll
-            for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + 64 * s, 0, 0);
+                for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b64(rk, voff_k + 32 * s, 0, 0);
 #pragma unroll
-            for (int t = 0; t < 4; t++)
+                for (int t = 0; t < 4; t++)
 #pragma unroll
-                for (int cc = 0; cc < KS; cc++)
-                    pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D * 2 + 64 * cc, 0, 0);
+                    for (int cc = 0; cc < D / 64; cc++)
+                        pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D + 64 * cc, 0, 0);
+            } else {
+#pragma unroll
+                for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + 64 * s, 0, 0);
+#pragma unroll
+                for (int t = 0; t < 4; t++)
+#pragma unroll
+                    for (int cc = 0; cc < KS; cc++)
+                        pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D * 2 + 64 * cc, 0, 0);
+            }
         };
 
         float m_run[kRB], l_run[kRB];
@@ -152,17 +185,27 @@ void prefix_mfma_kernel(PrefixArgs a) {
             for (int i = 0; i < NB; i++) oacc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        auto compute = [&](const PrefixPage<D>& pb, int jp) {
+        auto compute = [&](const PrefixPage<D, FP8>& pb, int jp) {
             const int pg = pg0 + jp;
+            // K A operands (FP8: bytes widened to bf16 once, for both row blocks)
+            bf16x8 kf[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                if constexpr (FP8) {
+                    const uint32_t w0 = pb.k[ks][0], w1 = pb.k[ks][1];
+                    kf[ks] = __builtin_bit_cast(bf16x8, u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                                              e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)});
+                } else {
+                    kf[ks] = __builtin_bit_cast(bf16x8, pb.k[ks]);
+                }
+            }
             s16x4 pt[kRB];
 #pragma unroll
             for (int j = 0; j < kRB; j++) {
-                f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[0]), qf[j][0],
-                                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[j][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                 for (int ks = 1; ks < KS; ks++)
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb.k[ks]), qf[j][ks], s,
-                                                                0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[j][ks], s, 0, 0, 0);
                 // s[r] is the score of token pg*16 + 4grp + r for row 16j + col
                 if (pg * kPage + kPage > tok1) {
 #pragma unroll
@@ -188,18 +231,46 @@ void prefix_mfma_kernel(PrefixArgs a) {
                 l_run[j] += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
                 pt[j] = __builtin_bit_cast(s16x4, u32x2{p01, p23});
             }
+            if constexpr (FP8) {
+                // per 64-dim column c: block 4c + i gathers dim offset i of the 4 tokens
 #pragma unroll
-            for (int cc = 0; cc < KS; cc++) {
-                const uint32_t v0 = pb.v[0][cc], v1 = pb.v[1][cc], v2 = pb.v[2][cc], v3 = pb.v[3][cc];
-                const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x05040100u),
-                                                                 __builtin_amdgcn_perm(v3, v2, 0x05040100u)});
-                const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x07060302u),
-                                                                 __builtin_amdgcn_perm(v3, v2, 0x07060302u)});
+                for (int cc = 0; cc < D / 64; cc++) {
+                    uint32_t lo[4], hi[4];
 #pragma unroll
-                for (int j = 0; j < kRB; j++) {
-                    oacc[j][2 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pt[j], oacc[j][2 * cc], 0, 0, 0);
-                    oacc[j][2 * cc + 1] =
-                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pt[j], oacc[j][2 * cc + 1], 0, 0, 0);
+                    for (int t = 0; t < 4; t++) {
+                        lo[t] = e4m3x2_to_bf16x2<false>(pb.v[t][cc]);   // dims +0, +1
+                        hi[t] = e4m3x2_to_bf16x2<true>(pb.v[t][cc]);    // dims +2, +3
+                    }
+                    s16x4 av[4];
+                    av[0] = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x05040100u),
+                                                            __builtin_amdgcn_perm(lo[3], lo[2], 0x05040100u)});
+                    av[1] = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u),
+                                                            __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)});
+                    av[2] = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x05040100u),
+                                                            __builtin_amdgcn_perm(hi[3], hi[2], 0x05040100u)});
+                    av[3] = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u),
+                                                            __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)});
+#pragma unroll
+                    for (int j = 0; j < kRB; j++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            oacc[j][4 * cc + i] =
+                                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[i], pt[j], oacc[j][4 * cc + i], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < KS; cc++) {
+                    const uint32_t v0 = pb.v[0][cc], v1 = pb.v[1][cc], v2 = pb.v[2][cc], v3 = pb.v[3][cc];
+                    const s16x4 ae = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x05040100u),
+                                                                     __builtin_amdgcn_perm(v3, v2, 0x05040100u)});
+                    const s16x4 ao = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(v1, v0, 0x07060302u),
+                                                                     __builtin_amdgcn_perm(v3, v2, 0x07060302u)});
+#pragma unroll
+                    for (int j = 0; j < kRB; j++) {
+                        oacc[j][2 * cc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pt[j], oacc[j][2 * cc], 0, 0, 0);
+                        oacc[j][2 * cc + 1] =
+                            __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pt[j], oacc[j][2 * cc + 1], 0, 0, 0);
+                    }
                 }
             }
         };
@@ -211,14 +282,14 @@ void prefix_mfma_kernel(PrefixArgs a) {
         // chunk reads zeros and is masked out, so it adds exactly nothing, and
         // the loop body has no early exit between its loads.
         const int nj = npg > wave ? (npg - wave + 3) / 4 : 0;
-        const int nj_pad = (nj + kBufs - 1) / kBufs * kBufs;
-        PrefixPage<D> buf[kBufs];
+        const int nj_pad = (nj + NBUF - 1) / NBUF * NBUF;
+        PrefixPage<D, FP8> buf[NBUF];
 #pragma unroll
-        for (int u = 0; u < kBufs - 1; u++) load(buf[u], wave + 4 * u);
-        for (int n = 0; n < nj_pad; n += kBufs) {
+        for (int u = 0; u < NBUF - 1; u++) load(buf[u], wave + 4 * u);
+        for (int n = 0; n < nj_pad; n += NBUF) {
 #pragma unroll
-            for (int u = 0; u < kBufs; u++) {
-                load(buf[(u + kBufs - 1) % kBufs], wave + 4 * (n + u + kBufs - 1));
+            for (int u = 0; u < NBUF; u++) {
+                load(buf[(u + NBUF - 1) % NBUF], wave + 4 * (n + u + NBUF - 1));
                 compute(buf[u], wave + 4 * (n + u));
             }
         }
@@ -226,8 +297,7 @@ void prefix_mfma_kernel(PrefixArgs a) {
         for (int j = 0; j < kRB; j++) l_run[j] = sum_xor32(sum_xor16(l_run[j]));
 
         // ---- merge the four wavefronts: 2,3 into 0,1, then 1 into 0 --------
-        // O^T block i of row block j, register r: row 16j + col,
-        // dim 32(i/2) + 2(4grp + r) + i%2
+        // O^T block i of row block j, register r: row 16j + col, dim ot_dim
         auto put = [&](int slot) {
             float* o = s_o + slot * LD::SLOT;
 #pragma unroll
@@ -240,7 +310,7 @@ void prefix_mfma_kernel(PrefixArgs a) {
                 for (int i = 0; i < NB; i++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        o[(16 * j + col) * LD::STRIDE + 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1)] = oacc[j][i][r];
+                        o[(16 * j + col) * LD::STRIDE + ot_dim<FP8>(i, grp, r)] = oacc[j][i][r];
             }
         };
         auto take = [&](int slot) {
@@ -258,7 +328,7 @@ void prefix_mfma_kernel(PrefixArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; r++)
                         oacc[j][i][r] = wa * oacc[j][i][r] +
-                                        wb * o[(16 * j + col) * LD::STRIDE + 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1)];
+                                        wb * o[(16 * j + col) * LD::STRIDE + ot_dim<FP8>(i, grp, r)];
             }
         };
         if (wave >= 2) put(wave - 2);
@@ -273,15 +343,14 @@ void prefix_mfma_kernel(PrefixArgs a) {
             float* o = s_o;
 #pragma unroll
             for (int j = 0; j < kRB; j++) {
-                const float inv = l_run[j] > 0.f ? 1.f / l_run[j] : 0.f;
+                const float inv = l_run[j] > 0.f ? a.v_scale / l_run[j] : 0.f;
                 if (grp == 0)
                     s_m[16 * j + col] = l_run[j] > 0.f ? (m_run[j] + __log2f(l_run[j])) * kLn2 : -INFINITY;
 #pragma unroll
                 for (int i = 0; i < NB; i++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        o[(16 * j + col) * LD::STRIDE + 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1)] =
-                            oacc[j][i][r] * inv;
+                        o[(16 * j + col) * LD::STRIDE + ot_dim<FP8>(i, grp, r)] = oacc[j][i][r] * inv;
             }
         }
         __syncthreads();
@@ -323,15 +392,14 @@ hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream) {
     const long n_items = (long)((a.prefix_len + a.chunk - 1) / a.chunk) * a.Hkv * ((N + kRows - 1) / kRows);
     const dim3 grid((unsigned)std::min<long>(n_items, 4096));
     const size_t lds = prefix_lds_bytes(a.D);
-    if (a.D == 64) {
-        hipFuncSetAttribute((const void*)prefix_mfma_kernel<64>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        prefix_mfma_kernel<64><<<grid, 256, lds, stream>>>(a);
-    } else {
-        hipFuncSetAttribute((const void*)prefix_mfma_kernel<128>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        prefix_mfma_kernel<128><<<grid, 256, lds, stream>>>(a);
-    }
+    auto go = [&](auto kern) {
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        kern<<<grid, 256, lds, stream>>>(a);
+    };
+    if (a.in_fp8)
+        a.D == 64 ? go(prefix_mfma_kernel<64, true>) : go(prefix_mfma_kernel<128, true>);
+    else
+        a.D == 64 ? go(prefix_mfma_kernel<64, false>) : go(prefix_mfma_kernel<128, false>);
     return hipGetLastError();
 }
 

@@ -112,6 +112,8 @@ def normal(gen, shape, dtype, e4m3_scale=1.0):
 
 
 def _const(value, dtype):
+    if dtype == "e4m3":
+        return 0x7E            # the largest E4M3 code
     return bf16_bits(np.float32(value)).item() if dtype == "bf16" else np.float32(value)
 
 
@@ -236,10 +238,16 @@ def paged_decode_fp8_inputs(B, Hq, Hkv, D, seed, lengths=None, length_range=(512
 
 def cascade_inputs(R, H, D, dtype, seed, prefix_len=4096, suffix_range=(128, 1024),
                    suffix_lens=None, page_size=PAGE_SIZE, Hkv=None,
-                   tail_garbage=True):
+                   tail_garbage=True, kv_scale=1.0 / 32):
     """Shared-prefix decode: R requests share one prefix of ``prefix_len``
     tokens, stored once, plus their own suffixes.  Prefix and suffix pages
-    are all placed by one permutation of the pool."""
+    are all placed by one permutation of the pool.  dtype 'fp8': bf16
+    queries over an E4M3 cache with per-tensor scale ``kv_scale`` (as
+    ``paged_decode_fp8_inputs``)."""
+    if dtype == "fp8":
+        c = cascade_inputs(R, H, D, "e4m3", seed, prefix_len, suffix_range, suffix_lens,
+                           page_size, Hkv, tail_garbage, kv_scale)
+        return c | dict(dtype="fp8", k_scale=kv_scale, v_scale=kv_scale)
     Hkv = Hkv or H
     gen = generator(seed)
     if suffix_lens is None:
@@ -250,9 +258,9 @@ def cascade_inputs(R, H, D, dtype, seed, prefix_len=4096, suffix_range=(128, 102
     physical = gen.permutation(max(1, total)).astype(np.int32)
     prefix_pages = physical[:npre].copy()
     suffix_table = _tables(suffix_lens, physical[npre:], page_size)
-    q = normal(gen, (R, H, D), dtype)
-    k_pages = normal(gen, (max(1, total), Hkv, page_size, D), dtype)
-    v_pages = normal(gen, (max(1, total), Hkv, page_size, D), dtype)
+    q = normal(gen, (R, H, D), "bf16" if dtype == "e4m3" else dtype)
+    k_pages = normal(gen, (max(1, total), Hkv, page_size, D), dtype, kv_scale)
+    v_pages = normal(gen, (max(1, total), Hkv, page_size, D), dtype, kv_scale)
     if tail_garbage:
         _fill_tails(k_pages, v_pages, suffix_table, suffix_lens, page_size, dtype)
         if prefix_len % page_size:
@@ -285,12 +293,16 @@ FP8_WORKLOADS = {
        "page 16",
     4: "paged decode GQA B128 Hq32 Hkv8 D128, FP8 E4M3 cache (scale 1/32), bf16 q/o, "
        "L~logU[1024,32768], page 16, split <= 512",
+    5: "shared-prefix cascade decode, 64 requests, prefix 4096, suffix U[128,1024], H32 D128, "
+       "FP8 E4M3 cache (scale 1/32), bf16 q/o, page 16",
 }
 
 
 def fp8_workload(n, seed=None):
-    """Workloads 3 and 4 over an FP8 cache (same shapes and length draws)."""
+    """Workloads 3, 4 and 5 over an FP8 cache (same shapes and length draws)."""
     seed = 1000 + n if seed is None else seed
+    if n == 5:
+        return cascade_inputs(64, 32, 128, "fp8", seed)
     if n == 3:
         return paged_decode_fp8_inputs(32, 32, 32, 128, seed, length_range=(512, 8192),
                                        length_dist="uniform")

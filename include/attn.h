@@ -271,6 +271,8 @@ int attn_merge_states(void *o_a, float *lse_a, const void *o_b, const float *lse
  * prefix_len == 0 gives O = 0 and lse = -inf.  bf16 runs the MFMA prefix
  * kernel; fp32 (the exactness test mode) runs the paged decode kernel with
  * the one prefix table shared by every request.
+ * attn_shared_prefix_workspace_bytes takes dtype ATTN_FP8_E4M3 for the
+ * workspace of attn_decode_shared_prefix_fp8.
  */
 size_t attn_shared_prefix_workspace_bytes(int batch, int heads_q, int heads_kv, int head_dim,
                                           int prefix_len, int dtype);
@@ -280,6 +282,24 @@ int attn_decode_shared_prefix(const void *q, const void *k_pages, const void *v_
                               int batch, int heads_q, int heads_kv, int head_dim,
                               int page_size, int dtype, int o_dtype, float scale,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_shared_prefix_fp8 -- attn_decode_shared_prefix over an FP8 KV
+ * cache (OCP E4M3 bytes with per-tensor scales, as attn_decode_paged_fp8):
+ * q bf16, o `o_dtype` (ATTN_BF16 or ATTN_F32), k_pages / v_pages uint8
+ * [num_pages, heads_kv, page_size, head_dim], cached values k_scale * e4m3
+ * and v_scale * e4m3 (finite and > 0, else ATTN_E_ARG).  The workspace is
+ * attn_shared_prefix_workspace_bytes(..., ATTN_FP8_E4M3).  The suffix stage
+ * is attn_decode_paged_fp8; the merge is attn_merge_states.  Errors as
+ * attn_decode_shared_prefix.
+ */
+int attn_decode_shared_prefix_fp8(const void *q, const void *k_pages, const void *v_pages,
+                                  float k_scale, float v_scale,
+                                  const int32_t *prefix_pages, int prefix_len,
+                                  void *o, float *lse,
+                                  int batch, int heads_q, int heads_kv, int head_dim,
+                                  int page_size, int o_dtype, float scale,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -165,6 +165,30 @@ def test_shared_prefix_checks(lib):
     assert f(B=0) == OK
 
 
+def test_shared_prefix_fp8_checks(lib):
+    # every case here is rejected on the host, before anything is launched
+    f = lambda **kw: lib.attn_decode_shared_prefix_fp8(
+        kw.get("q", FAKE), FAKE, FAKE, kw.get("ks", 0.5), kw.get("vs", 0.25), kw.get("pp", FAKE),
+        kw.get("plen", 64), FAKE, None, kw.get("B", 4), kw.get("Hq", 4), kw.get("Hkv", 4),
+        kw.get("D", 128), kw.get("page", 16), kw.get("odt", 0), kw.get("scale", 0.1), None, 0,
+        None)
+    assert f(q=None) == E_NULL
+    assert f(pp=None) == E_NULL
+    assert f(plen=-1) == E_SHAPE
+    assert f(Hq=6, Hkv=4) == E_SHAPE
+    assert f(page=8) == E_UNSUP
+    assert f(D=96) == E_UNSUP
+    assert f(odt=2) == E_UNSUP
+    assert f(ks=0.0) == E_ARG
+    assert f(vs=float("inf")) == E_ARG
+    assert f(scale=-2.0) == E_ARG
+    assert f(plen=100000) == E_WS      # several prefix chunks and no workspace
+    assert f(B=0) == OK
+    # the plain entry does not take the FP8 cache type
+    assert lib.attn_decode_shared_prefix(FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, 4, 4, 4, 128,
+                                         16, 2, 0, 0.1, None, 0, None) == E_UNSUP
+
+
 def test_decode_plan(lib):
     # workload shapes: long contexts over many sequences get 1024-token chunks
     assert attn.attn_decode_plan(32, 32, 8192) == (1024, 8)

@@ -155,3 +155,66 @@ def test_fp8_workloads_full_size_sampled(n):
     assert_close(o[rows], ro, "bf16", f"O rows {rows}")
     assert_close(lse[rows], rl, "bf16", f"lse rows {rows}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# --- shared-prefix cascade over an FP8 cache ----------------------------------
+
+@pytest.mark.parametrize("R,H,Hkv,plen,D", [
+    (3, 4, 4, 15, 128), (5, 8, 2, 100, 128), (70, 4, 4, 300, 128), (9, 4, 1, 517, 64),
+    (64, 32, 32, 4096, 128), (16, 2, 2, 20000, 128),
+])
+@pytest.mark.parametrize("o_dtype", ["bf16", "f32"])
+def test_fp8_shared_prefix(R, H, Hkv, plen, D, o_dtype):
+    """The MFMA prefix stage over an FP8 cache against per-request decode of
+    the prefix: more than 64 query rows per kv head, GQA groups, ragged
+    prefix lengths, one and many prefix chunks."""
+    require_gpu()
+    c = wl.cascade_inputs(R, H, D, "fp8", 31 + R + plen, prefix_len=plen, suffix_range=(1, 2),
+                          Hkv=Hkv)
+    q = dev(c["q"])
+    o = empty_like_out(q.shape, o_dtype)
+    lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+    attn.attn_decode_shared_prefix_fp8(q, dev(c["k_pages"]), dev(c["v_pages"]), c["k_scale"],
+                                       c["v_scale"], dev(c["prefix_pages"]), plen, o, lse,
+                                       scale=c["scale"])
+    torch.cuda.synchronize()
+    table = np.broadcast_to(c["prefix_pages"], (R, len(c["prefix_pages"]))).copy()
+    ro, rl = oracle.decode_paged_fp8(c["q"], c["k_pages"], c["v_pages"], c["k_scale"],
+                                     c["v_scale"], table, np.full(R, plen, np.int32), c["scale"])
+    assert_close(host(o), ro, "bf16", "prefix O")
+    assert_close(host(lse), rl, "bf16", "prefix lse")
+
+
+def run_cascade_fp8(c):
+    q = dev(c["q"])
+    kp, vp = dev(c["k_pages"]), dev(c["v_pages"])
+    o_p, o_s = torch.empty_like(q), torch.empty_like(q)
+    l_p = torch.empty(q.shape[:2], device="cuda")
+    l_s = torch.empty(q.shape[:2], device="cuda")
+    attn.attn_decode_shared_prefix_fp8(q, kp, vp, c["k_scale"], c["v_scale"],
+                                       dev(c["prefix_pages"]), c["prefix_len"], o_p, l_p,
+                                       scale=c["scale"])
+    attn.attn_decode_paged_fp8(q, kp, vp, c["k_scale"], c["v_scale"], dev(c["suffix_table"]),
+                               dev(c["suffix_lens"]), o_s, l_s,
+                               max_kv_len=int(c["suffix_lens"].max()), scale=c["scale"])
+    attn.attn_merge_states(o_p, l_p, o_s, l_s)
+    torch.cuda.synchronize()
+    return host(o_p), host(l_p)
+
+
+def test_fp8_cascade_workload5_full_size():
+    """Workload 5's shape over an FP8 cache (64 requests, 4096-token prefix,
+    suffixes U[128, 1024]): prefix stage, suffix decode and merge against the
+    plain decode of each request's whole key sequence."""
+    require_gpu()
+    c = wl.fp8_workload(5)
+    o, lse = run_cascade_fp8(c)
+    rows = [0, 1, 31, 63]
+    npre = len(c["prefix_pages"])
+    table = np.stack([np.concatenate([c["prefix_pages"], c["suffix_table"][r]]) for r in rows])
+    lens = (c["prefix_len"] + c["suffix_lens"][rows]).astype(np.int32)
+    assert c["prefix_len"] == npre * 16
+    ro, rl = oracle.decode_paged_fp8(c["q"][rows], c["k_pages"], c["v_pages"], c["k_scale"],
+                                     c["v_scale"], table.astype(np.int32), lens, c["scale"])
+    assert_close(o[rows], ro, "bf16", "cascade O")
+    assert_close(lse[rows], rl, "bf16", "cascade lse")

@@ -250,12 +250,16 @@ def attn_decode_shared_prefix(q, k_pages, v_pages, prefix_pages, prefix_len, o, 
         _dense(t, n)
     B, Hq, D = q.shape
     P, Hkv, page, _ = k_pages.shape
+    if o.shape != q.shape or v_pages.shape != k_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("shape mismatch")
     if prefix_len > 0:
         _dense(prefix_pages, "prefix_pages")
         if prefix_pages.dtype != torch.int32 or prefix_pages.numel() * page < prefix_len:
             raise ValueError("prefix_pages must be int32 covering prefix_len tokens")
     if lse is not None:
         _dense(lse, "lse")
+        if lse.shape != (B, Hq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, Hq]")
     dt = _dtype(q)
     scale = D ** -0.5 if scale is None else scale
     need = attn_shared_prefix_workspace_bytes(B, Hq, Hkv, D, prefix_len, dt)
@@ -280,12 +284,16 @@ def attn_decode_shared_prefix_fp8(q, k_pages, v_pages, k_scale, v_scale, prefix_
         raise TypeError("q must be bf16 and the pages uint8 (E4M3 bytes)")
     B, Hq, D = q.shape
     P, Hkv, page, _ = k_pages.shape
+    if o.shape != q.shape or v_pages.shape != k_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("shape mismatch")
     if prefix_len > 0:
         _dense(prefix_pages, "prefix_pages")
         if prefix_pages.dtype != torch.int32 or prefix_pages.numel() * page < prefix_len:
             raise ValueError("prefix_pages must be int32 covering prefix_len tokens")
     if lse is not None:
         _dense(lse, "lse")
+        if lse.shape != (B, Hq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, Hq]")
     scale = D ** -0.5 if scale is None else scale
     need = attn_shared_prefix_workspace_bytes(B, Hq, Hkv, D, prefix_len, FP8_E4M3)
     if workspace is None and need:

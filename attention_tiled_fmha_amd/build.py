@@ -27,9 +27,10 @@ FLAGS = [
 ]
 
 
-# Per-file extras: the prefill softmax never sees NaN (scores are finite or
-# -inf), so fmax needs no NaN canonicalisation there.
-FILE_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
+# Per-file extras: the prefill and shared-prefix softmax never see NaN
+# (scores are finite or -inf, and the cache tail past the prefix reads as
+# zeros), so fmax needs no NaN canonicalisation there.
+FILE_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"], "prefix_mfma.hip": ["-fno-honor-nans"]}
 
 
 def sources():

@@ -55,12 +55,14 @@ size_t decode_ws_bytes(int batch, int heads_q, int head_dim, int max_splits) {
 int check_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
 
 // Shared-prefix chunking: an item is (chunk, kv head, block of 32 query rows),
-// one 4-wavefront workgroup each; aim for about two items per compute unit,
-// in chunks of 64 .. 1024 tokens.
+// one 4-wavefront workgroup each; aim for about one item per compute unit,
+// in chunks of 64 .. 1024 tokens.  Measured on the 64-request, 4096-token
+// prefix: one item per CU beats two or four, since each item pays a fixed
+// start (queries, page table, first pages) and a cross-wave merge.
 void prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int* chunk, int* n_chunks) {
     const long rows = (long)batch * (heads_q / heads_kv);
     const long per_chunk = (long)heads_kv * ((rows + 31) / 32);
-    const long want = std::max(1L, (2L * kPlanCUs + per_chunk - 1) / per_chunk);
+    const long want = std::max(1L, (1L * kPlanCUs + per_chunk - 1) / per_chunk);
     long c = (prefix_len + want - 1) / want;
     c = std::min(1024L, std::max(64L, (c + 63) / 64 * 64));
     *chunk = (int)c;

@@ -10,13 +10,18 @@
 // request.
 //
 // The kernel is the paged decode kernel (decode_mfma.hip) with 32 query rows
-// per item instead of G <= 16: per 16-token page a wavefront does, for each
-// of two 16-row blocks j,
+// per item instead of G <= 16: per 16-token page a wavefront does, for two
+// 16-row blocks j,
 //   S_j^T = K Q_j^T      D/32 x v_mfma_f32_16x16x32_bf16
 //   softmax(S_j)         per row over the page
 //   O_j^T += V^T P_j^T   D/16 x v_mfma_f32_16x16x16_bf16
 // where the K and V^T operand fragments, loaded once per page, serve both
-// blocks.  K is loaded straight into operand order and V transposed in
+// blocks.  Both blocks' scores are formed before either softmax, and one
+// wave-uniform test decides a (rare) rescale of both, so the two MFMA chains
+// and the two reductions overlap.  The register budget is held to 256 per
+// lane (two waves per SIMD): the O accumulators then live in VGPRs, where
+// the rescale multiplies them in place; with AGPR accumulators the compiler
+// copied all of them out and back around the rescale branch on every page.  K is loaded straight into operand order and V transposed in
 // registers, through per-page buffer descriptors that cover only the prefix
 // (the tail of the last page reads zeros).
 //
@@ -95,7 +100,7 @@ struct PrefixLds {
 };
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefix_mfma_kernel(PrefixArgs a) {
     constexpr int EB = FP8 ? 1 : 2;            // bytes per cached element
     constexpr int NBUF = FP8 ? 2 * kBufs : kBufs;   // as many bytes in flight for FP8
@@ -199,33 +204,53 @@ void prefix_mfma_kernel(PrefixArgs a) {
                     kf[ks] = __builtin_bit_cast(bf16x8, pb.k[ks]);
                 }
             }
-            s16x4 pt[kRB];
+            // scores of every row block first: independent MFMA chains
+            f32x4 s[kRB];
 #pragma unroll
             for (int j = 0; j < kRB; j++) {
-                f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[j][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[j][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                 for (int ks = 1; ks < KS; ks++)
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[j][ks], s, 0, 0, 0);
-                // s[r] is the score of token pg*16 + 4grp + r for row 16j + col
-                if (pg * kPage + kPage > tok1) {
+                    s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[j][ks], s[j], 0, 0, 0);
+            }
+            // s[j][r] is the score of token pg*16 + 4grp + r for row 16j + col
+            if (pg * kPage + kPage > tok1) {
+#pragma unroll
+                for (int j = 0; j < kRB; j++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        if (pg * kPage + 4 * grp + r >= tok1) s[r] = -INFINITY;
-                }
-                float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-                mx = max_xor32(max_xor16(mx));
-                const float m_new = fmaxf(m_run[j], mx * sl2);
-                if (__builtin_amdgcn_ballot_w64(m_new > m_run[j] + kRescaleThresh)) {
-                    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[j] - m_new);
+                        if (pg * kPage + 4 * grp + r >= tok1) s[j][r] = -INFINITY;
+            }
+            float mx[kRB];
+#pragma unroll
+            for (int j = 0; j < kRB; j++) mx[j] = fmaxf(fmaxf(s[j][0], s[j][1]), fmaxf(s[j][2], s[j][3]));
+#pragma unroll
+            for (int j = 0; j < kRB; j++) mx[j] = max_xor16(mx[j]);
+#pragma unroll
+            for (int j = 0; j < kRB; j++) mx[j] = max_xor32(mx[j]);
+            bool grow = false;
+#pragma unroll
+            for (int j = 0; j < kRB; j++) {
+                mx[j] = fmaxf(m_run[j], mx[j] * sl2);
+                grow |= mx[j] > m_run[j] + kRescaleThresh;
+            }
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+                for (int j = 0; j < kRB; j++) {
+                    const float alpha = (mx[j] == -INFINITY) ? 1.f : fast_exp2(m_run[j] - mx[j]);
                     l_run[j] *= alpha;
 #pragma unroll
                     for (int i = 0; i < NB; i++) oacc[j][i] *= alpha;
-                    m_run[j] = m_new;
+                    m_run[j] = mx[j];
                 }
+            }
+            s16x4 pt[kRB];
+#pragma unroll
+            for (int j = 0; j < kRB; j++) {
                 const float m_eff = (m_run[j] == -INFINITY) ? 0.f : m_run[j];
                 float p[4];
 #pragma unroll
-                for (int r = 0; r < 4; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m_eff));
+                for (int r = 0; r < 4; r++) p[r] = fast_exp2(__builtin_fmaf(s[j][r], sl2, -m_eff));
                 const uint32_t p01 = pack_bf16x2(p[0], p[1]), p23 = pack_bf16x2(p[2], p[3]);
                 // the row sum adds the bf16-rounded P that meets V
                 l_run[j] += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));

@@ -204,8 +204,10 @@ def bench_decode_fp8(n, steps, warmup):
                 tokens_per_s=int(d["kv_lens"].sum()) * d["Hkv"] / (mean_ms * 1e-3))
 
 
-def bench_cascade(steps, warmup):
-    c = wl.workload(5)
+def bench_cascade(steps, warmup, fp8=False):
+    """Workload 5: prefix stage + suffix decode + merge on one stream, timed as
+    one step.  With fp8 the cache is OCP E4M3 bytes with per-tensor scales."""
+    c = wl.fp8_workload(5) if fp8 else wl.workload(5)
     q = dev(c["q"])
     kp, vp = dev(c["k_pages"]), dev(c["v_pages"])
     pp, st, sl = dev(c["prefix_pages"]), dev(c["suffix_table"]), dev(c["suffix_lens"])
@@ -213,8 +215,10 @@ def bench_cascade(steps, warmup):
     o_p, o_s = torch.empty_like(q), torch.empty_like(q)
     l_p, l_s = (torch.empty((R, H), device="cuda") for _ in range(2))
     maxlen = int(c["suffix_lens"].max())
+    cache_dt = attn.FP8_E4M3 if fp8 else attn.BF16
     ws_p = torch.empty(max(1, attn.attn_shared_prefix_workspace_bytes(R, H, c["Hkv"], D,
-                                                                          c["prefix_len"])),
+                                                                          c["prefix_len"],
+                                                                          cache_dt)),
                        dtype=torch.uint8, device="cuda")
     ws_s = torch.empty(max(1, attn.attn_decode_workspace_bytes(R, H, c["Hkv"], D, maxlen)),
                        dtype=torch.uint8, device="cuda")
@@ -227,17 +231,26 @@ def bench_cascade(steps, warmup):
         flush.sum()
 
     def step(i):
-        attn.attn_decode_shared_prefix(q, kp, vp, pp, c["prefix_len"], o_p, l_p, scale=c["scale"],
-                                       workspace=ws_p)
-        attn.attn_decode_paged(q, kp, vp, st, sl, o_s, l_s, max_kv_len=maxlen, scale=c["scale"],
-                               workspace=ws_s)
+        if fp8:
+            attn.attn_decode_shared_prefix_fp8(q, kp, vp, c["k_scale"], c["v_scale"], pp,
+                                               c["prefix_len"], o_p, l_p, scale=c["scale"],
+                                               workspace=ws_p)
+            attn.attn_decode_paged_fp8(q, kp, vp, c["k_scale"], c["v_scale"], st, sl, o_s, l_s,
+                                       max_kv_len=maxlen, scale=c["scale"], workspace=ws_s)
+        else:
+            attn.attn_decode_shared_prefix(q, kp, vp, pp, c["prefix_len"], o_p, l_p,
+                                           scale=c["scale"], workspace=ws_p)
+            attn.attn_decode_paged(q, kp, vp, st, sl, o_s, l_s, max_kv_len=maxlen,
+                                   scale=c["scale"], workspace=ws_s)
         attn.attn_merge_states(o_p, l_p, o_s, l_s)
 
     durs, span, _ = time_launches(step, steps, warmup, before=before)
-    nbytes = kv_bytes([c["prefix_len"]], c["Hkv"], D) + kv_bytes(c["suffix_lens"], c["Hkv"], D)
+    elem = 1 if fp8 else 2
+    nbytes = (kv_bytes([c["prefix_len"]], c["Hkv"], D, elem=elem)
+              + kv_bytes(c["suffix_lens"], c["Hkv"], D, elem=elem))
     mean_ms = float(np.mean(durs))
-    return dict(workload=wl.WORKLOADS[5], kv_bytes=nbytes, mean_ms=mean_ms,
-                gbs=nbytes / (mean_ms * 1e-3) / 1e9,
+    return dict(workload=(wl.FP8_WORKLOADS if fp8 else wl.WORKLOADS)[5], kv_bytes=nbytes,
+                mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
                 frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
 
 
@@ -310,6 +323,10 @@ def main():
         log("cascade workload 5 ...")
         decode["workload5"] = bench_cascade(args.steps, args.warmup)
         log(f"  {decode['workload5']['gbs']:.0f} GB/s")
+        torch.cuda.empty_cache()
+        log("cascade workload 5, FP8 cache ...")
+        decode["workload5_fp8"] = bench_cascade(args.steps, args.warmup, fp8=True)
+        log(f"  {decode['workload5_fp8']['gbs']:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle) ...")

@@ -218,10 +218,10 @@ def test_workspace_bytes(lib):
 
 
 def test_shared_prefix_workspace(lib):
-    # 64 requests x 32 heads over a 4096-token prefix: 8 chunks of 512 keys
-    # (32 kv heads x two blocks of 32 rows x 8 chunks: two items per CU)
+    # 64 requests x 32 heads over a 4096-token prefix: 4 chunks of 1024 keys
+    # (32 kv heads x two blocks of 32 rows x 4 chunks: one item per CU)
     n = attn.attn_shared_prefix_workspace_bytes(64, 32, 32, 128, 4096, 0)
-    rows = 64 * 32 * 8
+    rows = 64 * 32 * 4
     assert n == -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert attn.attn_shared_prefix_workspace_bytes(64, 32, 32, 128, 0, 0) == 0
     assert attn.attn_shared_prefix_workspace_bytes(64, 32, 5, 128, 4096, 0) == 0  # bad group

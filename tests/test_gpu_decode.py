@@ -247,6 +247,43 @@ def test_cascade_workload5_full_size():
     assert_close(lse[rows], rl, "bf16", "cascade lse")
 
 
+def test_cascade_two_streams_workload5():
+    """The prefix stage on a second stream, concurrent with the suffix decode
+    on the first (the two stages share nothing but the read-only cache), then
+    the merge once both are done: the same result as one stream."""
+    require_gpu()
+    c = wl.workload(5)
+    q = dev(c["q"])
+    kp, vp = dev(c["k_pages"]), dev(c["v_pages"])
+    R, H, D = q.shape
+    o_p, o_s = torch.empty_like(q), torch.empty_like(q)
+    l_p, l_s = (torch.empty((R, H), device="cuda") for _ in range(2))
+    pp, st, sl = dev(c["prefix_pages"]), dev(c["suffix_table"]), dev(c["suffix_lens"])
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    for rep in range(3):
+        side.wait_stream(main)
+        attn.attn_decode_shared_prefix(q, kp, vp, pp, c["prefix_len"], o_p, l_p, scale=c["scale"],
+                                       stream=side)
+        attn.attn_decode_paged(q, kp, vp, st, sl, o_s, l_s, max_kv_len=int(c["suffix_lens"].max()),
+                               scale=c["scale"])
+        main.wait_stream(side)
+        attn.attn_merge_states(o_p, l_p, o_s, l_s)
+        torch.cuda.synchronize()
+        o, lse = host(o_p), host(l_p)
+        if rep == 0:
+            first = (o.copy(), lse.copy())
+        else:
+            # the same kernels on the same data: bit-identical on every repetition
+            assert np.array_equal(o, first[0])
+            assert np.array_equal(lse, first[1])
+    rows = [0, 17, 63]
+    ro, rl = oracle.cascade_decode(c["q"][rows], c["k_pages"], c["v_pages"], c["prefix_pages"],
+                                   c["prefix_len"], c["suffix_table"][rows], c["suffix_lens"][rows],
+                                   c["scale"])
+    assert_close(o[rows], ro, "bf16", "cascade O")
+    assert_close(lse[rows], rl, "bf16", "cascade lse")
+
+
 @pytest.mark.parametrize("R,H,Hkv,plen,D", [
     (1, 1, 1, 1, 128), (3, 4, 4, 15, 128), (5, 8, 2, 100, 128), (70, 4, 4, 300, 128),
     (40, 8, 2, 1000, 128), (9, 4, 1, 517, 64), (64, 32, 32, 4096, 128), (16, 2, 2, 20000, 128),

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 
 #include "kernels.h"
 
@@ -22,6 +23,10 @@ constexpr int kGridYZ = 65535;
 bool dim_ok(int d) { return d == 64 || d == 128; }
 bool dtype_ok(int t) { return t == ATTN_BF16 || t == ATTN_F32; }
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+// Tensors are read and written with 16-byte vector accesses; lse, tables,
+// lengths and counters with 4-byte ones.  NULL passes (checked separately).
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool al4(const void* p) { return ((uintptr_t)p & 3) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int plan(int batch, int heads_kv, int max_kv_len, int num_cus, int requested, int* split,
@@ -32,12 +37,13 @@ int plan(int batch, int heads_kv, int max_kv_len, int num_cus, int requested, in
     if (requested > 0) {
         s = (requested + kMinSplit - 1) / kMinSplit * kMinSplit;
     } else {
-        // Aim for ~8 chunks per compute unit over the batch's worst case, in
-        // power-of-two chunks between 64 and 1024 tokens: long contexts and
-        // big batches get long chunks (less combine traffic), small batches
-        // get short ones (enough workgroups to fill the GPU).
-        const double per_item =
-            (double)batch * heads_kv * (double)max_kv_len / (8.0 * num_cus);
+        // The longest power-of-two chunk (64 .. 1024 tokens) that still
+        // leaves at least num_cus (sequence, kv head, chunk) items at the
+        // batch's worst case, batch * heads_kv * max_kv_len / s.  Measured
+        // over batch 1..128 and contexts 1k..32k (D = 128): every item pays
+        // a fixed start, so short chunks are slow, and this choice was the
+        // fastest or within 4% of it on every shape.
+        const double per_item = (double)batch * heads_kv * (double)max_kv_len / num_cus;
         s = kMinSplit;
         while (s < kMaxSplit && 2.0 * s <= per_item) s *= 2;
     }
@@ -90,6 +96,9 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
     if (batch == 0) return ATTN_OK;
     if (!q || !k_pages || !v_pages || !o || (!block_table && max_kv_len > 0))
         return ATTN_E_NULL;
+    if (!al16(q) || !al16(k_pages) || !al16(v_pages) || !al16(o) || !al16(workspace) ||
+        !al4(lse) || !al4(block_table) || !al4(kv_lens) || !al4(fallback_count))
+        return ATTN_E_ARG;
     if (batch > kGridYZ || heads_kv > kGridYZ) return ATTN_E_UNSUPPORTED;
     int split = 0, max_splits = 0;
     const int rc = plan(batch, heads_kv, max_kv_len, kPlanCUs, requested_split, &split, &max_splits);
@@ -146,7 +155,7 @@ const char* attn_status_str(int status) {
         case ATTN_E_UNSUPPORTED: return "unsupported configuration";
         case ATTN_E_WORKSPACE: return "workspace missing or too small";
         case ATTN_E_HIP: return "HIP launch error";
-        case ATTN_E_ARG: return "argument value out of domain";
+        case ATTN_E_ARG: return "argument value out of domain or misaligned pointer";
         default: return "unknown status";
     }
 }
@@ -162,6 +171,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
     if (!scale_ok(scale)) return ATTN_E_ARG;
     if (batch == 0 || seq_q == 0) return ATTN_OK;
     if (!q || !o || (seq_kv > 0 && (!k || !v))) return ATTN_E_NULL;
+    if (!al16(q) || !al16(k) || !al16(v) || !al16(o) || !al4(lse)) return ATTN_E_ARG;
     if ((long)batch * heads_q * ((seq_q + 255) / 256) > 0x7fffffffL) return ATTN_E_UNSUPPORTED;
     hipError_t e;
     if (dtype == ATTN_F32)
@@ -242,6 +252,7 @@ int attn_merge_states(void* o_a, float* lse_a, const void* o_b, const float* lse
     if (!dim_ok(head_dim)) return ATTN_E_UNSUPPORTED;
     if (rows == 0) return ATTN_OK;
     if (!o_a || !lse_a || !o_b || !lse_b) return ATTN_E_NULL;
+    if (!al16(o_a) || !al16(o_b) || !al4(lse_a) || !al4(lse_b)) return ATTN_E_ARG;
     return check_hip(attn::launch_merge_states(o_a, lse_a, o_b, lse_b, rows, head_dim,
                                                o_dtype == ATTN_F32, (hipStream_t)stream));
 }
@@ -283,6 +294,9 @@ static int shared_prefix_common(const void* q, const void* k_pages, const void* 
     if (!scale_ok(scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return ATTN_E_ARG;
     if (batch == 0) return ATTN_OK;
     if (!q || !k_pages || !v_pages || !prefix_pages || !o) return ATTN_E_NULL;
+    if (!al16(q) || !al16(k_pages) || !al16(v_pages) || !al16(o) || !al16(workspace) ||
+        !al4(lse) || !al4(prefix_pages))
+        return ATTN_E_ARG;
     const long rows = (long)batch * (heads_q / heads_kv);
     if ((rows + 63) / 64 > kGridYZ || heads_kv > kGridYZ) return ATTN_E_UNSUPPORTED;
     int chunk = 0, n_chunks = 0;

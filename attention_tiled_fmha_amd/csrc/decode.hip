@@ -305,43 +305,71 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
 // Combine the per-chunk states of every (sequence, head) row that was split:
 //   lse = ln sum_c exp(lse_c),  o = sum_c exp(lse_c - lse) o_c.
+// One 256-thread workgroup per row: D/4 lanes cover the row's dims with
+// 16-byte loads, and the 256 / (D/4) lane groups take every NG-th chunk,
+// each folding its chunks with a running max; the groups' states are then
+// merged through LDS.  The many chunks of a few rows (small batches) are
+// read by the whole workgroup at once instead of one wavefront in sequence.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-    const int lane = threadIdx.x & 63;
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (long)a.B * a.Hq) return;
+    constexpr int LPR = D / 4;       // lanes per row, 4 dims each
+    constexpr int NG = 256 / LPR;    // chunk groups: 8 (D = 128) or 16 (D = 64)
+    __shared__ float s_m[NG], s_l[NG];
+    __shared__ f32x4 s_o[NG][LPR];
+    const long row = blockIdx.x;
     const int b = (int)(row / a.Hq);
     const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
     const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
-    if (nsplit <= 1) return;  // written directly by the split kernel
+    if (nsplit <= 1) return;  // written directly by the split kernel (uniform per workgroup)
+    const int grp = threadIdx.x / LPR, dl = threadIdx.x % LPR;
     const float* ls = a.ws_lse + row * a.max_splits;
-    float M = -INFINITY;
-    for (int c = lane; c < nsplit; c += kWave) M = fmaxf(M, ls[c]);
-    M = wave_max(M);
-    constexpr int PER = D / kWave;  // 1 or 2 dims per lane
-    float ot[PER] = {};
-    float lt = 0.f;
-    for (int c = 0; c < nsplit; c++) {
+    const f32x4* os = (const f32x4*)(a.ws_o + row * a.max_splits * D) + dl;
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = grp; c < nsplit; c += NG) {
         const float lc = ls[c];
-        const float w = (lc == -INFINITY) ? 0.f : expf(lc - M);
-        lt += w;
-        const float* oc = a.ws_o + (row * a.max_splits + c) * D;
+        const f32x4 oc = os[(size_t)c * LPR];
+        const float mn = fmaxf(m, lc);
+        const float sa = (m == -INFINITY) ? 0.f : expf(m - mn);
+        const float sb = (lc == -INFINITY) ? 0.f : expf(lc - mn);
+        l = fmaf(l, sa, sb);
 #pragma unroll
-        for (int e = 0; e < PER; e++) ot[e] = fmaf(w, oc[lane * PER + e], ot[e]);
+        for (int e = 0; e < 4; e++) acc[e] = fmaf(acc[e], sa, sb * oc[e]);
+        m = mn;
+    }
+    if (dl == 0) {
+        s_m[grp] = m;
+        s_l[grp] = l;
+    }
+    s_o[grp][dl] = acc;
+    __syncthreads();
+    if (grp != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NG; g++) M = fmaxf(M, s_m[g]);
+    float lt = 0.f;
+    f32x4 ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < NG; g++) {
+        const float w = (s_m[g] == -INFINITY) ? 0.f : expf(s_m[g] - M);
+        lt = fmaf(w, s_l[g], lt);
+        const f32x4 og = s_o[g][dl];
+#pragma unroll
+        for (int e = 0; e < 4; e++) ot[e] = fmaf(w, og[e], ot[e]);
     }
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-    for (int e = 0; e < PER; e++) {
-        const int d = lane * PER + e;
-        if (a.out_f32) ((float*)a.o)[row * D + d] = ot[e] * inv;
-        else ((uint16_t*)a.o)[row * D + d] = f32_to_bf16(ot[e] * inv);
+    if (a.out_f32) {
+        *(f32x4*)((float*)a.o + row * D + 4 * dl) = f32x4{ot[0] * inv, ot[1] * inv, ot[2] * inv, ot[3] * inv};
+    } else {
+        *(u32x2*)((uint16_t*)a.o + row * D + 4 * dl) =
+            u32x2{(uint32_t)f32_to_bf16(ot[0] * inv) | ((uint32_t)f32_to_bf16(ot[1] * inv) << 16),
+                  (uint32_t)f32_to_bf16(ot[2] * inv) | ((uint32_t)f32_to_bf16(ot[3] * inv) << 16)};
     }
-    if (a.lse && lane == 0) a.lse[row] = lt > 0.f ? M + logf(lt) : -INFINITY;
+    if (a.lse && dl == 0) a.lse[row] = lt > 0.f ? M + logf(lt) : -INFINITY;
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
-    const long rows = (long)a.B * a.Hq;
-    const unsigned blocks = (unsigned)((rows + 3) / 4);
+    const unsigned blocks = (unsigned)((long)a.B * a.Hq);
     if (a.D == 64) decode_combine_kernel<64><<<blocks, 256, 0, stream>>>(a);
     else decode_combine_kernel<128><<<blocks, 256, 0, stream>>>(a);
     return hipGetLastError();

@@ -254,6 +254,51 @@ def bench_cascade(steps, warmup, fp8=False):
                 frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
 
 
+def bench_graph_decode(steps, warmup, B, length_range, layers=8):
+    """The attention of one decode step of a model with ``layers`` layers: per
+    layer a GQA paged decode (B Hq32 Hkv8 D128 bf16, L~U[length_range], split
+    decode + combine) over the layer's own cache.  Launched eagerly from
+    Python, then replayed as one captured HIP graph; both timed back to back,
+    so host launch gaps count."""
+    per_layer = []
+    for layer in range(layers):
+        d = wl.paged_decode_inputs(B, 32, 8, 128, "bf16", 1100 + layer, length_range=length_range)
+        maxlen = int(d["kv_lens"].max())
+        t = dict(q=dev(d["q"]), kp=dev(d["k_pages"]), vp=dev(d["v_pages"]),
+                 bt=dev(d["block_table"]), kl=dev(d["kv_lens"]), maxlen=maxlen, scale=d["scale"],
+                 nbytes=kv_bytes(d["kv_lens"], 8, 128),
+                 ws=torch.empty(max(1, attn.attn_decode_workspace_bytes(B, 32, 8, 128, maxlen)),
+                                dtype=torch.uint8, device="cuda"))
+        t["o"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty(t["q"].shape[:2], device="cuda")
+        per_layer.append(t)
+
+    def step(i=0):
+        for t in per_layer:
+            attn.attn_decode_paged(t["q"], t["kp"], t["vp"], t["bt"], t["kl"], t["o"], t["lse"],
+                                   max_kv_len=t["maxlen"], scale=t["scale"], workspace=t["ws"])
+
+    eager, _, _ = time_launches(step, steps, warmup)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    graph, _, _ = time_launches(lambda i: g.replay(), steps, warmup)
+    nbytes = sum(t["nbytes"] for t in per_layer)
+    eager_ms, graph_ms = float(np.mean(eager)), float(np.mean(graph))
+    lo, hi = length_range
+    return dict(workload=f"{layers} layers x paged decode GQA B{B} Hq32 Hkv8 D128 bf16, "
+                         f"L~U[{lo},{hi}], page 16, each layer its own cache",
+                kv_bytes=nbytes, eager_us=round(eager_ms * 1e3, 2), graph_us=round(graph_ms * 1e3, 2),
+                eager_gbs=round(nbytes / (eager_ms * 1e-3) / 1e9, 1),
+                graph_gbs=round(nbytes / (graph_ms * 1e-3) / 1e9, 1))
+
+
 def cpu_baseline(target_s=15.0):
     """The fp64 oracle on (b, h) pairs of the prefill workload, timed on the
     host cores; throughput in the bench's unit (algorithmic causal TFLOP/s)."""
@@ -327,6 +372,11 @@ def main():
         log("cascade workload 5, FP8 cache ...")
         decode["workload5_fp8"] = bench_cascade(args.steps, args.warmup, fp8=True)
         log(f"  {decode['workload5_fp8']['gbs']:.0f} GB/s")
+        for key, B, lr in (("decode_step_graph_b1", 1, (256, 1024)),
+                           ("decode_step_graph_b4", 4, (1024, 4096))):
+            log(f"8-layer decode step B{B}, eager vs graph replay ...")
+            decode[key] = bench_graph_decode(args.steps, args.warmup, B, lr)
+            log(f"  eager {decode[key]['eager_us']:.1f} us, graph {decode[key]['graph_us']:.1f} us")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle) ...")

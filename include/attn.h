@@ -18,6 +18,11 @@
  *  - Tensor arguments are DEVICE pointers owned by the caller; the library
  *    never allocates, frees or retains them.  Scratch space (where needed)
  *    is passed in by the caller as `workspace`.
+ *  - Alignment: q, k, v, o, the page pools and the workspace are accessed
+ *    with 16-byte vector loads and stores and must be 16-byte aligned; lse,
+ *    block tables, page lists, kv_lens and counters must be 4-byte aligned
+ *    (hipMalloc and torch allocations are 256-byte aligned).  A misaligned
+ *    pointer returns ATTN_E_ARG.
  *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *    NULL = the default stream).  Results are valid once the stream has
  *    synchronised.  Nothing is launched when a call returns an error.
@@ -50,7 +55,8 @@ typedef enum {
     ATTN_E_UNSUPPORTED = 3, /* well-formed but not implemented (head_dim, ...)  */
     ATTN_E_WORKSPACE = 4,   /* workspace missing or smaller than required       */
     ATTN_E_HIP = 5,         /* the HIP runtime reported an error on launch      */
-    ATTN_E_ARG = 6          /* a value outside its domain (scale <= 0 or NaN)   */
+    ATTN_E_ARG = 6          /* a value outside its domain (scale <= 0 or NaN,
+                               a misaligned pointer)                            */
 } attn_status;
 
 /* ATTN_FP8_E4M3 names an FP8 KV cache (OCP E4M3 bytes); it is accepted only

@@ -189,13 +189,35 @@ def test_shared_prefix_fp8_checks(lib):
                                          16, 2, 0, 0.1, None, 0, None) == E_UNSUP
 
 
+def test_misaligned_pointers(lib):
+    # rejected on the host before any launch: tensors need 16-byte alignment,
+    # lse / tables / lengths 4-byte
+    odd16 = ctypes.c_void_p(0x1008)
+    odd4 = ctypes.c_void_p(0x1002)
+    assert prefill(lib, q=odd16) == E_ARG
+    assert prefill(lib, o=odd16) == E_ARG
+    assert prefill(lib, lse=odd4) == E_ARG
+    assert decode(lib, k=odd16) == E_ARG
+    assert decode(lib, kl=odd4) == E_ARG
+    assert decode(lib, lse=odd4) == E_ARG
+    assert decode_fp8(lib, v=odd16) == E_ARG
+    assert lib.attn_merge_states(odd16, FAKE, FAKE, FAKE, 4, 128, 0, None) == E_ARG
+    assert lib.attn_merge_states(FAKE, odd4, FAKE, FAKE, 4, 128, 0, None) == E_ARG
+    assert lib.attn_decode_shared_prefix(FAKE, FAKE, FAKE, odd4, 64, FAKE, None, 4, 4, 4, 128,
+                                         16, 0, 0, 0.1, None, 0, None) == E_ARG
+    assert lib.attn_decode_shared_prefix(FAKE, FAKE, odd16, FAKE, 64, FAKE, None, 4, 4, 4, 128,
+                                         16, 0, 0, 0.1, None, 0, None) == E_ARG
+
+
 def test_decode_plan(lib):
     # workload shapes: long contexts over many sequences get 1024-token chunks
     assert attn.attn_decode_plan(32, 32, 8192) == (1024, 8)
     assert attn.attn_decode_plan(128, 8, 32768) == (1024, 32)
-    # a small batch gets short chunks, so there are enough workgroups
+    # a small batch gets shorter chunks, about one item per CU: 1 x 8 kv heads
+    # x 4096 tokens over 256 CUs -> 128-token chunks, 32 per sequence
     s, n = attn.attn_decode_plan(1, 8, 4096)
-    assert s == 64 and n == 64
+    assert s == 128 and n == 32
+    assert attn.attn_decode_plan(4, 8, 4096) == (512, 8)
     assert attn.attn_decode_plan(1, 1, 0) == (64, 1)
     # forced chunk lengths round up to a multiple of 64
     assert attn.attn_decode_plan(4, 4, 1000, requested_split=100) == (128, 8)

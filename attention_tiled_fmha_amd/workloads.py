@@ -204,6 +204,19 @@ def paged_decode_inputs(B, Hq, Hkv, D, dtype, seed, lengths=None,
                 max_kv_len=int(lengths.max(initial=0)))
 
 
+def paged_prefill_inputs(B, Hq, Hkv, Tq, D, dtype, seed, lengths=None,
+                         length_range=(1024, 8192), length_dist="uniform",
+                         page_size=PAGE_SIZE, tail_garbage=True, permute=True):
+    """Chunked prefill: Tq new query tokens per sequence (its last Tq
+    positions, q [B,Hq,Tq,D]) over the paged cache of ``paged_decode_inputs``
+    (same seed, same draws), whose kv_lens count the new tokens too."""
+    d = paged_decode_inputs(B, Hq, Hkv, D, dtype, seed, lengths, length_range, length_dist,
+                            page_size, tail_garbage, permute)
+    d["q"] = normal(generator(seed + 7919), (B, Hq, Tq, D), dtype)
+    d["Tq"] = Tq
+    return d
+
+
 def paged_decode_fp8_inputs(B, Hq, Hkv, D, seed, lengths=None, length_range=(512, 8192),
                             length_dist="uniform", kv_scale=1.0 / 32, page_size=PAGE_SIZE,
                             tail_garbage=True):

@@ -50,6 +50,9 @@ def load(path=_LIB_PATH):
     lib.oracle_decode_paged.argtypes = [vp, vp, vp, ip, vp, vp, dp, dp, ip, ip,
                                         ip, ip, ip, ip, ctypes.c_long,
                                         ctypes.c_double, ip]
+    lib.oracle_prefill_paged.restype = ip
+    lib.oracle_prefill_paged.argtypes = [vp, vp, vp, ip, vp, vp, dp, dp, ip, ip, ip, ip, ip,
+                                         ip, ip, ctypes.c_long, ip, ctypes.c_double, ip]
     lib.oracle_decode_paged_fp8.restype = ip
     cd = ctypes.c_double
     lib.oracle_decode_paged_fp8.argtypes = [vp, ip, vp, vp, cd, cd, vp, vp, dp, dp, ip, ip, ip,
@@ -150,6 +153,39 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale, threads=None,
                                  float(scale), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_decode_paged failed ({rc})")
+    return o, lse
+
+
+def prefill_paged(q, k_pages, v_pages, block_table, kv_lens, causal, scale, threads=None,
+                  lib=None):
+    """Prefill of Tq new tokens per sequence against a paged cache.
+
+    q [B,Hq,Tq,D] (the last Tq positions of each sequence); k_pages, v_pages
+    [P,Hkv,page,D]; block_table int32 [B,maxp]; kv_lens int32 [B] (keys per
+    sequence, the new tokens included).  Causal: query i sees key j when
+    j <= i + kv_lens[b] - Tq.  Returns (o [B,Hq,Tq,D], lse [B,Hq,Tq]) in fp64.
+    """
+    lib = lib or _get()
+    q = np.ascontiguousarray(q)
+    k_pages = np.ascontiguousarray(k_pages)
+    v_pages = np.ascontiguousarray(v_pages)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    kl = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    dt = _dtype_code(q)
+    if _dtype_code(k_pages) != dt or _dtype_code(v_pages) != dt:
+        raise TypeError("q and the pages must share one element type")
+    B, Hq, Tq, D = q.shape
+    P, Hkv, page, Dk = k_pages.shape
+    if Dk != D or v_pages.shape != k_pages.shape or bt.shape[0] != B or kl.shape != (B,):
+        raise ValueError("shape mismatch")
+    o = np.zeros((B, Hq, Tq, D), np.float64)
+    lse = np.zeros((B, Hq, Tq), np.float64)
+    rc = lib.oracle_prefill_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), dt, _ptr(bt),
+                                  _ptr(kl), _dptr(o), _dptr(lse), B, Hq, Hkv, Tq, D, page,
+                                  bt.shape[1], P, int(bool(causal)), float(scale),
+                                  threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill_paged failed ({rc})")
     return o, lse
 
 

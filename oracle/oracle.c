@@ -264,6 +264,72 @@ int oracle_decode_paged(const void *q, const void *k_pages, const void *v_pages,
 }
 
 /*
+ * Prefill against a paged cache (chunked prefill).  The Tq query tokens of
+ * sequence b are its last Tq positions; they attend the sequence's
+ * kv_lens[b] cached keys, which include themselves, so query i sits at
+ * position kv_lens[b] - Tq + i and, under the causal mask, sees key j
+ * exactly when j <= i + (kv_lens[b] - Tq): the bottom-right alignment of
+ * attend_rows with tk = kv_lens[b].  (The xhh.club summary, "FlashAttention
+ * and paged attention", says the tiled kernel and the paged cache can be
+ * used together; the gather is the paged-cache reading above.)
+ * q is [B][Hq][Tq][D]; k_pages, v_pages, block_table, kv_lens as
+ * oracle_decode_paged; o is fp64 [B][Hq][Tq][D], lse fp64 [B][Hq][Tq].
+ */
+int oracle_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
+                         int dtype, const int32_t *block_table,
+                         const int32_t *kv_lens, double *o, double *lse,
+                         int B, int Hq, int Hkv, int Tq, int D, int page_size,
+                         int max_pages, long num_pages, int causal, double scale,
+                         int nthreads)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Tq < 0 || D <= 0 || page_size <= 0)
+        return -1;
+    for (int b = 0; b < B; b++) {
+        const int L = kv_lens[b];
+        if (L < 0 || (L + page_size - 1) / page_size > max_pages)
+            return -1;
+        for (int p = 0; p < (L + page_size - 1) / page_size; p++) {
+            const int32_t pg = block_table[(size_t)b * max_pages + p];
+            if (pg < 0 || pg >= num_pages)
+                return -1;
+        }
+    }
+    const int group = Hq / Hkv;
+    int failed = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic)
+    for (long bh = 0; bh < (long)B * Hq; bh++) {
+        const int b = (int)(bh / Hq), h = (int)(bh % Hq), kvh = h / group;
+        const int L = kv_lens[b];
+        const int32_t *table = block_table + (size_t)b * max_pages;
+        double *K = malloc(sizeof(double) * ((size_t)L * D + 1));
+        double *V = malloc(sizeof(double) * ((size_t)L * D + 1));
+        double *Q = malloc(sizeof(double) * ((size_t)Tq * D + 1));
+        double *S = malloc(sizeof(double) * ((size_t)Tq * L + 1));
+        if (!K || !V || !Q || !S) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            /* the sequence's logical key/value rows, through its table */
+            for (int t = 0; t < L; t++) {
+                const size_t page = (size_t)table[t / page_size];
+                const size_t src = ((page * Hkv + kvh) * page_size + t % page_size) * D;
+                for (int c = 0; c < D; c++) {
+                    K[(size_t)t * D + c] = load_elem(k_pages, dtype, src + c);
+                    V[(size_t)t * D + c] = load_elem(v_pages, dtype, src + c);
+                }
+            }
+            const size_t qbase = (size_t)bh * Tq * D;
+            for (size_t e = 0; e < (size_t)Tq * D; e++)
+                Q[e] = load_elem(q, dtype, qbase + e);
+            attend_rows(Q, K, V, Tq, L, D, causal, scale, S, o + qbase, lse + (size_t)bh * Tq);
+        }
+        free(K); free(V); free(Q); free(S);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
  * Paged decode over an FP8 cache: k_pages and v_pages are E4M3 bytes
  * [num_pages][Hkv][page_size][D], dequantised as k_scale * e4m3(byte) and
  * v_scale * e4m3(byte); q is in dtype q_dtype.  Everything else as

@@ -499,11 +499,99 @@ def check_decode_fp8(lib):
             _close(l1[b, h], s + math.log(L), 1e-13, f"fp8 uniform lse L={L}")
 
 
+# --- prefill against a paged cache (chunked prefill) -----------------------------
+
+def _tiny_paged(r, B, Hkv, D, page, lens):
+    """A random pool holding each sequence's pages at permuted places."""
+    npages = [-(-L // page) for L in lens]
+    pool = max(1, sum(npages))
+    phys = r.permutation(pool).astype(np.int32)
+    table = np.zeros((B, max(1, max(npages))), np.int32)
+    at = 0
+    for b, n in enumerate(npages):
+        table[b, :n] = phys[at:at + n]
+        at += n
+    kp = r.standard_normal((pool, Hkv, page, D))
+    vp = r.standard_normal((pool, Hkv, page, D))
+    return kp, vp, table
+
+
+def check_prefill_paged_brute(lib):
+    """Gather through the table and bottom-right causal offset against the
+    pure-Python brute force on each sequence's logical keys."""
+    r = _rng(41)
+    for (B, Hq, Hkv, Tq, D, page, lens) in ((2, 2, 1, 3, 3, 2, [5, 3]),
+                                            (3, 2, 2, 2, 2, 4, [1, 7, 2]),
+                                            (1, 4, 2, 4, 2, 2, [4])):
+        kp, vp, table = _tiny_paged(r, B, Hkv, D, page, lens)
+        q = r.standard_normal((B, Hq, Tq, D))
+        kl = np.asarray(lens, np.int32)
+        for causal in (False, True):
+            o, lse = oracle.prefill_paged(q, kp, vp, table, kl, causal, 0.6, lib=lib)
+            for b, L in enumerate(lens):
+                K = [[[float(x) for x in kp[table[b, t // page], h, t % page]] for t in range(L)]
+                     for h in range(Hkv)]
+                V = [[[float(x) for x in vp[table[b, t // page], h, t % page]] for t in range(L)]
+                     for h in range(Hkv)]
+                bo, bl = brute.attention([q[b].tolist()], [K], [V], causal, 0.6)
+                _close(o[b], bo[0], 1e-14, f"paged prefill brute o b={b} causal={causal}")
+                _close(lse[b], bl[0], 1e-14, f"paged prefill brute lse b={b} causal={causal}")
+
+
+def check_prefill_paged_identical_keys(lib):
+    """Identical keys: query i of the chunk sees n_i = kv_len - Tq + i + 1 keys
+    (causal, bottom-right) or all kv_len, so O_i is the mean of those value
+    rows and lse_i = s_i + ln n_i, a closed form in the offset."""
+    r = _rng(43)
+    B, Hq, Hkv, Tq, D, page = 2, 2, 1, 5, 4, 4
+    lens = [9, 5]
+    kp, vp, table = _tiny_paged(r, B, Hkv, D, page, lens)
+    k0 = np.array([0.5, -1.0, 0.25, 2.0])
+    kp[:] = k0
+    q = r.standard_normal((B, Hq, Tq, D))
+    kl = np.asarray(lens, np.int32)
+    for causal in (False, True):
+        o, lse = oracle.prefill_paged(q, kp, vp, table, kl, causal, 0.8, lib=lib)
+        for b, L in enumerate(lens):
+            vrows = np.stack([vp[table[b, t // page], 0, t % page] for t in range(L)])
+            for h in range(Hq):
+                for i in range(Tq):
+                    n = L - Tq + i + 1 if causal else L
+                    s = 0.8 * float(q[b, h, i] @ k0)
+                    _close(o[b, h, i], vrows[:n].mean(0), 1e-13, f"identical keys o {b,h,i}")
+                    _close(lse[b, h, i], s + math.log(n), 1e-13, f"identical keys lse {b,h,i}")
+
+
+def check_prefill_paged_placement_and_decode(lib):
+    """The same logical cache under two physical placements gives the same
+    bits, and a one-token chunk is the paged decode of that token."""
+    r = _rng(47)
+    B, Hq, Hkv, D, page = 3, 4, 2, 8, 4
+    lens = [13, 4, 9]
+    kp, vp, table = _tiny_paged(r, B, Hkv, D, page, lens)
+    q = r.standard_normal((B, Hq, 3, D))
+    kl = np.asarray(lens, np.int32)
+    # move every page to a new place
+    perm = r.permutation(kp.shape[0])
+    kp2 = np.empty_like(kp); vp2 = np.empty_like(vp)
+    kp2[perm] = kp; vp2[perm] = vp
+    table2 = perm[table].astype(np.int32)
+    for causal in (False, True):
+        o1, l1 = oracle.prefill_paged(q, kp, vp, table, kl, causal, 0.4, lib=lib)
+        o2, l2 = oracle.prefill_paged(q, kp2, vp2, table2, kl, causal, 0.4, lib=lib)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "page placement changed result"
+    o, l = oracle.prefill_paged(q[:, :, 2:], kp, vp, table, kl, True, 0.4, lib=lib)
+    od, ld = oracle.decode_paged(q[:, :, 2], kp, vp, table, kl, 0.4, lib=lib)
+    _close(o[:, :, 0], od, 1e-15, "one-token chunk vs decode o")
+    _close(l[:, :, 0], ld, 1e-15, "one-token chunk vs decode lse")
+
+
 ALL_CHECKS = [
     check_hand_2x2, check_identical_keys, check_dominant_score,
     check_single_key_and_row0, check_scale_zero, check_brute_force, check_scipy,
     check_rows_sum_to_one, check_permutation, check_merge_split, check_merge_algebra,
     check_cascade, check_decode_vs_prefill, check_gqa_mapping, check_token_set,
     check_lse_dropped_page, check_tail_garbage, check_bf16_widening, check_unified_fallback,
-    check_e4m3_values, check_decode_fp8,
+    check_e4m3_values, check_decode_fp8, check_prefill_paged_brute,
+    check_prefill_paged_identical_keys, check_prefill_paged_placement_and_decode,
 ]

@@ -45,6 +45,18 @@ MUTATIONS = {
     "e4m3 no NaN code": ("if (e == 15 && m == 7)\n        return NAN;", ""),
     "fp8 key scale ignored": ("K[(size_t)t * D + c] = k_scale * oracle_e4m3_value",
                               "K[(size_t)t * D + c] = oracle_e4m3_value"),
+    "paged prefill reads sequence 0's table": (
+        "const int32_t *table = block_table + (size_t)b * max_pages;",
+        "const int32_t *table = block_table + (size_t)0 * max_pages;"),
+    "paged prefill causal flag dropped": (
+        "attend_rows(Q, K, V, Tq, L, D, causal, scale, S, o + qbase, lse + (size_t)bh * Tq);",
+        "attend_rows(Q, K, V, Tq, L, D, 0, scale, S, o + qbase, lse + (size_t)bh * Tq);"),
+    "paged prefill queries of head 0": (
+        "const size_t qbase = (size_t)bh * Tq * D;",
+        "const size_t qbase = (size_t)(bh - h) * Tq * D;"),
+    "paged prefill gathers the wrong kv head": (
+        "const int b = (int)(bh / Hq), h = (int)(bh % Hq), kvh = h / group;\n        const int L = kv_lens[b];",
+        "const int b = (int)(bh / Hq), h = (int)(bh % Hq), kvh = h % Hkv;\n        const int L = kv_lens[b];"),
     "fp8 scales swapped": ("V[(size_t)t * D + c] = v_scale * oracle_e4m3_value",
                            "V[(size_t)t * D + c] = k_scale * oracle_e4m3_value"),
 }

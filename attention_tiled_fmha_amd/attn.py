@@ -35,6 +35,8 @@ SIGNATURES = {
     "attn_shared_prefix_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "attn_decode_shared_prefix": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i,
                                        _i, _i, _f, _vp, _sz, _vp]),
+    "attn_prefill_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                               _i, _i, _f, _vp]),
     "attn_decode_shared_prefix_fp8": (_i, [_vp, _vp, _vp, _f, _f, _vp, _i, _vp, _vp, _i, _i, _i,
                                            _i, _i, _i, _f, _vp, _sz, _vp]),
 }
@@ -120,6 +122,37 @@ def attn_prefill(q, k, v, o, lse=None, causal=False, scale=None, stream=None):
     scale = D ** -0.5 if scale is None else scale
     _check(load().attn_prefill(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, Tq, Tk, D, dt,
                                int(bool(causal)), float(scale), _stream(stream)), "attn_prefill")
+
+
+def attn_prefill_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse=None, causal=True,
+                       scale=None, stream=None):
+    """Chunked prefill: q, o bf16 [B,Hq,Tq,D] (each sequence's last Tq
+    positions); k_pages, v_pages bf16 [P,Hkv,16,D]; block_table int32
+    [B,maxp]; kv_lens int32 [B] (keys per sequence, the chunk included);
+    lse fp32 [B,Hq,Tq] or None."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"),
+                 (block_table, "block_table"), (kv_lens, "kv_lens"), (o, "o")):
+        _dense(t, n)
+    B, Hq, Tq, D = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    if o.shape != q.shape or v_pages.shape != k_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if block_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
+        raise TypeError("block_table and kv_lens must be int32")
+    if block_table.shape[0] != B or kv_lens.shape != (B,):
+        raise ValueError("block_table / kv_lens shape mismatch")
+    if lse is not None:
+        _dense(lse, "lse")
+        if lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, Hq, Tq]")
+    dt = _dtype(q)
+    if not (_dtype(k_pages) == _dtype(v_pages) == dt):
+        raise TypeError("q and the pages must share one element type")
+    scale = D ** -0.5 if scale is None else scale
+    _check(load().attn_prefill_paged(
+        _p(q), _p(k_pages), _p(v_pages), _p(block_table), _p(kv_lens), _p(o), _p(lse), B, Hq,
+        Hkv, Tq, D, page, block_table.shape[1], dt, int(bool(causal)), float(scale),
+        _stream(stream)), "attn_prefill_paged")
 
 
 def attn_decode_plan(batch, heads_kv, max_kv_len, num_cus=0, requested_split=0):

@@ -184,6 +184,29 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
     return check_hip(e);
 }
 
+int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* block_table, const int32_t* kv_lens, void* o, float* lse,
+                       int batch, int heads_q, int heads_kv, int seq_q, int head_dim,
+                       int page_size, int max_pages_per_seq, int dtype, int causal, float scale,
+                       void* stream) {
+    if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+    if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || seq_q < 0 || max_pages_per_seq < 0)
+        return ATTN_E_SHAPE;
+    if (heads_q % heads_kv) return ATTN_E_SHAPE;
+    if (!dim_ok(head_dim) || page_size != kPageSize) return ATTN_E_UNSUPPORTED;
+    if (!scale_ok(scale)) return ATTN_E_ARG;
+    if (batch == 0 || seq_q == 0) return ATTN_OK;
+    if (!q || !k_pages || !v_pages || !block_table || !kv_lens || !o) return ATTN_E_NULL;
+    if (!al16(q) || !al16(k_pages) || !al16(v_pages) || !al16(o) || !al4(lse) ||
+        !al4(block_table) || !al4(kv_lens))
+        return ATTN_E_ARG;
+    if ((long)batch * heads_q * ((seq_q + 255) / 256) > 0x7fffffffL) return ATTN_E_UNSUPPORTED;
+    return check_hip(attn::launch_prefill_paged_bf16(q, k_pages, v_pages, block_table, kv_lens, o,
+                                                     lse, batch, heads_q, heads_kv, seq_q,
+                                                     head_dim, max_pages_per_seq, causal != 0,
+                                                     scale, (hipStream_t)stream));
+}
+
 int attn_decode_plan(int batch, int heads_kv, int max_kv_len, int num_cus, int requested_split,
                      int* split_tokens, int* max_splits) {
     if (!split_tokens || !max_splits) return ATTN_E_NULL;

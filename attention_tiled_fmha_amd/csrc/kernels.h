@@ -14,6 +14,14 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                float* lse, int B, int Hq, int Hkv, int Tq, int Tk,
                                int D, bool causal, float scale, hipStream_t stream);
 
+// Prefill of Tq new tokens per sequence against a paged bf16 cache
+// [pages][Hkv][16][D]; sequence b has kv_lens[b] keys, its queries are its
+// last Tq positions (causal diagonal at kv_lens[b] - Tq).
+hipError_t launch_prefill_paged_bf16(const void* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* block_table, const int32_t* kv_lens,
+                                     void* o, float* lse, int B, int Hq, int Hkv, int Tq, int D,
+                                     int bt_stride, bool causal, float scale, hipStream_t stream);
+
 // Dense prefill, fp32 in/out, fp32 arithmetic (the exactness test mode).
 hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* o,
                               float* lse, int B, int Hq, int Hkv, int Tq, int Tk, int D,

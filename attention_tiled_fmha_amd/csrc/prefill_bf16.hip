@@ -128,6 +128,45 @@ __device__ __forceinline__ void load_stage(Stage& st, const uint16_t* __restrict
     for (int j = 0; j < 4; j++) st.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, off.v + j * D * 2, 0, 0);
 }
 
+// Paged K/V (prefill against a paged cache, [pages][Hkv][16][D]): within a
+// 32-key tile, the K rows of one wavefront's chunks (4 for D = 128, 8 for
+// D = 64) and the keys of its V units (the same) lie in one 16-token page,
+// slot 0 or 1 of the tile, so each wavefront loads through a descriptor
+// over that page alone: its base from the sequence's block-table entry, its
+// size the page's valid rows (a page at or past the sequence's length has
+// none and reads zeros without touching memory).
+struct PagedKV {
+    const uint16_t* kpool;
+    const uint16_t* vpool;
+    const int32_t* table;   // this sequence's block-table row
+    int Hkv, kvh, Tk;
+    int slot_k, slot_v;     // this wavefront's page within a tile, -1 = no rows
+};
+
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* pool, const PagedKV& pk,
+                                                            int k0, int slot) {
+    const int p = k0 / 16 + max(slot, 0);
+    const int valid = slot < 0 ? 0 : max(0, min(16, pk.Tk - p * 16));
+    const int bytes = __builtin_amdgcn_readfirstlane(valid * D * 2);
+    const uint16_t* base = pool;
+    if (bytes > 0) {
+        const int phys = __builtin_amdgcn_readfirstlane(pk.table[p]);
+        base = pool + ((size_t)phys * pk.Hkv + pk.kvh) * 16 * D;
+    }
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kRsrcWord3);
+}
+
+template <int D>
+__device__ __forceinline__ void load_stage_paged(Stage& st, const PagedKV& pk, int k0k, int k0v,
+                                                 const LoadOffsets<D>& off) {
+    const __amdgpu_buffer_rsrc_t rk = page_rsrc<D>(pk.kpool, pk, k0k, pk.slot_k);
+    const __amdgpu_buffer_rsrc_t rv = page_rsrc<D>(pk.vpool, pk, k0v, pk.slot_v);
+    st.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; j++) st.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, off.v + j * D * 2, 0, 0);
+}
+
 template <int D>
 __device__ __forceinline__ void store_stage(const Stage& st, unsigned char* kbuf,
                                             unsigned char* vbuf, int tid, bool do_k, bool do_v) {
@@ -150,12 +189,13 @@ __device__ __forceinline__ void store_stage(const Stage& st, unsigned char* kbuf
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                         float* __restrict__ lse, int BH, int Hq, int Hkv, int Tq, int Tk,
-                         int n_qtiles, float scale_log2) {
+                         float* __restrict__ lse, int BH, int Hq, int Hkv, int Tq, int Tk_dense,
+                         int n_qtiles, float scale_log2, const int32_t* __restrict__ block_table,
+                         const int32_t* __restrict__ kv_lens, int bt_stride) {
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF_BYTES];
 
@@ -178,11 +218,14 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int q0 = qt * kBM;
     const int qw0 = q0 + rb * 32;        // this wavefront's first row
     const int qrow = qw0 + li;           // the query row of this lane
+    // paged: the sequence's own key count (its chunk of Tq queries is its
+    // last Tq positions, so the causal diagonal sits at kv_len - Tq)
+    const int Tk = PAGED ? __builtin_amdgcn_readfirstlane(kv_lens[b]) : Tk_dense;
     const int diag = Tk - Tq;
 
     const uint16_t* qp = q + (size_t)bh * Tq * D;
-    const uint16_t* kp = k + (size_t)(b * Hkv + kvh) * Tk * D;
-    const uint16_t* vp = v + (size_t)(b * Hkv + kvh) * Tk * D;
+    const uint16_t* kp = PAGED ? k : k + (size_t)(b * Hkv + kvh) * Tk * D;
+    const uint16_t* vp = PAGED ? v : v + (size_t)(b * Hkv + kvh) * Tk * D;
 
     // Q fragments (B operand of S^T = K Q^T): row qrow, dims 16s + 8hi .. +7.
     // Loaded unconditionally (clamped row, zeroed past Tq) so that no
@@ -228,10 +271,20 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     pf[0] = pf[1] = bf16x8{};
     for (int i = tid; i < C::V_BYTES / 16; i += kThreads)
         *(u32x4*)(smem + C::BUF_BYTES + C::K_BYTES + 16 * i) = u32x4{0, 0, 0, 0};
-    const LoadOffsets<D> off(tid);
+    LoadOffsets<D> off(tid);
+    PagedKV pk{};
+    if constexpr (PAGED) {
+        // first K row / V key of this wavefront's share of a tile
+        const int rowk = (wave * 64) / C::CPR, rowv = 4 * ((wave * 64) / (D / 2));
+        pk = PagedKV{kp, vp, block_table + (size_t)b * bt_stride, Hkv, kvh, Tk,
+                     rowk < kBN ? rowk / 16 : -1, rowv < kBN ? rowv / 16 : -1};
+        off.k -= max(pk.slot_k, 0) * 16 * D * 2;   // offsets within the page
+        off.v -= max(pk.slot_v, 0) * 16 * D * 2;
+    }
     Stage st0, st1;
     auto load_pair = [&](Stage& st, int t) {  // K(t+1), V(t)
-        load_stage<D>(st, kp, vp, (t + 1) * kBN, t * kBN, Tk, off);
+        if constexpr (PAGED) load_stage_paged<D>(st, pk, (t + 1) * kBN, t * kBN, off);
+        else load_stage<D>(st, kp, vp, (t + 1) * kBN, t * kBN, Tk, off);
     };
     auto store_pair = [&](const Stage& st, int t) {
         if (t < n_tiles)
@@ -239,7 +292,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                            tid, t + 1 < n_tiles, true);
     };
     if (n_tiles > 0) {
-        load_stage<D>(st0, kp, vp, 0, 0, Tk, off);
+        if constexpr (PAGED) load_stage_paged<D>(st0, pk, 0, 0, off);
+        else load_stage<D>(st0, kp, vp, 0, 0, Tk, off);
         store_stage<D>(st0, smem, smem, tid, true, false);
     }
     __builtin_amdgcn_s_waitcnt(0);  // Q and the first K tile have landed
@@ -395,12 +449,33 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
     auto go = [&](auto kern) {
         kern<<<grid, kThreads, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k,
                                             (const uint16_t*)v, (uint16_t*)o, lse, BH, Hq, Hkv,
-                                            Tq, Tk, n_qtiles, sl2);
+                                            Tq, Tk, n_qtiles, sl2, nullptr, nullptr, 0);
     };
     if (D == 64)
-        causal ? go(prefill_bf16_kernel<64, true>) : go(prefill_bf16_kernel<64, false>);
+        causal ? go(prefill_bf16_kernel<64, true, false>) : go(prefill_bf16_kernel<64, false, false>);
     else
-        causal ? go(prefill_bf16_kernel<128, true>) : go(prefill_bf16_kernel<128, false>);
+        causal ? go(prefill_bf16_kernel<128, true, false>) : go(prefill_bf16_kernel<128, false, false>);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_paged_bf16(const void* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* block_table, const int32_t* kv_lens,
+                                     void* o, float* lse, int B, int Hq, int Hkv, int Tq, int D,
+                                     int bt_stride, bool causal, float scale, hipStream_t stream) {
+    const int BH = B * Hq;
+    const int n_qtiles = (Tq + kBM - 1) / kBM;
+    const dim3 grid(BH * n_qtiles);
+    const float sl2 = scale * kLog2e;
+    auto go = [&](auto kern) {
+        kern<<<grid, kThreads, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k_pages,
+                                            (const uint16_t*)v_pages, (uint16_t*)o, lse, BH, Hq,
+                                            Hkv, Tq, 0, n_qtiles, sl2, block_table, kv_lens,
+                                            bt_stride);
+    };
+    if (D == 64)
+        causal ? go(prefill_bf16_kernel<64, true, true>) : go(prefill_bf16_kernel<64, false, true>);
+    else
+        causal ? go(prefill_bf16_kernel<128, true, true>) : go(prefill_bf16_kernel<128, false, true>);
     return hipGetLastError();
 }
 

@@ -9,9 +9,12 @@ is its throughput in algorithmic TFLOP/s: 4*D flop per attended
 (query, key) pair, T(T+1)/2 pairs per (b, h) under the causal mask.
 
 The paged-decode workloads (MHA B32, GQA 32/8 B128, the same two over an
-FP8 E4M3 cache, shared-prefix cascade) are timed in the same run and reported
-under "decode" in KV GB/s: unique K+V bytes read (one byte per element for
-FP8), the shared prefix counted once.
+FP8 E4M3 cache, shared-prefix cascade over bf16 and FP8 caches) are timed in
+the same run and reported under "decode" in KV GB/s: unique K+V bytes read
+(one byte per element for FP8), the shared prefix counted once; "decode"
+also holds 8-layer decode steps launched eagerly and replayed as a HIP
+graph.  Chunked prefill against the paged cache is reported under
+"prefill_paged" in algorithmic TFLOP/s.
 
 Timing: W untimed warm-up steps, then K steps bracketed by a device
 synchronisation on both sides; HIP events on the launch stream give each
@@ -139,9 +142,39 @@ def bench_prefill(steps, warmup):
         tflops=flops / (span / steps * 1e-3) / 1e12, flops=flops, wall_s=wall,
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                      traffic=traffic, kernel="prefill_bf16_kernel<128,true>",
+                      traffic=traffic, kernel="prefill_bf16_kernel<128,true,false>",
                       algorithmic_bytes=int(4 * B * H * T * D * 2 + B * H * T * 4),
                       source_digest=digest))
+
+
+def bench_prefill_paged(steps, warmup):
+    """Chunked prefill: a 512-token chunk per sequence against its paged
+    cache (B4 Hq32 Hkv8 D128 bf16, kv_len U[2048, 8192], causal with the
+    diagonal at kv_len - 512); three input sets rotate.  Algorithmic flops:
+    4 D per visible (query, key) pair."""
+    B, Hq, Hkv, Tq, D = 4, 32, 8, 512, 128
+    sets, flops = [], []
+    for s in range(3):
+        d = wl.paged_prefill_inputs(B, Hq, Hkv, Tq, D, "bf16", 1009 + 100 * s,
+                                    length_range=(2048, 8192))
+        sets.append((dev(d["q"]), dev(d["k_pages"]), dev(d["v_pages"]), dev(d["block_table"]),
+                     dev(d["kv_lens"]), d["scale"]))
+        L = d["kv_lens"].astype(np.float64)
+        flops.append(4.0 * D * Hq * float(np.sum(Tq * (L - Tq) + Tq * (Tq + 1) / 2)))
+    o = torch.empty((B, Hq, Tq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, Tq), device="cuda")
+
+    def step(i):
+        q, kp, vp, bt, kl, scale = sets[i % 3]
+        attn.attn_prefill_paged(q, kp, vp, bt, kl, o, lse, causal=True, scale=scale)
+
+    durs, span, _ = time_launches(step, steps, warmup)
+    mean_flops = float(np.mean([flops[i % 3] for i in range(steps)]))
+    mean_ms = span / steps
+    return dict(workload="chunked prefill B4 Hq32 Hkv8 D128 bf16, 512-token chunk against a "
+                         "paged cache, kv_len U[2048,8192], causal (bottom-right), page 16",
+                mean_ms=mean_ms, tflops=round(mean_flops / (mean_ms * 1e-3) / 1e12, 2),
+                frac_mfma=round(mean_flops / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
 
 
 def kv_bytes(lengths, hkv, d, elem=2):
@@ -354,7 +387,12 @@ def main():
     pre = bench_prefill(args.steps, args.warmup)
     log(f"  {pre['tflops']:.1f} TFLOP/s, mean launch {pre['mean_launch_ms'] * 1e3:.1f} us")
     decode = {}
+    paged_prefill = None
     if not args.prefill_only:
+        log("chunked prefill against the paged cache ...")
+        paged_prefill = bench_prefill_paged(args.steps, args.warmup)
+        log(f"  {paged_prefill['tflops']:.1f} TFLOP/s")
+        torch.cuda.empty_cache()
         for n in (3, 4):
             log(f"decode workload {n} ...")
             decode[f"workload{n}"] = bench_decode(n, args.steps, args.warmup)
@@ -403,6 +441,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                        for kk, vv in v.items()} for k, v in decode.items()},
+        "prefill_paged": paged_prefill,
     }
     print(json.dumps(line), flush=True)
 

@@ -91,6 +91,42 @@ int attn_prefill(const void *q, const void *k, const void *v, void *o, float *ls
                  int head_dim, int dtype, int causal, float scale, void *stream);
 
 /*
+ * attn_prefill_paged -- prefill of a chunk of new tokens against a paged KV
+ * cache (chunked prefill).
+ *
+ * The tiled fused kernel of attn_prefill with its keys and values read
+ * through a block table, the two used together as the xhh.club summary
+ * ("fast attention kernels and operator fusion", section "FlashAttention and
+ * paged attention") describes.  Sequence b holds kv_lens[b] tokens in the
+ * cache, the chunk's own tokens included (their K/V are written before the
+ * call); the seq_q queries of the chunk are its last seq_q positions, so
+ * query i sits at position kv_lens[b] - seq_q + i.
+ *
+ *   q, o        : [batch, heads_q, seq_q, head_dim] bf16 (dtype ATTN_BF16)
+ *   k_pages,
+ *   v_pages     : [num_pages, heads_kv, page_size, head_dim] bf16
+ *   block_table : int32 [batch, max_pages_per_seq] (device)
+ *   kv_lens     : int32 [batch] (device)
+ *   lse         : [batch, heads_q, seq_q] fp32, or NULL
+ *   causal != 0 masks key j for query i when j > i + kv_lens[b] - seq_q;
+ *            a query with no visible key (kv_lens[b] < seq_q) gets O = 0 and
+ *            lse = -inf.
+ *
+ * Device-side preconditions (not checked): 0 <= kv_lens[b] <=
+ * page_size * max_pages_per_seq; block_table[b][p] a valid page for
+ * p < ceil(kv_lens[b] / page_size).  Entries past that are never read, and
+ * slots past kv_lens[b] in the last page are never read.
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_UNSUPPORTED (dtype other than
+ * bf16, head_dim not 64/128, page_size != 16), ATTN_E_ARG (scale,
+ * alignment), ATTN_E_HIP.
+ */
+int attn_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
+                       const int32_t *block_table, const int32_t *kv_lens, void *o, float *lse,
+                       int batch, int heads_q, int heads_kv, int seq_q, int head_dim,
+                       int page_size, int max_pages_per_seq, int dtype, int causal, float scale,
+                       void *stream);
+
+/*
  * Split-KV planning for paged decode.
  *
  * FlashDecoding splits the key/value length into independent partial

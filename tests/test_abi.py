@@ -209,6 +209,30 @@ def test_misaligned_pointers(lib):
                                          16, 0, 0, 0.1, None, 0, None) == E_ARG
 
 
+def test_prefill_paged_checks(lib):
+    # every case here is rejected on the host, before anything is launched
+    f = lambda **kw: lib.attn_prefill_paged(
+        kw.get("q", FAKE), kw.get("k", FAKE), FAKE, kw.get("bt", FAKE), kw.get("kl", FAKE),
+        kw.get("o", FAKE), kw.get("lse", None), kw.get("B", 2), kw.get("Hq", 8),
+        kw.get("Hkv", 2), kw.get("Tq", 64), kw.get("D", 128), kw.get("page", 16),
+        kw.get("maxp", 8), kw.get("dt", 0), kw.get("causal", 1), kw.get("scale", 0.1), None)
+    assert f(q=None) == E_NULL
+    assert f(bt=None) == E_NULL
+    assert f(kl=None) == E_NULL
+    assert f(Hq=6, Hkv=4) == E_SHAPE
+    assert f(Tq=-1) == E_SHAPE
+    assert f(maxp=-1) == E_SHAPE
+    assert f(dt=1) == E_UNSUP          # bf16 only
+    assert f(dt=2) == E_UNSUP
+    assert f(page=32) == E_UNSUP
+    assert f(D=96) == E_UNSUP
+    assert f(scale=0.0) == E_ARG
+    assert f(k=ctypes.c_void_p(0x1008)) == E_ARG
+    assert f(kl=ctypes.c_void_p(0x1002)) == E_ARG
+    assert f(B=0, q=None) == OK
+    assert f(Tq=0, q=None) == OK
+
+
 def test_decode_plan(lib):
     # workload shapes: long contexts over many sequences get 1024-token chunks
     assert attn.attn_decode_plan(32, 32, 8192) == (1024, 8)

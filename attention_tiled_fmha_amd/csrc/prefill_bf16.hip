@@ -209,12 +209,19 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int grp = wave >> 2;
     const int rb = 2 * (wave & 3) + grp;
 
-    // Heaviest query tiles first; bh = id % BH keeps one (b, h) on one XCD
-    // when BH is a multiple of 8 (workgroups are dealt to XCDs round-robin).
+    // Heaviest query tiles first.  Workgroups are dealt to the 8 XCDs
+    // round-robin, so id % 8 picks the XCD: with slot = id % BH, the kv group
+    // kg = slot % (B * Hkv) and the head within the group g = slot / (B * Hkv),
+    // every query tile of every head that reads one kv head's K/V lands on
+    // one XCD (and its L2) when BH and B * Hkv are multiples of 8.  Without
+    // grouped heads this is the identity, slot = b * Hq + h.
     const int id = blockIdx.x;
-    const int bh = id % BH;
+    const int slot = id % BH;
     const int qt = n_qtiles - 1 - id / BH;
-    const int b = bh / Hq, h = bh % Hq, kvh = h / (Hq / Hkv);
+    const int KG = (BH / Hq) * Hkv;      // (batch, kv head) groups
+    const int kg = slot % KG, g_in = slot / KG;
+    const int b = kg / Hkv, kvh = kg % Hkv, h = kvh * (Hq / Hkv) + g_in;
+    const int bh = b * Hq + h;
     const int q0 = qt * kBM;
     const int qw0 = q0 + rb * 32;        // this wavefront's first row
     const int qrow = qw0 + li;           // the query row of this lane

@@ -1,5 +1,10 @@
 """Replay of captured decode steps (HIP graphs) against eager launches.
 
+Graph replay as the xhh.club summary ("fast attention kernels and operator
+fusion", section on torch.compile and CUDA Graphs) describes it: a recorded
+sequence of GPU work resubmitted with one CPU call, for repeated small decode
+steps, valid while addresses and shapes stay fixed.
+
 Every call of the library is asynchronous on the caller's stream, allocates
 nothing when the caller passes the workspace, never synchronises and issues
 no memset; the split plan is made on the host from the host-side bound

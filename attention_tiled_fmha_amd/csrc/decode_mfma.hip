@@ -37,7 +37,11 @@
 // (chunk, kv head, sequence) items chunk-major.  The grid over the longest
 // sequence holds many empty chunks (a batch of mixed lengths); as separate
 // workgroups each of them cost a launch and a cold length load, here a few
-// scalar instructions.
+// scalar instructions.  With chunks of at most 512 tokens an item holds two
+// consecutive chunks of one (sequence, kv head): the first chunk's state is
+// merged and written while the second chunk's first pages are in flight,
+// which saves one pipeline start per two chunks (measured 2-3% on 512-token
+// chunks of bf16, 4-5% of FP8); each chunk still gets its own partial state.
 #include "common.h"
 #include "kernels.h"
 
@@ -93,6 +97,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Chunks per work item: two consecutive chunks of one (sequence, kv head)
+// share an item when each chunk's pages split evenly over the wavefronts'
+// unit pairs and both fit one 64-entry table window; the page pipeline then
+// runs on across the chunk boundary.  The unified-max path keeps one.
+__host__ __device__ inline int chunks_per_item(const DecodeArgs& a, bool fp8) {
+    const int unit = fp8 ? 2 : 1;   // pages per unit
+    return (!a.unified && a.split_tokens <= 32 * kPage && a.split_tokens % (8 * kPage * unit) == 0) ? 2 : 1;
+}
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int EB = FP8 ? 1 : 2;   // bytes per cached element
@@ -107,14 +120,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ float s_x[4][kMaxG];     // unified max: largest raw score per row
     __shared__ float s_o[4][kMaxG][D];
     const float phi_l2 = a.phi * kLog2e;
-    auto item = [&](const int c, const int kvh, const int b) {
+    const int cpi = chunks_per_item(a, FP8);
+    auto item = [&](const int ci, const int kvh, const int b) {
         // lengths past the host bound are clamped, so no index leaves the planned
         // split range or the block-table row
         const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
         const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
 
         if (L <= 0) {  // nothing to attend: O = 0, lse = -inf
-            if (c == 0 && wave == 0) {
+            if (ci == 0 && wave == 0) {
                 for (int g = 0; g < G; g++) {
                     const size_t row = (size_t)b * a.Hq + kvh * G + g;
                     for (int d = lane; d < D; d += kWave) {
@@ -126,10 +140,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             }
             return;
         }
+        const int c = ci * cpi;                   // the item's first chunk
         if (c >= nsplit) return;
+        const int ncs = min(cpi, nsplit - c);     // its chunks (the first of two is full)
 
         const int tok0 = c * a.split_tokens;
-        const int tok1 = min(L, tok0 + a.split_tokens);
+        const int tok1 = min(L, tok0 + ncs * a.split_tokens);
         const int pg0 = tok0 / kPage, pg1 = (tok1 + kPage - 1) / kPage;
         const int npg = pg1 - pg0;
         const int32_t* table = a.block_table + (size_t)b * a.bt_stride;
@@ -151,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             }
         }
 
-        // the chunk's block-table entries (at most 64 pages): entry pg0 + lane,
+        // the item's block-table entries (at most 64 pages): entry pg0 + lane,
         // picked with v_readlane
         const int tblv = lane < npg ? table[pg0 + lane] : 0;
         auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(tblv, j); };
@@ -187,6 +203,37 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                     for (int cc = 0; cc < D / 32; cc++)
                         pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D * 2 + 64 * cc, 0, 0);
             }
+        };
+
+        // merge the four wavefronts' published states and write chunk cc's
+        // result (straight to the output when the sequence is one chunk)
+        auto finish = [&](int cc) {
+            for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+                const int g = idx / D, d = idx % D;
+                float M = -INFINITY;
+                for (int w = 0; w < 4; w++) M = fmaxf(M, s_m[w][g]);
+                float lt = 0.f, ot = 0.f;
+                if (M != -INFINITY) {
+                    for (int w = 0; w < 4; w++) {
+                        const float wt = (s_m[w][g] == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
+                        lt = fmaf(wt, s_l[w][g], lt);
+                        ot = fmaf(wt, s_o[w][g][d], ot);
+                    }
+                }
+                const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+                const float ov = ot * inv;
+                const float lse = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
+                const size_t row = (size_t)b * a.Hq + kvh * G + g;
+                if (nsplit == 1) {
+                    if (a.out_f32) ((float*)a.o)[row * D + d] = ov;
+                    else ((uint16_t*)a.o)[row * D + d] = f32_to_bf16(ov);
+                    if (a.lse && d == 0) a.lse[row] = lse;
+                } else {
+                    a.ws_o[(row * a.max_splits + cc) * D + d] = ov;
+                    if (d == 0) a.ws_lse[row * a.max_splits + cc] = lse;
+                }
+            }
+            __syncthreads();   // s_o is rewritten next
         };
 
         float m_run = -INFINITY, l_run = 0.f, smax = -INFINITY;
@@ -307,37 +354,59 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     #pragma unroll
                 for (int i = 0; i < PU; i++) compute(u.p[i], PU * j + i);
             };
+            // publish this wavefront's state to LDS, then a workgroup barrier
+            auto publish = [&]() {
+                l_run = sum_xor32(sum_xor16(l_run));   // tokens of the four lane groups
+                if (!exact) smax = max_xor32(max_xor16(smax));
+                if (grp == 0) {
+                    s_m[wave][col] = m_run;
+                    s_l[wave][col] = l_run;
+                    s_x[wave][col] = smax;
+                }
+    #pragma unroll
+                for (int i = 0; i < NB; i++)
+    #pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2 (bf16),
+                        // 64(i/4) + 4(4grp + r) + i%4 (FP8)
+                        const int dim = FP8 ? 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3)
+                                            : 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
+                        s_o[wave][col][dim] = oacc[i][r];
+                    }
+                __syncthreads();
+            };
             const int nunits = (npg + PU - 1) / PU;
             const int nj = nunits > wave ? (nunits - wave + 3) / 4 : 0;
             Unit ba, bb;
             load_u(ba, wave);
-            for (int n = 0; n < nj; n += 2) {
+            int n = 0;
+            if (ncs == 2) {
+                // the first chunk is full and gives every wavefront the same,
+                // even number of units; its state is merged and written while
+                // the second chunk's first loads are in flight
+                const int nb = a.split_tokens / (kPage * PU * 4);
+                for (; n < nb; n += 2) {
+                    load_u(bb, wave + 4 * (n + 1));
+                    compute_u(ba, wave + 4 * n);
+                    load_u(ba, wave + 4 * (n + 2));
+                    compute_u(bb, wave + 4 * (n + 1));
+                }
+                publish();
+                finish(c);
+                m_run = exact ? -INFINITY : phi_l2;
+                l_run = 0.f;
+                smax = -INFINITY;
+    #pragma unroll
+                for (int i = 0; i < NB; i++) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            for (; n < nj; n += 2) {
                 load_u(bb, wave + 4 * (n + 1));
                 compute_u(ba, wave + 4 * n);
                 if (n + 1 >= nj) break;
                 load_u(ba, wave + 4 * (n + 2));
                 compute_u(bb, wave + 4 * (n + 1));
             }
-            l_run = sum_xor32(sum_xor16(l_run));   // tokens of the four lane groups
-            if (!exact) smax = max_xor32(max_xor16(smax));
-
-            // publish this wavefront's state
-            if (grp == 0) {
-                s_m[wave][col] = m_run;
-                s_l[wave][col] = l_run;
-                s_x[wave][col] = smax;
-            }
-    #pragma unroll
-            for (int i = 0; i < NB; i++)
-    #pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2 (bf16),
-                    // 64(i/4) + 4(4grp + r) + i%4 (FP8)
-                    const int dim = FP8 ? 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3)
-                                        : 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
-                    s_o[wave][col][dim] = oacc[i][r];
-                }
-            __syncthreads();
+            publish();
         };
 
         if (a.unified) {
@@ -363,36 +432,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             pass(std::true_type{});
         }
 
-        for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-            const int g = idx / D, d = idx % D;
-            float M = -INFINITY;
-            for (int w = 0; w < 4; w++) M = fmaxf(M, s_m[w][g]);
-            float lt = 0.f, ot = 0.f;
-            if (M != -INFINITY) {
-                for (int w = 0; w < 4; w++) {
-                    const float wt = (s_m[w][g] == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
-                    lt = fmaf(wt, s_l[w][g], lt);
-                    ot = fmaf(wt, s_o[w][g][d], ot);
-                }
-            }
-            const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
-            const float ov = ot * inv;
-            const float lse = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
-            const size_t row = (size_t)b * a.Hq + kvh * G + g;
-            if (nsplit == 1) {
-                if (a.out_f32) ((float*)a.o)[row * D + d] = ov;
-                else ((uint16_t*)a.o)[row * D + d] = f32_to_bf16(ov);
-                if (a.lse && d == 0) a.lse[row] = lse;
-            } else {
-                a.ws_o[(row * a.max_splits + c) * D + d] = ov;
-                if (d == 0) a.ws_lse[row * a.max_splits + c] = lse;
-            }
-        }
-        __syncthreads();   // s_o is rewritten by the next item
+        finish(c + ncs - 1);
     };
     // persistent workgroups walk the (chunk, kv head, sequence) items; empty
     // chunks of short sequences cost a few scalar instructions
-    const long n_items = (long)a.max_splits * a.Hkv * a.B;
+    const long n_items = (long)((a.max_splits + cpi - 1) / cpi) * a.Hkv * a.B;
     for (long n = blockIdx.x; n < n_items; n += gridDim.x) {
         const int kvh = (int)(n % a.Hkv);
         const long r = n / a.Hkv;
@@ -408,7 +452,8 @@ bool decode_mfma_supported(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
-    const long n_items = (long)a.max_splits * a.Hkv * a.B;
+    const int cpi = chunks_per_item(a, a.in_fp8);
+    const long n_items = (long)((a.max_splits + cpi - 1) / cpi) * a.Hkv * a.B;
     const dim3 grid((unsigned)std::min<long>(n_items, 8192));
     if (a.in_fp8) {
         if (a.D == 64) decode_mfma_kernel<64, true><<<grid, 256, 0, stream>>>(a);

@@ -53,6 +53,8 @@ def load(path=_LIB_PATH):
     lib.oracle_prefill_paged.restype = ip
     lib.oracle_prefill_paged.argtypes = [vp, vp, vp, ip, vp, vp, dp, dp, ip, ip, ip, ip, ip,
                                          ip, ip, ctypes.c_long, ip, ctypes.c_double, ip]
+    lib.oracle_flat_gemm.restype = ip
+    lib.oracle_flat_gemm.argtypes = [vp, vp, ip, dp, ip, ip, ip, ip]
     lib.oracle_decode_paged_fp8.restype = ip
     cd = ctypes.c_double
     lib.oracle_decode_paged_fp8.argtypes = [vp, ip, vp, vp, cd, cd, vp, vp, dp, dp, ip, ip, ip,
@@ -187,6 +189,26 @@ def prefill_paged(q, k_pages, v_pages, block_table, kv_lens, causal, scale, thre
     if rc != 0:
         raise RuntimeError(f"oracle_prefill_paged failed ({rc})")
     return o, lse
+
+
+def flat_gemm(a, w, threads=None, lib=None):
+    """C = A W^T: a [m,k], w [n,k] (bf16 bits, fp32 or fp64).  Returns fp64 [m,n]."""
+    lib = lib or _get()
+    a = np.ascontiguousarray(a)
+    w = np.ascontiguousarray(w)
+    dt = _dtype_code(a)
+    if _dtype_code(w) != dt:
+        raise TypeError("a and w must share one element type")
+    m, k = a.shape
+    n, kw = w.shape
+    if kw != k:
+        raise ValueError("shape mismatch")
+    c = np.zeros((m, n), np.float64)
+    rc = lib.oracle_flat_gemm(_ptr(a), _ptr(w), dt, _dptr(c), m, n, k,
+                              threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_flat_gemm failed ({rc})")
+    return c
 
 
 def e4m3_value(byte, lib=None):

@@ -330,6 +330,30 @@ int oracle_prefill_paged(const void *q, const void *k_pages, const void *v_pages
 }
 
 /*
+ * Flat GEMM of the decode phase: C = A W^T with A [m][k] (the m tokens of a
+ * decode step, m small) and W [n][k] (a layer's weight, n x k as the
+ * FlashDecoding++ summary, section 5, writes the projections' shapes), so
+ * C[i][j] = sum_t A[i][t] * W[j][t], summed in t order in fp64.  Inputs in
+ * `dtype`, widened exactly; c is fp64 [m][n].
+ */
+int oracle_flat_gemm(const void *a, const void *w, int dtype, double *c,
+                     int m, int n, int k, int nthreads)
+{
+    if (m < 0 || n < 0 || k < 0)
+        return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+    for (long ij = 0; ij < (long)m * n; ij++) {
+        const int i = (int)(ij / n), j = (int)(ij % n);
+        double acc = 0.0;
+        for (int t = 0; t < k; t++)
+            acc += load_elem(a, dtype, (size_t)i * k + t) * load_elem(w, dtype, (size_t)j * k + t);
+        c[ij] = acc;
+    }
+    return 0;
+}
+
+/*
  * Paged decode over an FP8 cache: k_pages and v_pages are E4M3 bytes
  * [num_pages][Hkv][page_size][D], dequantised as k_scale * e4m3(byte) and
  * v_scale * e4m3(byte); q is in dtype q_dtype.  Everything else as

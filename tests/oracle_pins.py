@@ -586,6 +586,35 @@ def check_prefill_paged_placement_and_decode(lib):
     _close(l[:, :, 0], ld, 1e-15, "one-token chunk vs decode lse")
 
 
+# --- flat GEMM of the decode phase ----------------------------------------------
+
+def check_flat_gemm(lib):
+    """C = A W^T against a pure-Python triple loop (math.fsum) on tiny shapes,
+    a one-hot A that selects columns of W (fixes which operand is transposed
+    and the index order), and numpy's matmul of the widened values."""
+    r = _rng(53)
+    for (m, n, k) in ((1, 1, 1), (2, 3, 4), (3, 5, 2), (4, 2, 7)):
+        a = r.standard_normal((m, k))
+        w = r.standard_normal((n, k))
+        c = oracle.flat_gemm(a, w, lib=lib)
+        ref = [[math.fsum(a[i, t] * w[j, t] for t in range(k)) for j in range(n)] for i in range(m)]
+        _close(c, ref, 1e-14, f"flat gemm brute {(m, n, k)}")
+    m, n, k = 3, 6, 5
+    w = r.standard_normal((n, k))
+    a = np.zeros((m, k))
+    picks = [4, 0, 2]
+    for i, t in enumerate(picks):
+        a[i, t] = 1.0
+    c = oracle.flat_gemm(a, w, lib=lib)
+    assert np.array_equal(c, w[:, picks].T), "one-hot rows must select columns of W"
+    a = wl.normal(wl.generator(54), (16, 256), "bf16")
+    w = wl.normal(wl.generator(55), (48, 256), "bf16")
+    c = oracle.flat_gemm(a, w, lib=lib)
+    af = wl.bf16_to_f32(a).astype(np.float64)
+    wf = wl.bf16_to_f32(w).astype(np.float64)
+    _close(c, af @ wf.T, 1e-12, "flat gemm vs numpy matmul (bf16 inputs)")
+
+
 ALL_CHECKS = [
     check_hand_2x2, check_identical_keys, check_dominant_score,
     check_single_key_and_row0, check_scale_zero, check_brute_force, check_scipy,
@@ -594,4 +623,5 @@ ALL_CHECKS = [
     check_lse_dropped_page, check_tail_garbage, check_bf16_widening, check_unified_fallback,
     check_e4m3_values, check_decode_fp8, check_prefill_paged_brute,
     check_prefill_paged_identical_keys, check_prefill_paged_placement_and_decode,
+    check_flat_gemm,
 ]

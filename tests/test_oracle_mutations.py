@@ -57,6 +57,12 @@ MUTATIONS = {
     "paged prefill gathers the wrong kv head": (
         "const int b = (int)(bh / Hq), h = (int)(bh % Hq), kvh = h / group;\n        const int L = kv_lens[b];",
         "const int b = (int)(bh / Hq), h = (int)(bh % Hq), kvh = h % Hkv;\n        const int L = kv_lens[b];"),
+    "flat gemm W read transposed": ("load_elem(w, dtype, (size_t)j * k + t)",
+                                    "load_elem(w, dtype, (size_t)t * n + j)"),
+    "flat gemm last k dropped": ("for (int t = 0; t < k; t++)\n            acc += load_elem(a",
+                                 "for (int t = 0; t < k - 1; t++)\n            acc += load_elem(a"),
+    "flat gemm rows of A swapped with columns": ("const int i = (int)(ij / n), j = (int)(ij % n);",
+                                                 "const int j = (int)(ij / m), i = (int)(ij % m);"),
     "fp8 scales swapped": ("V[(size_t)t * D + c] = v_scale * oracle_e4m3_value",
                            "V[(size_t)t * D + c] = k_scale * oracle_e4m3_value"),
 }

@@ -39,6 +39,9 @@ SIGNATURES = {
                                _i, _i, _f, _vp]),
     "attn_decode_shared_prefix_fp8": (_i, [_vp, _vp, _vp, _f, _f, _vp, _i, _vp, _vp, _i, _i, _i,
                                            _i, _i, _i, _f, _vp, _sz, _vp]),
+    "attn_flat_gemm_plan": (_i, [_i, _i, _i, _i, _vp, _ip, _ip]),
+    "attn_flat_gemm_workspace_bytes": (_sz, [_i, _i, _i, _vp]),
+    "attn_flat_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
 }
 
 
@@ -336,3 +339,46 @@ def attn_decode_shared_prefix_fp8(q, k_pages, v_pages, k_scale, v_scale, prefix_
         _p(q), _p(k_pages), _p(v_pages), float(k_scale), float(v_scale), _p(prefix_pages),
         int(prefix_len), _p(o), _p(lse), B, Hq, Hkv, D, page, _dtype(o), float(scale),
         _p(workspace), ws_bytes, _stream(stream)), "attn_decode_shared_prefix_fp8")
+
+
+class FlatGemmOpts(ctypes.Structure):
+    _fields_ = [("splits", ctypes.c_int), ("rows_per_workgroup", ctypes.c_int),
+                ("reserved", ctypes.c_int * 6)]
+
+
+def _fg_opts(splits, rows):
+    return ctypes.byref(FlatGemmOpts(int(splits), int(rows)))
+
+
+def attn_flat_gemm_plan(m, n, k, num_cus=0, splits=0, rows_per_workgroup=0):
+    """Host-only: (k slices, rows of W per workgroup) the planner picks for
+    C = A W^T."""
+    s, r = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().attn_flat_gemm_plan(m, n, k, num_cus, _fg_opts(splits, rows_per_workgroup),
+                                      ctypes.byref(s), ctypes.byref(r)), "attn_flat_gemm_plan")
+    return s.value, r.value
+
+
+def attn_flat_gemm_workspace_bytes(m, n, k, splits=0, rows_per_workgroup=0):
+    return load().attn_flat_gemm_workspace_bytes(m, n, k, _fg_opts(splits, rows_per_workgroup))
+
+
+def attn_flat_gemm(a, w, c, splits=0, rows_per_workgroup=0, workspace=None, stream=None):
+    """C = A W^T: a bf16 [m, k], w bf16 [n, k], c bf16 or fp32 [m, n]."""
+    for t, nm in ((a, "a"), (w, "w"), (c, "c")):
+        _dense(t, nm)
+    if a.dim() != 2 or w.dim() != 2 or c.dim() != 2:
+        raise ValueError("a, w, c must be 2-D")
+    m, k = a.shape
+    n, kw = w.shape
+    if kw != k or tuple(c.shape) != (m, n):
+        raise ValueError("shape mismatch")
+    if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("a and w must be bf16")
+    need = attn_flat_gemm_workspace_bytes(m, n, k, splits, rows_per_workgroup)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().attn_flat_gemm(_p(a), _p(w), _p(c), m, n, k, BF16, _dtype(c), _p(workspace),
+                                 ws_bytes, _stream(stream), _fg_opts(splits, rows_per_workgroup)),
+           "attn_flat_gemm")

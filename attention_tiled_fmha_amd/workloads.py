@@ -342,3 +342,26 @@ def workload(n, seed=None):
     if n == 5:
         return cascade_inputs(64, 32, 128, "bf16", seed)
     raise ValueError(f"no workload {n}")
+
+
+# ---------------------------------------------------------------------------
+# flat GEMM of the decode phase
+# ---------------------------------------------------------------------------
+
+# Weight shapes [n, k] of the four projections of one Llama2-7B layer
+# (hidden size 4096, FFN size 11008): fused K/Q/V, O, fused gate + up, down.
+LLAMA2_7B_PROJECTIONS = {
+    "qkv": (12288, 4096),
+    "o": (4096, 4096),
+    "gate_up": (22016, 4096),
+    "down": (4096, 11008),
+}
+
+
+def flat_gemm_inputs(m, n, k, seed):
+    """A [m, k] (the m tokens of one decode step) and W [n, k] (a projection's
+    weight), bf16 i.i.d. N(0,1); drawn in that order."""
+    gen = generator(seed)
+    a = normal(gen, (m, k), "bf16")
+    w = normal(gen, (n, k), "bf16")
+    return dict(a=a, w=w, m=m, n=n, k=k, seed=seed)

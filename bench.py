@@ -14,7 +14,9 @@ the same run and reported under "decode" in KV GB/s: unique K+V bytes read
 (one byte per element for FP8), the shared prefix counted once; "decode"
 also holds 8-layer decode steps launched eagerly and replayed as a HIP
 graph.  Chunked prefill against the paged cache is reported under
-"prefill_paged" in algorithmic TFLOP/s.
+"prefill_paged" in algorithmic TFLOP/s, and the flat GEMM of the decode
+projections (one Llama2-7B layer's four weights, m = 1, 16, 64 tokens) under
+"flat_gemm" in GB/s of weight + activation bytes.
 
 Timing: W untimed warm-up steps, then K steps bracketed by a device
 synchronisation on both sides; HIP events on the launch stream give each
@@ -332,6 +334,44 @@ def bench_graph_decode(steps, warmup, B, length_range, layers=8):
                 graph_gbs=round(nbytes / (graph_ms * 1e-3) / 1e9, 1))
 
 
+def bench_flat_gemm(steps, warmup, ms=(1, 16, 64)):
+    """Flat GEMM C = A W^T of the decode phase over the four projection
+    shapes of one Llama2-7B layer (bf16 A [m, k], W [n, k], bf16 C), for
+    m tokens per step.  Each shape rotates through enough device copies of W
+    (>= 768 MB) that the 256 MB last-level cache cannot hold them; launches
+    run back to back.  Bytes: W + A + C (W dominates)."""
+    out = {}
+    for m in ms:
+        res, tot_bytes, tot_ms = {}, 0, 0.0
+        for name, (n, k) in wl.LLAMA2_7B_PROJECTIONS.items():
+            d = wl.flat_gemm_inputs(m, n, k, 1200 + m)
+            a = dev(d["a"])
+            w0 = dev(d["w"])
+            copies = max(2, -(-(768 << 20) // (n * k * 2)))
+            ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+            c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+            def step(i):
+                attn.attn_flat_gemm(a, ws[i % copies], c)
+
+            durs, span, _ = time_launches(step, steps, warmup)
+            mean_ms = span / steps
+            nbytes = n * k * 2 + m * k * 2 + m * n * 2
+            res[name] = dict(n=n, k=k, us=round(mean_ms * 1e3, 2),
+                             gbs=round(nbytes / (mean_ms * 1e-3) / 1e9, 1),
+                             frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+            tot_bytes += nbytes
+            tot_ms += mean_ms
+            del ws, w0
+            torch.cuda.empty_cache()
+        res["layer"] = dict(us=round(tot_ms * 1e3, 2), gbs=round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
+                            frac_hbm=round(tot_bytes / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        out[f"m{m}"] = res
+    return dict(workload="flat GEMM C = A W^T, the four decode projections of one Llama2-7B "
+                         "layer (qkv 12288x4096, o 4096x4096, gate_up 22016x4096, "
+                         "down 4096x11008), bf16, m tokens", results=out)
+
+
 def cpu_baseline(target_s=15.0):
     """The fp64 oracle on (b, h) pairs of the prefill workload, timed on the
     host cores; throughput in the bench's unit (algorithmic causal TFLOP/s)."""
@@ -364,6 +404,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
+    ap.add_argument("--flat-gemm-only", action="store_true",
+                    help="time only the flat GEMM of the decode projections (prints its JSON)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write elementwise kernel, "
                          "the reference for scaling HBM byte counters")
@@ -383,11 +425,19 @@ def main():
         del src, dst
         log("copy calibration: 3 x (1 GiB read + 1 GiB write)")
 
+    if args.flat_gemm_only:
+        flat = bench_flat_gemm(args.steps, args.warmup)
+        for mk, r in flat["results"].items():
+            log(f"  {mk}: layer {r['layer']['us']:.1f} us, {r['layer']['gbs']:.0f} GB/s")
+        print(json.dumps(flat), flush=True)
+        return
+
     log("prefill B4 H32 T1024 D128 causal bf16 ...")
     pre = bench_prefill(args.steps, args.warmup)
     log(f"  {pre['tflops']:.1f} TFLOP/s, mean launch {pre['mean_launch_ms'] * 1e3:.1f} us")
     decode = {}
     paged_prefill = None
+    flat = None
     if not args.prefill_only:
         log("chunked prefill against the paged cache ...")
         paged_prefill = bench_prefill_paged(args.steps, args.warmup)
@@ -415,6 +465,10 @@ def main():
             log(f"8-layer decode step B{B}, eager vs graph replay ...")
             decode[key] = bench_graph_decode(args.steps, args.warmup, B, lr)
             log(f"  eager {decode[key]['eager_us']:.1f} us, graph {decode[key]['graph_us']:.1f} us")
+        log("flat GEMM, Llama2-7B decode projections ...")
+        flat = bench_flat_gemm(args.steps, args.warmup)
+        for mk, r in flat["results"].items():
+            log(f"  {mk}: layer {r['layer']['us']:.1f} us, {r['layer']['gbs']:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle) ...")
@@ -442,6 +496,7 @@ def main():
         "decode": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                        for kk, vv in v.items()} for k, v in decode.items()},
         "prefill_paged": paged_prefill,
+        "flat_gemm": flat,
     }
     print(json.dumps(line), flush=True)
 

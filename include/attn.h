@@ -343,6 +343,56 @@ int attn_decode_shared_prefix_fp8(const void *q, const void *k_pages, const void
                                   int page_size, int o_dtype, float scale,
                                   void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Flat GEMM of the decode phase: C = A W^T.
+ *
+ * In decode the projections around attention (K/Q/V, O, the two FFN layers)
+ * multiply the m tokens of one step (m = batch size, small) by a weight of n
+ * rows and k columns: a "flat" GEMM whose cost is reading the weight once.
+ * The FlashDecoding++ summary (wenjunhu.com/d/2311396.html, sections 1 and 4)
+ * pads such an m only to the matrix unit's smallest tile instead of 64 and
+ * hides memory latency with double buffering; its section 5 picks the kernel
+ * from m, n and k (writing each projection's weight as n x k).  Here m is
+ * padded to 16 on the bf16 matrix core and a larger m (prefill) is left to a
+ * conventional GEMM library.
+ *
+ *   a : [m, k] bf16 (dtype ATTN_BF16), row-major
+ *   w : [n, k] bf16, row-major (a linear layer's weight: C[i][j] = a_i . w_j)
+ *   c : [m, n] `c_dtype` (ATTN_BF16, rounded to nearest even, or ATTN_F32)
+ *   workspace : at least attn_flat_gemm_workspace_bytes(m, n, k, opts)
+ *               bytes (NULL allowed when that is 0): fp32 partials of the
+ *               k slices, added in slice order, so results do not depend on
+ *               the timing of the launch
+ *   opts : NULL = the planner's choices, or an attn_flat_gemm_opts
+ * Products are accumulated in fp32.  m, n or k may be 0 (k == 0 gives C = 0).
+ * Alignment: a, w and the workspace 16 bytes, c 4 bytes.
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE (negative sizes or options),
+ * ATTN_E_UNSUPPORTED (m > 64, k not a multiple of 8 or above 2^22, dtype
+ * other than bf16, c_dtype other than bf16 / fp32, rows_per_workgroup other
+ * than 0, 16, 64), ATTN_E_WORKSPACE,
+ * ATTN_E_ARG (alignment), ATTN_E_HIP.
+ *
+ * attn_flat_gemm_plan: host-only.  The planner's choice for this shape on
+ * num_cus compute units (<= 0: 256): rows of w per workgroup (16, or 64
+ * when m > 8, so that one A fragment serves four row blocks) and k slices
+ * across workgroups (at most 4, and only when the row blocks alone leave
+ * compute units idle or unevenly loaded).  Fields of opts that are > 0 override the choice; splits is
+ * clamped to the number of 32-wide k steps.
+ * attn_flat_gemm_workspace_bytes returns 0 for an unsupported shape.
+ */
+typedef struct {
+    int splits;               /* 0 = planner; > 0 forces that many k slices       */
+    int rows_per_workgroup;   /* 0 = planner; 16 or 64 forces it                  */
+    int reserved[6];
+} attn_flat_gemm_opts;
+
+int attn_flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts *opts,
+                        int *splits, int *rows_per_workgroup);
+size_t attn_flat_gemm_workspace_bytes(int m, int n, int k, const attn_flat_gemm_opts *opts);
+int attn_flat_gemm(const void *a, const void *w, void *c, int m, int n, int k, int dtype,
+                   int c_dtype, void *workspace, size_t workspace_bytes, void *stream,
+                   const attn_flat_gemm_opts *opts);
+
 #ifdef __cplusplus
 }
 #endif

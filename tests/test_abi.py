@@ -271,3 +271,67 @@ def test_shared_prefix_workspace(lib):
     assert n == -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert attn.attn_shared_prefix_workspace_bytes(64, 32, 32, 128, 0, 0) == 0
     assert attn.attn_shared_prefix_workspace_bytes(64, 32, 5, 128, 4096, 0) == 0  # bad group
+
+
+def flat_gemm(lib, ws=None, ws_bytes=0, splits=0, rows=0, **kw):
+    a = dict(a=FAKE, w=FAKE, c=FAKE, m=4, n=64, k=256, dt=0, cdt=0)
+    a.update(kw)
+    opts = ctypes.byref(attn.FlatGemmOpts(splits, rows))
+    return lib.attn_flat_gemm(a["a"], a["w"], a["c"], a["m"], a["n"], a["k"], a["dt"], a["cdt"],
+                              ws, ws_bytes, None, opts)
+
+
+def test_flat_gemm_checks(lib):
+    assert flat_gemm(lib, a=None) == E_NULL
+    assert flat_gemm(lib, w=None) == E_NULL
+    assert flat_gemm(lib, c=None) == E_NULL
+    assert flat_gemm(lib, m=-1) == E_SHAPE
+    assert flat_gemm(lib, n=-1) == E_SHAPE
+    assert flat_gemm(lib, k=-8) == E_SHAPE
+    assert flat_gemm(lib, splits=-1) == E_SHAPE
+    assert flat_gemm(lib, rows=-16) == E_SHAPE
+    assert flat_gemm(lib, rows=32) == E_UNSUP
+    assert flat_gemm(lib, m=65) == E_UNSUP          # prefill-size m: a conventional GEMM
+    assert flat_gemm(lib, k=100) == E_UNSUP         # k not a multiple of 8
+    assert flat_gemm(lib, k=(1 << 22) + 8) == E_UNSUP
+    assert flat_gemm(lib, dt=1) == E_UNSUP          # fp32 inputs
+    assert flat_gemm(lib, cdt=2) == E_UNSUP
+    assert flat_gemm(lib, a=ctypes.c_void_p(0x1008)) == E_ARG
+    assert flat_gemm(lib, c=ctypes.c_void_p(0x1002)) == E_ARG
+    # k slices need a workspace for their partials
+    assert flat_gemm(lib, splits=4) == E_WS
+    opts = ctypes.byref(attn.FlatGemmOpts(4, 0))
+    need = lib.attn_flat_gemm_workspace_bytes(4, 64, 256, opts)
+    assert need == -(-4 * 4 * 64 * 4 // 256) * 256
+    assert flat_gemm(lib, splits=4, ws=FAKE, ws_bytes=need - 1) == E_WS
+    # empty outputs are a no-op, even with NULL pointers
+    assert flat_gemm(lib, a=None, w=None, c=None, m=0) == OK
+    assert flat_gemm(lib, a=None, w=None, c=None, n=0) == OK
+
+
+def test_flat_gemm_plan(lib):
+    plan = attn.attn_flat_gemm_plan
+    # m <= 8: 16 rows per workgroup; the Llama2-7B decode projections have
+    # >= 256 row blocks of 16, so no k slices and no workspace
+    for n, k in ((12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008)):
+        for m in (1, 8):
+            assert plan(m, n, k) == (1, 16)
+            assert attn.attn_flat_gemm_workspace_bytes(m, n, k) == 0
+    # m > 8: 64 rows per workgroup, k sliced while the grid stays within 3
+    # workgroups per CU (at most 4 slices, two register batches per wavefront)
+    assert plan(16, 4096, 4096) == (4, 64)     # 64 row blocks
+    assert plan(16, 12288, 4096) == (4, 64)    # 192
+    assert plan(16, 22016, 4096) == (2, 64)    # 344
+    assert plan(64, 4096, 11008) == (4, 64)
+    assert plan(64, 4096, 512) == (1, 64)      # 16 steps: 2 slices would leave 1 per wavefront
+    assert attn.attn_flat_gemm_workspace_bytes(16, 4096, 4096) == 4 * 16 * 4096 * 4
+    # forced rows per workgroup: 16 rows, n = 256 (16 row blocks), k = 8192
+    # (256 steps), m = 16 (8 steps per batch): 4 slices of 64 steps
+    assert plan(16, 256, 8192, rows_per_workgroup=16) == (4, 16)
+    assert plan(16, 256, 8192, num_cus=16, rows_per_workgroup=16) == (1, 16)
+    # forced counts are clamped to the number of 32-wide k steps
+    assert plan(4, 64, 256, splits=100) == (8, 16)
+    assert plan(4, 64, 256, splits=3) == (3, 16)
+    assert plan(1, 1, 0) == (1, 16)
+    with pytest.raises(attn.AttnError):
+        plan(65, 64, 256)

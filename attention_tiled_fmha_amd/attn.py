@@ -343,11 +343,11 @@ def attn_decode_shared_prefix_fp8(q, k_pages, v_pages, k_scale, v_scale, prefix_
 
 class FlatGemmOpts(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int), ("rows_per_workgroup", ctypes.c_int),
-                ("reserved", ctypes.c_int * 6)]
+                ("waves_per_workgroup", ctypes.c_int), ("reserved", ctypes.c_int * 5)]
 
 
-def _fg_opts(splits, rows):
-    return ctypes.byref(FlatGemmOpts(int(splits), int(rows)))
+def _fg_opts(splits, rows, waves=0):
+    return ctypes.byref(FlatGemmOpts(int(splits), int(rows), int(waves)))
 
 
 def attn_flat_gemm_plan(m, n, k, num_cus=0, splits=0, rows_per_workgroup=0):
@@ -359,11 +359,13 @@ def attn_flat_gemm_plan(m, n, k, num_cus=0, splits=0, rows_per_workgroup=0):
     return s.value, r.value
 
 
-def attn_flat_gemm_workspace_bytes(m, n, k, splits=0, rows_per_workgroup=0):
-    return load().attn_flat_gemm_workspace_bytes(m, n, k, _fg_opts(splits, rows_per_workgroup))
+def attn_flat_gemm_workspace_bytes(m, n, k, splits=0, rows_per_workgroup=0, waves_per_workgroup=0):
+    return load().attn_flat_gemm_workspace_bytes(
+        m, n, k, _fg_opts(splits, rows_per_workgroup, waves_per_workgroup))
 
 
-def attn_flat_gemm(a, w, c, splits=0, rows_per_workgroup=0, workspace=None, stream=None):
+def attn_flat_gemm(a, w, c, splits=0, rows_per_workgroup=0, waves_per_workgroup=0,
+                   workspace=None, stream=None):
     """C = A W^T: a bf16 [m, k], w bf16 [n, k], c bf16 or fp32 [m, n]."""
     for t, nm in ((a, "a"), (w, "w"), (c, "c")):
         _dense(t, nm)
@@ -375,10 +377,11 @@ def attn_flat_gemm(a, w, c, splits=0, rows_per_workgroup=0, workspace=None, stre
         raise ValueError("shape mismatch")
     if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
         raise TypeError("a and w must be bf16")
-    need = attn_flat_gemm_workspace_bytes(m, n, k, splits, rows_per_workgroup)
+    need = attn_flat_gemm_workspace_bytes(m, n, k, splits, rows_per_workgroup, waves_per_workgroup)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().attn_flat_gemm(_p(a), _p(w), _p(c), m, n, k, BF16, _dtype(c), _p(workspace),
-                                 ws_bytes, _stream(stream), _fg_opts(splits, rows_per_workgroup)),
+                                 ws_bytes, _stream(stream),
+                                 _fg_opts(splits, rows_per_workgroup, waves_per_workgroup)),
            "attn_flat_gemm")

@@ -60,32 +60,44 @@ size_t decode_ws_bytes(int batch, int heads_q, int head_dim, int max_splits) {
 
 int check_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
 
-// Flat GEMM planning, from measurements of the four decode projections of a
-// Llama2-7B layer (n x k = 12288 x 4096, 4096 x 4096, 22016 x 4096,
-// 4096 x 11008) at m = 1 .. 64:
-//  - rows per workgroup: 16 for m <= 8 (one row block, all of k split over
-//    the workgroup's 8 wavefronts), else 64 (four row blocks share every A
-//    fragment, so A is re-read from L2 a quarter as often; at m = 64 this
-//    took the layer from 283 to ~175 us);
-//  - k slices across workgroups (fp32 partials plus a reduction launch):
-//    with 16 rows only while the row blocks leave compute units idle; with
-//    64 rows up to 4 slices while the grid stays within 3 workgroups per CU
-//    (2 and 4 slices beat 1 and 8 on every shape but one).  Every wavefront
-//    keeps at least one register batch of 32-wide k steps (two with 64
-//    rows).
+// Flat GEMM planning, from sweeps of (rows, wavefronts, k slices) over the
+// four decode projections of a Llama2-7B layer (n x k = 12288 x 4096,
+// 4096 x 4096, 22016 x 4096, 4096 x 11008) at m = 1, 8, 16, 64:
+//  - wavefronts per workgroup: 4 (more, smaller workgroups beat 8 on every
+//    shape but one, by up to 15%);
+//  - rows per workgroup: 16 for m <= 8, and for m <= 16 on weights of at
+//    most 2^24 elements; else 64 (four row blocks share every A fragment,
+//    so A is re-read from L2 a quarter as often: 283 -> ~170 us per layer
+//    at m = 64);
+//  - k slices across workgroups (fp32 partials plus a reduction launch of
+//    ~4 us): with 16 rows, doubled while the row blocks alone leave CUs
+//    idle, and 4 when the grid fills one to three rounds of resident
+//    workgroups (the last round's tail shrinks: gate_up at m = 1 33 us
+//    against 37); with 64 rows, none from 160 row blocks on (5/8 of the
+//    CUs), else up to 4.  Every wavefront keeps at least one register
+//    batch of 32-wide k steps (two with 64 rows).
 constexpr int kFgMaxM = 64;
 constexpr int kFgMaxK = 1 << 22;
-constexpr int kFgWaves = 8;
+constexpr int kFgWaves = 4;
+constexpr int kFgResident = 4;     // 4-wavefront workgroups resident per CU
 
 int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* o, int* splits,
-                   int* steps_per_split, int* row_blocks) {
+                   int* steps_per_split, int* row_blocks, int* waves) {
     if (m < 0 || n < 0 || k < 0) return ATTN_E_SHAPE;
-    if (o && (o->splits < 0 || o->rows_per_workgroup < 0)) return ATTN_E_SHAPE;
+    if (o && (o->splits < 0 || o->rows_per_workgroup < 0 || o->waves_per_workgroup < 0))
+        return ATTN_E_SHAPE;
     if (m > kFgMaxM || k > kFgMaxK || k % 8) return ATTN_E_UNSUPPORTED;
     if (o && o->rows_per_workgroup && o->rows_per_workgroup != 16 && o->rows_per_workgroup != 64)
         return ATTN_E_UNSUPPORTED;
+    if (o && o->waves_per_workgroup && o->waves_per_workgroup != 4 && o->waves_per_workgroup != 8)
+        return ATTN_E_UNSUPPORTED;
     if (num_cus <= 0) num_cus = kPlanCUs;
-    const int rb = (o && o->rows_per_workgroup) ? o->rows_per_workgroup / 16 : (m > 8 ? 4 : 1);
+    const int nw = (o && o->waves_per_workgroup) ? o->waves_per_workgroup : kFgWaves;
+    int rb;
+    if (o && o->rows_per_workgroup)
+        rb = o->rows_per_workgroup / 16;
+    else
+        rb = (m <= 8 || (m <= 16 && (long)n * k <= (1L << 24))) ? 1 : 4;
     const long rblocks = (n + 16L * rb - 1) / (16L * rb);
     const int nsteps = (k + 31) / 32;
     const int U = attn::flat_gemm_batch_steps(std::max(m, 1), rb);
@@ -93,16 +105,20 @@ int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* 
     if (o && o->splits > 0) {
         s = o->splits;
     } else if (rb == 1) {
-        while (rblocks * s < num_cus && nsteps / (2L * s * kFgWaves) >= U) s *= 2;
-    } else {
-        while (s < 4 && rblocks * 2 * s <= 3L * num_cus && nsteps / (2L * s * kFgWaves) >= 2 * U)
-            s *= 2;
+        while (rblocks * s < num_cus && nsteps / (2L * s * nw) >= U) s *= 2;
+        const long resident = (long)kFgResident * num_cus;
+        if (s == 1 && rblocks > resident && rblocks < 3 * resident && nsteps / (4L * nw) >= U)
+            s = 4;
+    } else if (rblocks * 8 < 5L * num_cus) {
+        s = 4;
+        while (s > 1 && nsteps / ((long)s * nw) < 2 * U) s /= 2;
     }
     s = std::max(1, std::min(s, std::max(nsteps, 1)));
     const int sps = std::max(1, (nsteps + s - 1) / s);
     *steps_per_split = sps;
     *splits = std::max(1, (nsteps + sps - 1) / sps);
     *row_blocks = rb;
+    *waves = nw;
     return ATTN_OK;
 }
 
@@ -447,15 +463,15 @@ int attn_decode_shared_prefix_fp8(const void* q, const void* k_pages, const void
 int attn_flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* opts,
                         int* splits, int* rows_per_workgroup) {
     if (!splits || !rows_per_workgroup) return ATTN_E_NULL;
-    int sps = 0, rb = 0;
-    const int rc = flat_gemm_plan(m, n, k, num_cus, opts, splits, &sps, &rb);
+    int sps = 0, rb = 0, nw = 0;
+    const int rc = flat_gemm_plan(m, n, k, num_cus, opts, splits, &sps, &rb, &nw);
     if (rc == ATTN_OK) *rows_per_workgroup = 16 * rb;
     return rc;
 }
 
 size_t attn_flat_gemm_workspace_bytes(int m, int n, int k, const attn_flat_gemm_opts* opts) {
-    int s = 0, sps = 0, rb = 0;
-    if (flat_gemm_plan(m, n, k, kPlanCUs, opts, &s, &sps, &rb) != ATTN_OK) return 0;
+    int s = 0, sps = 0, rb = 0, nw = 0;
+    if (flat_gemm_plan(m, n, k, kPlanCUs, opts, &s, &sps, &rb, &nw) != ATTN_OK) return 0;
     return flat_gemm_ws_bytes(m, n, s);
 }
 
@@ -463,8 +479,8 @@ int attn_flat_gemm(const void* a, const void* w, void* c, int m, int n, int k, i
                    int c_dtype, void* workspace, size_t workspace_bytes, void* stream,
                    const attn_flat_gemm_opts* opts) {
     if (dtype != ATTN_BF16 || !dtype_ok(c_dtype)) return ATTN_E_UNSUPPORTED;
-    int s = 0, sps = 0, rb = 0;
-    const int rc = flat_gemm_plan(m, n, k, kPlanCUs, opts, &s, &sps, &rb);
+    int s = 0, sps = 0, rb = 0, nw = 0;
+    const int rc = flat_gemm_plan(m, n, k, kPlanCUs, opts, &s, &sps, &rb, &nw);
     if (rc != ATTN_OK) return rc;
     if (m == 0 || n == 0) return ATTN_OK;
     if (!c || (k > 0 && (!a || !w))) return ATTN_E_NULL;
@@ -483,6 +499,7 @@ int attn_flat_gemm(const void* a, const void* w, void* c, int m, int n, int k, i
     p.splits = s;
     p.steps_per_split = sps;
     p.row_blocks = rb;
+    p.waves = nw;
     p.out_f32 = c_dtype == ATTN_F32;
     return check_hip(attn::launch_flat_gemm(p, (hipStream_t)stream));
 }

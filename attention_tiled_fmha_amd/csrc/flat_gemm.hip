@@ -18,13 +18,13 @@
 // is the operands' register order, so nothing is shuffled.  Four lanes read
 // 64 contiguous bytes of a row; the next step reads the next 64.
 //
-// A workgroup (8 wavefronts) owns 16 rows of W; its k range (all of k, or one
-// of `splits` slices when there are too few row blocks to fill the chip) is
-// cut into 8 contiguous per-wavefront ranges.  Each wavefront streams its
+// A workgroup (4 or 8 wavefronts) owns 16 or 64 rows of W; its k range (all
+// of k, or one of `splits` slices) is cut into contiguous per-wavefront
+// ranges.  Each wavefront streams its
 // range in batches of U steps with the next batch's loads in flight while the
 // current batch's MFMAs run: double buffering in registers, since every byte
 // of W is used once and staging it through LDS would only add traffic.  The
-// eight partial products are summed in fixed order through LDS.  With
+// wavefronts' partial products are summed in fixed order through LDS.  With
 // splits > 1 each slice writes fp32 partials to the workspace and
 // flat_gemm_reduce_kernel adds them in slice order.
 //
@@ -42,8 +42,6 @@ namespace attn {
 
 namespace {
 
-constexpr int kFgWaves = 8;
-constexpr int kFgThreads = kFgWaves * 64;
 constexpr int kRsrcWord3 = 0x00020000;     // raw 32-bit data, no swizzle
 constexpr int kOutOfRange = 0x7fffff00;    // an offset past every descriptor's size
 
@@ -54,11 +52,13 @@ struct Batch {
 };
 
 // RB 16-row blocks of W per workgroup (the same A fragments serve all of
-// them), MT token tiles, U k steps per register batch.
-template <int MT, int RB, int U, bool OUT_F32>
-__global__ __launch_bounds__(kFgThreads) void flat_gemm_kernel(
+// them), MT token tiles, U k steps per register batch, NW wavefronts.
+template <int MT, int RB, int U, int NW, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64) void flat_gemm_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ w, void* __restrict__ c,
     float* __restrict__ ws, int m, int n, int k, int splits, int steps_per_split) {
+    constexpr int kFgWaves = NW;
+    constexpr int kFgThreads = NW * 64;
     __shared__ __attribute__((aligned(16))) f32x4 red[kFgWaves][MT][64];
 
     const int tid = threadIdx.x;
@@ -177,11 +177,11 @@ template <int MT, int RB> struct BatchSteps {
     static constexpr int U = RB == 1 ? (MT == 1 ? 8 : MT == 2 ? 4 : 2) : (MT <= 2 ? 2 : 1);
 };
 
-template <int MT, int RB, bool OUT_F32>
-hipError_t go(const FlatGemmArgs& p, hipStream_t stream) {
+template <int MT, int RB, int NW, bool OUT_F32>
+hipError_t go_nw(const FlatGemmArgs& p, hipStream_t stream) {
     constexpr int U = BatchSteps<MT, RB>::U;
     const int rblocks = (p.n + 16 * RB - 1) / (16 * RB);
-    flat_gemm_kernel<MT, RB, U, OUT_F32><<<dim3(rblocks * p.splits), kFgThreads, 0, stream>>>(
+    flat_gemm_kernel<MT, RB, U, NW, OUT_F32><<<dim3(rblocks * p.splits), NW * 64, 0, stream>>>(
         (const uint16_t*)p.a, (const uint16_t*)p.w, p.c, p.ws, p.m, p.n, p.k, p.splits,
         p.steps_per_split);
     if (p.splits > 1) {
@@ -190,6 +190,12 @@ hipError_t go(const FlatGemmArgs& p, hipStream_t stream) {
         flat_gemm_reduce_kernel<OUT_F32><<<blocks, 256, 0, stream>>>(p.ws, p.c, mn, p.splits);
     }
     return hipGetLastError();
+}
+
+template <int MT, int RB, bool OUT_F32>
+hipError_t go(const FlatGemmArgs& p, hipStream_t stream) {
+    if (p.waves == 8) return go_nw<MT, RB, 8, OUT_F32>(p, stream);
+    return go_nw<MT, RB, 4, OUT_F32>(p, stream);
 }
 
 template <int RB, bool OUT_F32>

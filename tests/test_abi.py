@@ -291,6 +291,8 @@ def test_flat_gemm_checks(lib):
     assert flat_gemm(lib, splits=-1) == E_SHAPE
     assert flat_gemm(lib, rows=-16) == E_SHAPE
     assert flat_gemm(lib, rows=32) == E_UNSUP
+    opts16 = ctypes.byref(attn.FlatGemmOpts(0, 0, 16))
+    assert lib.attn_flat_gemm(FAKE, FAKE, FAKE, 4, 64, 256, 0, 0, None, 0, None, opts16) == E_UNSUP
     assert flat_gemm(lib, m=65) == E_UNSUP          # prefill-size m: a conventional GEMM
     assert flat_gemm(lib, k=100) == E_UNSUP         # k not a multiple of 8
     assert flat_gemm(lib, k=(1 << 22) + 8) == E_UNSUP
@@ -311,24 +313,24 @@ def test_flat_gemm_checks(lib):
 
 def test_flat_gemm_plan(lib):
     plan = attn.attn_flat_gemm_plan
-    # m <= 8: 16 rows per workgroup; the Llama2-7B decode projections have
-    # >= 256 row blocks of 16, so no k slices and no workspace
-    for n, k in ((12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008)):
-        for m in (1, 8):
-            assert plan(m, n, k) == (1, 16)
-            assert attn.attn_flat_gemm_workspace_bytes(m, n, k) == 0
-    # m > 8: 64 rows per workgroup, k sliced while the grid stays within 3
-    # workgroups per CU (at most 4 slices, two register batches per wavefront)
-    assert plan(16, 4096, 4096) == (4, 64)     # 64 row blocks
-    assert plan(16, 12288, 4096) == (4, 64)    # 192
-    assert plan(16, 22016, 4096) == (2, 64)    # 344
-    assert plan(64, 4096, 11008) == (4, 64)
-    assert plan(64, 4096, 512) == (1, 64)      # 16 steps: 2 slices would leave 1 per wavefront
-    assert attn.attn_flat_gemm_workspace_bytes(16, 4096, 4096) == 4 * 16 * 4096 * 4
-    # forced rows per workgroup: 16 rows, n = 256 (16 row blocks), k = 8192
-    # (256 steps), m = 16 (8 steps per batch): 4 slices of 64 steps
-    assert plan(16, 256, 8192, rows_per_workgroup=16) == (4, 16)
+    proj = ((12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008))   # qkv, o, gate_up, down
+    # m <= 8: 16 rows per workgroup.  qkv, o and down have 256..768 row
+    # blocks: one round of resident 4-wavefront workgroups, no k slices and
+    # no workspace; gate_up's 1376 fill 1.3 rounds, so k is sliced 4 ways
+    for m in (1, 8):
+        assert [plan(m, n, k) for n, k in proj] == [(1, 16), (1, 16), (4, 16), (1, 16)]
+        assert attn.attn_flat_gemm_workspace_bytes(m, 4096, 4096) == 0
+    # m = 16: 64 rows, except on the 2^24-element o weight; m = 64: 64 rows.
+    # With 64 rows, 192 or 344 row blocks take no slices, 64 take 4
+    assert [plan(16, n, k) for n, k in proj] == [(1, 64), (1, 16), (1, 64), (4, 64)]
+    assert [plan(64, n, k) for n, k in proj] == [(1, 64), (4, 64), (1, 64), (4, 64)]
+    assert attn.attn_flat_gemm_workspace_bytes(64, 4096, 4096) == 4 * 64 * 4096 * 4
+    # a short, deep weight (16 row blocks of 16, 256 steps): slices double
+    # while CUs stay idle and each wavefront keeps an 8-step batch
+    assert plan(16, 256, 8192, rows_per_workgroup=16) == (8, 16)
     assert plan(16, 256, 8192, num_cus=16, rows_per_workgroup=16) == (1, 16)
+    # 64 rows over 16 steps: 2 slices keep two 1-step batches per wavefront
+    assert plan(64, 4096, 512) == (2, 64)
     # forced counts are clamped to the number of 32-wide k steps
     assert plan(4, 64, 256, splits=100) == (8, 16)
     assert plan(4, 64, 256, splits=3) == (3, 16)

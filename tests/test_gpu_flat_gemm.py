@@ -19,11 +19,11 @@ from gpu_util import dev, host, require_gpu
 pytestmark = pytest.mark.gpu
 
 
-def run(d, c_dtype="bf16", splits=0, cols=None, rows=0):
+def run(d, c_dtype="bf16", splits=0, cols=None, rows=0, waves=0):
     a, w = dev(d["a"]), dev(d["w"])
     c = torch.full((d["m"], d["n"]), float("nan"),
                    dtype=torch.bfloat16 if c_dtype == "bf16" else torch.float32, device="cuda")
-    attn.attn_flat_gemm(a, w, c, splits=splits, rows_per_workgroup=rows)
+    attn.attn_flat_gemm(a, w, c, splits=splits, rows_per_workgroup=rows, waves_per_workgroup=waves)
     torch.cuda.synchronize()
     out = host(c)
     return out if cols is None else out[:, cols]
@@ -58,16 +58,19 @@ def test_flat_gemm_shapes(shape, c_dtype, rows):
     check(run(d, c_dtype, rows=rows), d, c_dtype, what=f"{shape} {c_dtype} rows {rows}")
 
 
+@pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("rows", [16, 64])
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
-def test_flat_gemm_forced_splits(splits, rows):
+def test_flat_gemm_forced_splits(splits, rows, waves):
     """k cut into slices across workgroups (fp32 partials in the workspace,
-    added in slice order) gives the same result to the bound."""
+    added in slice order) and over 4, 8 or 16 wavefronts per workgroup
+    gives the same result to the bound."""
     require_gpu()
-    d = wl.flat_gemm_inputs(9, 300, 2048, 77)
-    for c_dtype in ("bf16", "f32"):
-        check(run(d, c_dtype, splits=splits, rows=rows), d, c_dtype,
-              what=f"splits {splits} rows {rows} {c_dtype}")
+    for m in (9, 40):
+        d = wl.flat_gemm_inputs(m, 300, 2048, 77)
+        for c_dtype in ("bf16", "f32"):
+            check(run(d, c_dtype, splits=splits, rows=rows, waves=waves), d, c_dtype,
+                  what=f"m {m} splits {splits} rows {rows} waves {waves} {c_dtype}")
 
 
 def test_flat_gemm_planner_splits_small_n():

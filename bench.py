@@ -340,15 +340,14 @@ def bench_flat_gemm(steps, warmup, ms=(1, 16, 64)):
     m tokens per step.  Each shape rotates through enough device copies of W
     (>= 768 MB) that the 256 MB last-level cache cannot hold them; launches
     run back to back.  Bytes: W + A + C (W dominates)."""
-    out = {}
-    for m in ms:
-        res, tot_bytes, tot_ms = {}, 0, 0.0
-        for name, (n, k) in wl.LLAMA2_7B_PROJECTIONS.items():
-            d = wl.flat_gemm_inputs(m, n, k, 1200 + m)
-            a = dev(d["a"])
-            w0 = dev(d["w"])
-            copies = max(2, -(-(768 << 20) // (n * k * 2)))
-            ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    res = {m: {} for m in ms}
+    for name, (n, k) in wl.LLAMA2_7B_PROJECTIONS.items():
+        d = wl.flat_gemm_inputs(max(ms), n, k, 1200)
+        w0 = dev(d["w"])
+        copies = max(2, -(-(768 << 20) // (n * k * 2)))
+        ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+        for m in ms:
+            a = dev(d["a"][:m])
             c = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
 
             def step(i):
@@ -357,16 +356,19 @@ def bench_flat_gemm(steps, warmup, ms=(1, 16, 64)):
             durs, span, _ = time_launches(step, steps, warmup)
             mean_ms = span / steps
             nbytes = n * k * 2 + m * k * 2 + m * n * 2
-            res[name] = dict(n=n, k=k, us=round(mean_ms * 1e3, 2),
-                             gbs=round(nbytes / (mean_ms * 1e-3) / 1e9, 1),
-                             frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
-            tot_bytes += nbytes
-            tot_ms += mean_ms
-            del ws, w0
-            torch.cuda.empty_cache()
-        res["layer"] = dict(us=round(tot_ms * 1e3, 2), gbs=round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
-                            frac_hbm=round(tot_bytes / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
-        out[f"m{m}"] = res
+            res[m][name] = dict(n=n, k=k, us=round(mean_ms * 1e3, 2), bytes=nbytes,
+                                gbs=round(nbytes / (mean_ms * 1e-3) / 1e9, 1),
+                                frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        del ws, w0
+        torch.cuda.empty_cache()
+    out = {}
+    for m in ms:
+        r = res[m]
+        tot_ms = sum(v["us"] for v in r.values()) * 1e-3
+        tot_bytes = sum(v.pop("bytes") for v in r.values())
+        r["layer"] = dict(us=round(tot_ms * 1e3, 2), gbs=round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
+                          frac_hbm=round(tot_bytes / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        out[f"m{m}"] = r
     return dict(workload="flat GEMM C = A W^T, the four decode projections of one Llama2-7B "
                          "layer (qkv 12288x4096, o 4096x4096, gate_up 22016x4096, "
                          "down 4096x11008), bf16, m tokens", results=out)

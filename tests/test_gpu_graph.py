@@ -130,3 +130,40 @@ def test_graph_replay_cascade():
                                    c["scale"])
     assert_close(host(bufs[0][0])[rows], ro, "bf16", "replayed cascade O")
     assert_close(host(bufs[0][1])[rows], rl, "bf16", "replayed cascade lse")
+
+
+def test_graph_replay_flat_gemm():
+    """The flat GEMM of a decode projection with k sliced across workgroups
+    (main kernel + partial-sum reduction, workspace passed in), captured once
+    and replayed with new activations each time; every replay equals the
+    eager launch bit for bit and the oracle to the GEMM bound."""
+    require_gpu()
+    m, n, k = 12, 1000, 4096
+    d = wl.flat_gemm_inputs(m, n, k, 4201)
+    w = dev(d["w"])
+    a = dev(d["a"])
+    c = torch.empty((m, n), device="cuda")
+    splits = 4
+    ws = torch.empty(attn.attn_flat_gemm_workspace_bytes(m, n, k, splits), dtype=torch.uint8,
+                     device="cuda")
+    assert ws.numel() > 0
+
+    def step():
+        attn.attn_flat_gemm(a, w, c, splits=splits, workspace=ws)
+
+    g = capture(step)
+    gen = wl.generator(4202)
+    for rep in range(3):
+        a_np = wl.normal(gen, (m, k), "bf16")
+        a.copy_(dev(a_np))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = c.clone()
+        c.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got, c), f"replay {rep} differs from the eager launch"
+        ref = oracle.flat_gemm(a_np, d["w"])
+        bound = k * 2.0 ** -24 * oracle.flat_gemm(a_np & 0x7FFF, d["w"] & 0x7FFF)
+        assert (np.abs(host(got) - ref) <= bound).all(), f"replay {rep} outside the bound"

@@ -115,10 +115,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, grp = lane >> 4;
     const int G = a.Hq / a.Hkv;
-    __shared__ float s_m[4][kMaxG];
-    __shared__ float s_l[4][kMaxG];
+    // the wavefronts' published states, two sets: an item's two chunks are
+    // published one after the other and merged together at its end
+    __shared__ float s_m[2][4][kMaxG];
+    __shared__ float s_l[2][4][kMaxG];
     __shared__ float s_x[4][kMaxG];     // unified max: largest raw score per row
-    __shared__ float s_o[4][kMaxG][D];
+    __shared__ float s_o[2][4][kMaxG][D];
     const float phi_l2 = a.phi * kLog2e;
     const int cpi = chunks_per_item(a, FP8);
     auto item = [&](const int ci, const int kvh, const int b) {
@@ -205,19 +207,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             }
         };
 
-        // merge the four wavefronts' published states and write chunk cc's
-        // result (straight to the output when the sequence is one chunk)
-        auto finish = [&](int cc) {
+        // merge the four wavefronts' states published in set `set` and write
+        // chunk cc's result (straight to the output when the sequence is one
+        // chunk); the caller synchronises before the set is published again
+        auto finish = [&](int cc, int set) {
             for (int idx = threadIdx.x; idx < G * D; idx += 256) {
                 const int g = idx / D, d = idx % D;
                 float M = -INFINITY;
-                for (int w = 0; w < 4; w++) M = fmaxf(M, s_m[w][g]);
+                for (int w = 0; w < 4; w++) M = fmaxf(M, s_m[set][w][g]);
                 float lt = 0.f, ot = 0.f;
                 if (M != -INFINITY) {
                     for (int w = 0; w < 4; w++) {
-                        const float wt = (s_m[w][g] == -INFINITY) ? 0.f : fast_exp2(s_m[w][g] - M);
-                        lt = fmaf(wt, s_l[w][g], lt);
-                        ot = fmaf(wt, s_o[w][g][d], ot);
+                        const float sm = s_m[set][w][g];
+                        const float wt = (sm == -INFINITY) ? 0.f : fast_exp2(sm - M);
+                        lt = fmaf(wt, s_l[set][w][g], lt);
+                        ot = fmaf(wt, s_o[set][w][g][d], ot);
                     }
                 }
                 const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
@@ -233,7 +237,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                     if (d == 0) a.ws_lse[row * a.max_splits + cc] = lse;
                 }
             }
-            __syncthreads();   // s_o is rewritten next
         };
 
         float m_run = -INFINITY, l_run = 0.f, smax = -INFINITY;
@@ -355,12 +358,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 for (int i = 0; i < PU; i++) compute(u.p[i], PU * j + i);
             };
             // publish this wavefront's state to LDS, then a workgroup barrier
-            auto publish = [&]() {
+            auto publish = [&](int set) {
                 l_run = sum_xor32(sum_xor16(l_run));   // tokens of the four lane groups
                 if (!exact) smax = max_xor32(max_xor16(smax));
                 if (grp == 0) {
-                    s_m[wave][col] = m_run;
-                    s_l[wave][col] = l_run;
+                    s_m[set][wave][col] = m_run;
+                    s_l[set][wave][col] = l_run;
                     s_x[wave][col] = smax;
                 }
     #pragma unroll
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                         // 64(i/4) + 4(4grp + r) + i%4 (FP8)
                         const int dim = FP8 ? 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3)
                                             : 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
-                        s_o[wave][col][dim] = oacc[i][r];
+                        s_o[set][wave][col][dim] = oacc[i][r];
                     }
                 __syncthreads();
             };
@@ -382,8 +385,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             int n = 0;
             if (ncs == 2) {
                 // the first chunk is full and gives every wavefront the same,
-                // even number of units; its state is merged and written while
-                // the second chunk's first loads are in flight
+                // even number of units; its state is published to the first
+                // set while the second chunk's first loads are in flight, and
+                // merged with the second chunk's at the end of the item
                 const int nb = a.split_tokens / (kPage * PU * 4);
                 for (; n < nb; n += 2) {
                     load_u(bb, wave + 4 * (n + 1));
@@ -391,8 +395,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                     load_u(ba, wave + 4 * (n + 2));
                     compute_u(bb, wave + 4 * (n + 1));
                 }
-                publish();
-                finish(c);
+                publish(0);
                 m_run = exact ? -INFINITY : phi_l2;
                 l_run = 0.f;
                 smax = -INFINITY;
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 load_u(ba, wave + 4 * (n + 2));
                 compute_u(bb, wave + 4 * (n + 1));
             }
-            publish();
+            publish(ncs == 2 ? 1 : 0);
         };
 
         if (a.unified) {
@@ -432,7 +435,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             pass(std::true_type{});
         }
 
-        finish(c + ncs - 1);
+        for (int h = 0; h < ncs; h++) finish(c + h, h);
+        __syncthreads();   // the published states are rewritten by the next item
     };
     // persistent workgroups walk the (chunk, kv head, sequence) items; empty
     // chunks of short sequences cost a few scalar instructions

@@ -18,8 +18,9 @@ graph.  Chunked prefill against the paged cache is reported under
 projections (one Llama2-7B layer's four weights, m = 1, 16, 64 tokens) under
 "flat_gemm" in GB/s of weight + activation bytes.
 
-Timing: W untimed warm-up steps, then K steps bracketed by a device
-synchronisation on both sides; HIP events on the launch stream give each
+Timing: an untimed spin-up (the same step repeated for 50 ms: the GPU drops
+its clocks while the host prepares each section's inputs), W untimed warm-up
+steps, then K steps bracketed by a device synchronisation on both sides; HIP events on the launch stream give each
 launch's duration (the roofline uses their mean).  The prefill rotates
 through three input sets so the 256 MB last-level cache cannot hold the
 working set; the cascade flushes it before every timed repetition.
@@ -59,14 +60,40 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+SPINUP_S = 0.05   # untimed spin-up before each section's warm-up, seconds
+
+
+def spin_up(fn, before=None, seconds=SPINUP_S):
+    """Run the step back to back until `seconds` of wall time have passed.
+    The bench prepares each section's inputs on the host while the GPU idles,
+    and an idle GPU drops its clocks: measured after W = 10 warm-up launches
+    alone, the causal prefill ran at 460-478 TFLOP/s, after ~28 ms of the
+    same launches at 557.  The spin-up brings the GPU back to the state it
+    holds under sustained load before the W warm-up and K timed steps."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        if before:
+            before(i)
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                break
+    torch.cuda.synchronize()
+
+
 def time_launches(fn, steps, warmup, before=None):
     """Per-launch durations (ms) from HIP events on the current stream, plus
-    the span of the K timed steps and its wall time.
+    the span of the K timed steps and its wall time.  An untimed spin-up
+    (spin_up) runs before the W warm-up steps.
 
     Without a per-step ``before`` the K steps are enqueued back to back
     between one pair of events (per-step events would add their own gaps), so
     every duration is span / K.  With ``before`` (e.g. a cache flush) each step
     gets its own event pair and ``before`` stays outside the timed spans."""
+    spin_up(fn, before)
     for i in range(warmup):
         if before:
             before(i)
@@ -484,6 +511,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spinup_s_per_section": SPINUP_S,
         "ms_per_step": round(pre["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -14,7 +14,9 @@ the same run and reported under "decode" in KV GB/s: unique K+V bytes read
 (one byte per element for FP8), the shared prefix counted once; "decode"
 also holds 8-layer decode steps launched eagerly and replayed as a HIP
 graph.  Chunked prefill against the paged cache is reported under
-"prefill_paged" in algorithmic TFLOP/s, and the flat GEMM of the decode
+"prefill_paged" in algorithmic TFLOP/s, the same prefill without the mask
+under "prefill_noncausal", workload 1 (the fp32 test mode) under
+"prefill_f32_test_mode", and the flat GEMM of the decode
 projections (one Llama2-7B layer's four weights, m = 1, 16, 64 tokens) under
 "flat_gemm" in GB/s of weight + activation bytes.
 
@@ -174,6 +176,50 @@ def bench_prefill(steps, warmup):
                       traffic=traffic, kernel="prefill_bf16_kernel<128,true,false>",
                       algorithmic_bytes=int(4 * B * H * T * D * 2 + B * H * T * 4),
                       source_digest=digest))
+
+
+def bench_prefill_noncausal(steps, warmup):
+    """The workload-2 shape without the mask (B4 H32 T1024 D128 bf16): every
+    (query, key) pair attended, 4 D flop each; three input sets rotate."""
+    sets = []
+    for s in range(3):
+        inp = wl.workload(2, seed=1002 + 100 * s)
+        sets.append(tuple(dev(inp[x]) for x in ("q", "k", "v")))
+    B, H, T, D = 4, 32, 1024, 128
+    o = torch.empty((B, H, T, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, T), device="cuda")
+
+    def step(i):
+        q, k, v = sets[i % 3]
+        attn.attn_prefill(q, k, v, o, lse, causal=False, scale=1.0 / math.sqrt(D))
+
+    durs, span, _ = time_launches(step, steps, warmup)
+    flops = 4.0 * D * T * T * B * H
+    mean_ms = span / steps
+    return dict(workload="non-causal prefill B4 H32 T1024 D128 bf16", mean_ms=mean_ms,
+                tflops=round(flops / (mean_ms * 1e-3) / 1e12, 2),
+                frac_mfma=round(flops / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+
+
+def bench_prefill_f32(steps, warmup):
+    """Workload 1: the fp32 test mode, non-causal B1 H1 T128 D64 (4.19 MFLOP;
+    launch-latency bound, reported in microseconds and against the fp32
+    vector peak of 157.3 TFLOP/s)."""
+    inp = wl.workload(1)
+    q, k, v = (dev(inp[x]) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device="cuda")
+
+    def step(i):
+        attn.attn_prefill(q, k, v, o, lse, causal=False, scale=inp["scale"])
+
+    durs, span, _ = time_launches(step, steps, warmup)
+    flops = 4.0 * 64 * 128 * 128
+    mean_ms = span / steps
+    return dict(workload="non-causal prefill B1 H1 T128 D64 fp32 (test mode)",
+                us=round(mean_ms * 1e3, 2),
+                tflops=round(flops / (mean_ms * 1e-3) / 1e12, 4),
+                frac_fp32_peak=round(flops / (mean_ms * 1e-3) / 1e12 / 157.3, 5))
 
 
 def bench_prefill_paged(steps, warmup):
@@ -467,6 +513,10 @@ def main():
     decode = {}
     paged_prefill = None
     flat = None
+    noncausal = bench_prefill_noncausal(args.steps, args.warmup)
+    log(f"  non-causal: {noncausal['tflops']:.1f} TFLOP/s")
+    f32_mode = bench_prefill_f32(args.steps, args.warmup)
+    log(f"  fp32 test mode (workload 1): {f32_mode['us']:.1f} us per launch")
     if not args.prefill_only:
         log("chunked prefill against the paged cache ...")
         paged_prefill = bench_prefill_paged(args.steps, args.warmup)
@@ -526,6 +576,8 @@ def main():
         "decode": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                        for kk, vv in v.items()} for k, v in decode.items()},
         "prefill_paged": paged_prefill,
+        "prefill_noncausal": noncausal,
+        "prefill_f32_test_mode": f32_mode,
         "flat_gemm": flat,
     }
     print(json.dumps(line), flush=True)

@@ -60,10 +60,15 @@ def test_fp32_mode_shapes(shape, causal):
     (1, 1, 1, 1, 1, 128), (1, 2, 2, 33, 33, 64), (2, 4, 4, 300, 300, 128),
     (1, 4, 2, 257, 257, 128), (1, 2, 1, 100, 400, 128), (1, 2, 2, 512, 512, 64),
     (2, 2, 2, 640, 640, 128),
+    # groups of 8 query heads with batch x kv heads not a multiple of the 8
+    # XCDs (the workgroup-to-head map), Tq > Tk, and 8 query tiles of 256
+    (3, 16, 2, 200, 200, 128), (2, 6, 3, 96, 160, 64), (1, 2, 2, 300, 100, 128),
+    (1, 2, 1, 2048, 2048, 128),
 ])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_shapes(shape, causal):
-    """bf16 MFMA kernel on ragged shapes spanning several tiles."""
+    """bf16 MFMA kernel on ragged shapes spanning several tiles, grouped heads
+    and Tq != Tk (bottom-right causal alignment)."""
     require_gpu()
     B, Hq, Hkv, Tq, Tk, D = shape
     check(wl.prefill_inputs(B, Hq, Hkv, Tq, Tk, D, "bf16", 11 + Tq), causal)

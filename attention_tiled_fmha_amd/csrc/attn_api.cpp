@@ -66,9 +66,10 @@ int check_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
 //  - wavefronts per workgroup: 4 (more, smaller workgroups beat 8 on every
 //    shape but one, by up to 15%);
 //  - rows per workgroup: 16 for m <= 8, and for m <= 16 on weights of at
-//    most 2^24 elements; else 64 (four row blocks share every A fragment,
-//    so A is re-read from L2 a quarter as often: 283 -> ~170 us per layer
-//    at m = 64);
+//    most 2^24 elements; 32 for m <= 32 when 64-row blocks alone would
+//    number 1.25x the CUs (gate_up at m = 16: 47.5 us against 52.3); else
+//    64 (four row blocks share every A fragment, so A is re-read from L2 a
+//    quarter as often: 283 -> ~170 us per layer at m = 64);
 //  - k slices across workgroups (fp32 partials plus a reduction launch of
 //    ~4 us): with 16 rows, doubled while the row blocks alone leave CUs
 //    idle, and 4 when the grid fills one to three rounds of resident
@@ -87,7 +88,8 @@ int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* 
     if (o && (o->splits < 0 || o->rows_per_workgroup < 0 || o->waves_per_workgroup < 0))
         return ATTN_E_SHAPE;
     if (m > kFgMaxM || k > kFgMaxK || k % 8) return ATTN_E_UNSUPPORTED;
-    if (o && o->rows_per_workgroup && o->rows_per_workgroup != 16 && o->rows_per_workgroup != 64)
+    if (o && o->rows_per_workgroup && o->rows_per_workgroup != 16 && o->rows_per_workgroup != 32 &&
+        o->rows_per_workgroup != 64)
         return ATTN_E_UNSUPPORTED;
     if (o && o->waves_per_workgroup && o->waves_per_workgroup != 4 && o->waves_per_workgroup != 8)
         return ATTN_E_UNSUPPORTED;
@@ -96,8 +98,12 @@ int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* 
     int rb;
     if (o && o->rows_per_workgroup)
         rb = o->rows_per_workgroup / 16;
+    else if (m <= 8 || (m <= 16 && (long)n * k <= (1L << 24)))
+        rb = 1;
+    else if (m <= 32 && (long)((n + 63) / 64) * 4 >= 5L * num_cus)
+        rb = 2;
     else
-        rb = (m <= 8 || (m <= 16 && (long)n * k <= (1L << 24))) ? 1 : 4;
+        rb = 4;
     const long rblocks = (n + 16L * rb - 1) / (16L * rb);
     const int nsteps = (k + 31) / 32;
     const int U = attn::flat_gemm_batch_steps(std::max(m, 1), rb);
@@ -109,6 +115,8 @@ int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* 
         const long resident = (long)kFgResident * num_cus;
         if (s == 1 && rblocks > resident && rblocks < 3 * resident && nsteps / (4L * nw) >= U)
             s = 4;
+    } else if (rb == 2) {
+        while (s < 4 && rblocks * s < num_cus && nsteps / (2L * s * nw) >= 2 * U) s *= 2;
     } else if (rblocks * 8 < 5L * num_cus) {
         s = 4;
         while (s > 1 && nsteps / ((long)s * nw) < 2 * U) s /= 2;

@@ -174,7 +174,9 @@ __global__ __launch_bounds__(256) void flat_gemm_reduce_kernel(const float* __re
 
 // Steps per register batch: the loads of two batches stay within ~130 VGPRs.
 template <int MT, int RB> struct BatchSteps {
-    static constexpr int U = RB == 1 ? (MT == 1 ? 8 : MT == 2 ? 4 : 2) : (MT <= 2 ? 2 : 1);
+    static constexpr int U = RB == 1 ? (MT == 1 ? 8 : MT == 2 ? 4 : 2)
+                           : RB == 2 ? (MT == 1 ? 4 : 2)
+                                     : (MT <= 2 ? 2 : 1);
 };
 
 template <int MT, int RB, int NW, bool OUT_F32>
@@ -221,11 +223,12 @@ int batch_steps(int m) {
 }  // namespace
 
 int flat_gemm_batch_steps(int m, int row_blocks) {
-    return row_blocks == 4 ? batch_steps<4>(m) : batch_steps<1>(m);
+    return row_blocks == 4 ? batch_steps<4>(m) : row_blocks == 2 ? batch_steps<2>(m) : batch_steps<1>(m);
 }
 
 hipError_t launch_flat_gemm(const FlatGemmArgs& p, hipStream_t stream) {
     if (p.row_blocks == 4) return p.out_f32 ? go_mt<4, true>(p, stream) : go_mt<4, false>(p, stream);
+    if (p.row_blocks == 2) return p.out_f32 ? go_mt<2, true>(p, stream) : go_mt<2, false>(p, stream);
     return p.out_f32 ? go_mt<1, true>(p, stream) : go_mt<1, false>(p, stream);
 }
 

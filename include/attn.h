@@ -369,14 +369,15 @@ int attn_decode_shared_prefix_fp8(const void *q, const void *k_pages, const void
  * Errors: ATTN_E_NULL, ATTN_E_SHAPE (negative sizes or options),
  * ATTN_E_UNSUPPORTED (m > 64, k not a multiple of 8 or above 2^22, dtype
  * other than bf16, c_dtype other than bf16 / fp32, rows_per_workgroup other
- * than 0, 16, 64, waves_per_workgroup other than 0, 4, 8),
+ * than 0, 16, 32, 64, waves_per_workgroup other than 0, 4, 8),
  * ATTN_E_WORKSPACE,
  * ATTN_E_ARG (alignment), ATTN_E_HIP.
  *
  * attn_flat_gemm_plan: host-only.  The planner's choice for this shape on
  * num_cus compute units (<= 0: 256): rows of w per workgroup (16 for
- * m <= 8, and for m <= 16 on weights of at most 2^24 elements; else 64, so
- * that one A fragment serves four row blocks) and k slices across
+ * m <= 8, and for m <= 16 on weights of at most 2^24 elements; 32 for
+ * m <= 32 on weights with at least 1.25 blocks of 64 rows per CU; else 64,
+ * so that one A fragment serves four row blocks) and k slices across
  * workgroups (at most 4, and only when the row blocks alone leave compute
  * units idle or unevenly loaded); workgroups are 4 wavefronts.  Fields of opts that are > 0 override the choice; splits is
  * clamped to the number of 32-wide k steps.
@@ -384,7 +385,7 @@ int attn_decode_shared_prefix_fp8(const void *q, const void *k_pages, const void
  */
 typedef struct {
     int splits;               /* 0 = planner; > 0 forces that many k slices       */
-    int rows_per_workgroup;   /* 0 = planner; 16 or 64 forces it                  */
+    int rows_per_workgroup;   /* 0 = planner; 16, 32 or 64 forces it              */
     int waves_per_workgroup;  /* 0 = planner; 4 or 8 forces it                    */
     int reserved[5];
 } attn_flat_gemm_opts;

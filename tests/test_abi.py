@@ -290,7 +290,7 @@ def test_flat_gemm_checks(lib):
     assert flat_gemm(lib, k=-8) == E_SHAPE
     assert flat_gemm(lib, splits=-1) == E_SHAPE
     assert flat_gemm(lib, rows=-16) == E_SHAPE
-    assert flat_gemm(lib, rows=32) == E_UNSUP
+    assert flat_gemm(lib, rows=48) == E_UNSUP
     opts16 = ctypes.byref(attn.FlatGemmOpts(0, 0, 16))
     assert lib.attn_flat_gemm(FAKE, FAKE, FAKE, 4, 64, 256, 0, 0, None, 0, None, opts16) == E_UNSUP
     assert flat_gemm(lib, m=65) == E_UNSUP          # prefill-size m: a conventional GEMM
@@ -322,7 +322,9 @@ def test_flat_gemm_plan(lib):
         assert attn.attn_flat_gemm_workspace_bytes(m, 4096, 4096) == 0
     # m = 16: 64 rows, except on the 2^24-element o weight; m = 64: 64 rows.
     # With 64 rows, 192 or 344 row blocks take no slices, 64 take 4
-    assert [plan(16, n, k) for n, k in proj] == [(1, 64), (1, 16), (1, 64), (4, 64)]
+    # gate_up's 344 blocks of 64 rows are >= 1.25 per CU: 32 rows for m <= 32
+    assert [plan(16, n, k) for n, k in proj] == [(1, 64), (1, 16), (1, 32), (4, 64)]
+    assert [plan(32, n, k) for n, k in proj] == [(1, 64), (4, 64), (1, 32), (4, 64)]
     assert [plan(64, n, k) for n, k in proj] == [(1, 64), (4, 64), (1, 64), (4, 64)]
     assert attn.attn_flat_gemm_workspace_bytes(64, 4096, 4096) == 4 * 64 * 4096 * 4
     # a short, deep weight (16 row blocks of 16, 256 steps): slices double

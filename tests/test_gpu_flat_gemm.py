@@ -45,7 +45,7 @@ SHAPES = [(1, 1, 8), (1, 15, 40), (5, 100, 264), (16, 16, 32), (17, 33, 96),
           (32, 200, 520), (40, 64, 1024), (64, 1000, 1024), (3, 4096, 4096), (16, 4096, 4096)]
 
 
-@pytest.mark.parametrize("rows", [0, 16, 64])
+@pytest.mark.parametrize("rows", [0, 16, 32, 64])
 @pytest.mark.parametrize("c_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_flat_gemm_shapes(shape, c_dtype, rows):
@@ -59,7 +59,7 @@ def test_flat_gemm_shapes(shape, c_dtype, rows):
 
 
 @pytest.mark.parametrize("waves", [4, 8])
-@pytest.mark.parametrize("rows", [16, 64])
+@pytest.mark.parametrize("rows", [16, 32, 64])
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
 def test_flat_gemm_forced_splits(splits, rows, waves):
     """k cut into slices across workgroups (fp32 partials in the workspace,

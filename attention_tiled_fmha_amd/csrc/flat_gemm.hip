@@ -18,13 +18,14 @@
 // is the operands' register order, so nothing is shuffled.  Four lanes read
 // 64 contiguous bytes of a row; the next step reads the next 64.
 //
-// A workgroup (4 or 8 wavefronts) owns 16 or 64 rows of W; its k range (all
-// of k, or one of `splits` slices) is cut into contiguous per-wavefront
-// ranges.  Each wavefront streams its
-// range in batches of U steps with the next batch's loads in flight while the
-// current batch's MFMAs run: double buffering in registers, since every byte
-// of W is used once and staging it through LDS would only add traffic.  The
-// wavefronts' partial products are summed in fixed order through LDS.  With
+// A workgroup (4 or 8 wavefronts) owns RB = 1, 2 or 4 row blocks of 16 rows
+// of W, all of which use the same A fragments; its k range (all of k, or one
+// of `splits` slices) is cut into contiguous per-wavefront ranges.  Each
+// wavefront streams its range in batches of U steps with the next batch's
+// loads in flight while the current batch's MFMAs run: double buffering in
+// registers, since every byte of W is used once and staging it through LDS
+// would only add traffic.  The wavefronts' partial products are summed in
+// fixed order through LDS.  With
 // splits > 1 each slice writes fp32 partials to the workspace and
 // flat_gemm_reduce_kernel adds them in slice order.
 //

@@ -103,7 +103,7 @@ hipError_t launch_merge_states(void* o_a, float* lse_a, const void* o_b, const f
 
 // Flat GEMM C = A W^T (A [m][k], W [n][k] bf16; C [m][n] bf16 or fp32) for
 // m <= 64.  A workgroup of `waves` wavefronts owns 16 * row_blocks rows of W
-// (row_blocks 1 or 4) and one of `splits` slices of steps_per_split 32-wide
+// (row_blocks 1, 2 or 4) and one of `splits` slices of steps_per_split 32-wide
 // k steps; with splits > 1 the slices' fp32 partials go to ws
 // ([splits][m][n]) and a second kernel adds them.  k is a multiple of 8.
 struct FlatGemmArgs {

@@ -383,3 +383,17 @@ def test_unified_max_default_split():
     ro, rl = oracle_decode(d)
     assert_close(o, ro, "bf16", "O")
     assert n == 0
+
+
+def test_decode_longest_context():
+    """A 131072-token sequence (128 chunks of 1024 tokens, a 128-way combine)
+    next to a 70001-token one (ragged last page), GQA 32/8, every row against
+    the oracle, with the planner's split and with forced 512-token chunks."""
+    require_gpu()
+    d = wl.paged_decode_inputs(2, 32, 8, 128, "bf16", 71, lengths=[131072, 70001])
+    assert attn.attn_decode_plan(2, 8, 131072) == (1024, 128)
+    ro, rl = oracle_decode(d)
+    for split in (0, 512):
+        o, lse = run_decode(d, split_tokens=split)
+        assert_close(o, ro, "bf16", f"O split {split}")
+        assert_close(lse, rl, "bf16", f"lse split {split}")

@@ -154,3 +154,27 @@ def test_prefill_causal_rows_without_keys():
         assert np.all(o[:, :, :40] == 0) and np.all(np.isneginf(lse[:, :, :40]))
         assert_close(o, ro, dt, "O")
         assert_close(lse, rl, dt, "lse")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_long_sequence_sampled_rows(causal):
+    """T = 16384 (64 query tiles of 256, 512 key tiles of 32) with grouped
+    heads: sampled query rows (the first and last, both sides of tile
+    boundaries, random ones) against the oracle.  A causal row i is the
+    non-causal attention of query i over keys 0..i, so each sampled row is
+    checked on exactly the keys it may see."""
+    require_gpu()
+    B, Hq, Hkv, T, D = 1, 4, 2, 16384, 128
+    inp = wl.prefill_inputs(B, Hq, Hkv, T, T, D, "bf16", 61 + int(causal))
+    o, lse = run_prefill(inp, causal)
+    rng = np.random.default_rng(62)
+    rows = sorted(set([0, 1, 31, 32, 255, 256, 257, 8191, 8192, T - 257, T - 256, T - 1]
+                      + rng.integers(0, T, 20).tolist()))
+    for h in (0, 3):
+        kvh = h // (Hq // Hkv)
+        for i in rows:
+            n = i + 1 if causal else T
+            ro, rl = oracle.attention(inp["q"][:, h:h + 1, i:i + 1], inp["k"][:, kvh:kvh + 1, :n],
+                                      inp["v"][:, kvh:kvh + 1, :n], False, inp["scale"])
+            assert_close(o[0, h, i], ro[0, 0, 0], "bf16", f"O (h={h}, row {i})")
+            assert_close(lse[0, h, i:i + 1], rl[0, 0], "bf16", f"lse (h={h}, row {i})")

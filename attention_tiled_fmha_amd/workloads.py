@@ -287,61 +287,70 @@ def cascade_inputs(R, H, D, dtype, seed, prefix_len=4096, suffix_range=(128, 102
 
 
 # ---------------------------------------------------------------------------
-# the five named workloads
+# the named workloads
 # ---------------------------------------------------------------------------
 
-WORKLOADS = {
-    1: "non-causal prefill B1 H1 T128 D64 fp32",
-    2: "causal prefill B4 H32 T1024 D128 bf16 (Llama2-7B attention shape)",
-    3: "paged decode MHA B32 H32 D128 bf16, L~U[512,8192], page 16",
-    4: "paged decode GQA B128 Hq32 Hkv8 D128 bf16, L~logU[1024,32768], page 16, "
-       "split <= 512",
-    5: "shared-prefix cascade decode, 64 requests, prefix 4096, suffix U[128,1024], "
-       "H32 D128 bf16, page 16",
-}
+PREFILL_F32 = "prefill_f32_b1_h1_t128_d64"
+PREFILL_CAUSAL = "prefill_causal_b4_h32_t1024_d128"
+DECODE_MHA = "decode_mha_b32_h32_d128"
+DECODE_GQA = "decode_gqa_b128_hq32_hkv8_d128"
+CASCADE = "cascade_r64_prefix4096_h32_d128"
 
+WORKLOADS = {
+    PREFILL_F32: "non-causal prefill B1 H1 T128 D64 fp32",
+    PREFILL_CAUSAL: "causal prefill B4 H32 T1024 D128 bf16 (Llama2-7B attention shape)",
+    DECODE_MHA: "paged decode MHA B32 H32 D128 bf16, L~U[512,8192], page 16",
+    DECODE_GQA: "paged decode GQA B128 Hq32 Hkv8 D128 bf16, L~logU[1024,32768], page 16, "
+                "split <= 512",
+    CASCADE: "shared-prefix cascade decode, 64 requests, prefix 4096, suffix U[128,1024], "
+             "H32 D128 bf16, page 16",
+}
 
 FP8_WORKLOADS = {
-    3: "paged decode MHA B32 H32 D128, FP8 E4M3 cache (scale 1/32), bf16 q/o, L~U[512,8192], "
-       "page 16",
-    4: "paged decode GQA B128 Hq32 Hkv8 D128, FP8 E4M3 cache (scale 1/32), bf16 q/o, "
-       "L~logU[1024,32768], page 16, split <= 512",
-    5: "shared-prefix cascade decode, 64 requests, prefix 4096, suffix U[128,1024], H32 D128, "
-       "FP8 E4M3 cache (scale 1/32), bf16 q/o, page 16",
+    DECODE_MHA: "paged decode MHA B32 H32 D128, FP8 E4M3 cache (scale 1/32), bf16 q/o, "
+                "L~U[512,8192], page 16",
+    DECODE_GQA: "paged decode GQA B128 Hq32 Hkv8 D128, FP8 E4M3 cache (scale 1/32), bf16 q/o, "
+                "L~logU[1024,32768], page 16, split <= 512",
+    CASCADE: "shared-prefix cascade decode, 64 requests, prefix 4096, suffix U[128,1024], "
+             "H32 D128, FP8 E4M3 cache (scale 1/32), bf16 q/o, page 16",
 }
 
+# default seeds (PCG64), one per workload
+SEEDS = {PREFILL_F32: 1001, PREFILL_CAUSAL: 1002, DECODE_MHA: 1003, DECODE_GQA: 1004, CASCADE: 1005}
 
-def fp8_workload(n, seed=None):
-    """Workloads 3, 4 and 5 over an FP8 cache (same shapes and length draws)."""
-    seed = 1000 + n if seed is None else seed
-    if n == 5:
+
+def fp8_workload(name, seed=None):
+    """The decode and cascade workloads over an FP8 cache (same shapes and
+    length draws as the bf16 ones)."""
+    seed = SEEDS[name] if seed is None else seed
+    if name == CASCADE:
         return cascade_inputs(64, 32, 128, "fp8", seed)
-    if n == 3:
+    if name == DECODE_MHA:
         return paged_decode_fp8_inputs(32, 32, 32, 128, seed, length_range=(512, 8192),
                                        length_dist="uniform")
-    if n == 4:
+    if name == DECODE_GQA:
         return paged_decode_fp8_inputs(128, 32, 8, 128, seed, length_range=(1024, 32768),
                                        length_dist="log-uniform") | dict(split_tokens=512)
-    raise ValueError(f"no FP8 workload {n}")
+    raise ValueError(f"no FP8 workload {name}")
 
 
-def workload(n, seed=None):
-    """Inputs of workload ``n`` (1..5), seeded with 1000 + n by default."""
-    seed = 1000 + n if seed is None else seed
-    if n == 1:
+def workload(name, seed=None):
+    """Inputs of the named workload, seeded from SEEDS by default."""
+    seed = SEEDS[name] if seed is None else seed
+    if name == PREFILL_F32:
         return prefill_inputs(1, 1, 1, 128, 128, 64, "f32", seed) | dict(causal=False)
-    if n == 2:
+    if name == PREFILL_CAUSAL:
         return prefill_inputs(4, 32, 32, 1024, 1024, 128, "bf16", seed) | dict(causal=True)
-    if n == 3:
+    if name == DECODE_MHA:
         return paged_decode_inputs(32, 32, 32, 128, "bf16", seed,
                                    length_range=(512, 8192), length_dist="uniform")
-    if n == 4:
+    if name == DECODE_GQA:
         return paged_decode_inputs(128, 32, 8, 128, "bf16", seed,
                                    length_range=(1024, 32768), length_dist="log-uniform") \
             | dict(split_tokens=512)
-    if n == 5:
+    if name == CASCADE:
         return cascade_inputs(64, 32, 128, "bf16", seed)
-    raise ValueError(f"no workload {n}")
+    raise ValueError(f"no workload {name}")
 
 
 # ---------------------------------------------------------------------------

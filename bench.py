@@ -15,7 +15,7 @@ the same run and reported under "decode" in KV GB/s: unique K+V bytes read
 also holds 8-layer decode steps launched eagerly and replayed as a HIP
 graph.  Chunked prefill against the paged cache is reported under
 "prefill_paged" in algorithmic TFLOP/s, the same prefill without the mask
-under "prefill_noncausal", workload 1 (the fp32 test mode) under
+under "prefill_noncausal", the fp32 test mode (B1 H1 T128 D64) under
 "prefill_f32_test_mode", and the flat GEMM of the decode
 projections (one Llama2-7B layer's four weights, m = 1, 16, 64 tokens) under
 "flat_gemm" in GB/s of weight + activation bytes.
@@ -151,7 +151,7 @@ def measured_traffic(name, digest):
 def bench_prefill(steps, warmup):
     sets = []
     for s in range(3):
-        inp = wl.workload(2, seed=1002 + 100 * s)
+        inp = wl.workload(wl.PREFILL_CAUSAL, seed=1002 + 100 * s)
         sets.append(tuple(dev(inp[x]) for x in ("q", "k", "v")))
     B, H, T, D = 4, 32, 1024, 128
     o = torch.empty((B, H, T, D), dtype=torch.bfloat16, device="cuda")
@@ -183,7 +183,7 @@ def bench_prefill_noncausal(steps, warmup):
     (query, key) pair attended, 4 D flop each; three input sets rotate."""
     sets = []
     for s in range(3):
-        inp = wl.workload(2, seed=1002 + 100 * s)
+        inp = wl.workload(wl.PREFILL_CAUSAL, seed=1002 + 100 * s)
         sets.append(tuple(dev(inp[x]) for x in ("q", "k", "v")))
     B, H, T, D = 4, 32, 1024, 128
     o = torch.empty((B, H, T, D), dtype=torch.bfloat16, device="cuda")
@@ -202,10 +202,10 @@ def bench_prefill_noncausal(steps, warmup):
 
 
 def bench_prefill_f32(steps, warmup):
-    """Workload 1: the fp32 test mode, non-causal B1 H1 T128 D64 (4.19 MFLOP;
+    """The fp32 test mode, non-causal B1 H1 T128 D64 (4.19 MFLOP;
     launch-latency bound, reported in microseconds and against the fp32
     vector peak of 157.3 TFLOP/s)."""
-    inp = wl.workload(1)
+    inp = wl.workload(wl.PREFILL_F32)
     q, k, v = (dev(inp[x]) for x in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], device="cuda")
@@ -256,8 +256,8 @@ def kv_bytes(lengths, hkv, d, elem=2):
     return int(np.sum(np.asarray(lengths, np.int64))) * hkv * d * 2 * elem
 
 
-def bench_decode(n, steps, warmup):
-    d = wl.workload(n)
+def bench_decode(name, steps, warmup):
+    d = wl.workload(name)
     q = dev(d["q"])
     kp, vp = dev(d["k_pages"]), dev(d["v_pages"])
     bt, kl = dev(d["block_table"]), dev(d["kv_lens"])
@@ -277,16 +277,16 @@ def bench_decode(n, steps, warmup):
     mean_ms = float(np.mean(durs))
     split_used, nsplit = attn.attn_decode_plan(d["B"], d["Hkv"], maxlen, 0, split)
     del kp, vp
-    return dict(workload=wl.WORKLOADS[n], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
+    return dict(workload=wl.WORKLOADS[name], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
                 mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
                 frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 split_tokens=split_used, max_splits=nsplit)
 
 
-def bench_decode_fp8(n, steps, warmup):
+def bench_decode_fp8(name, steps, warmup):
     """Workload n's shapes and lengths over an FP8 (OCP E4M3) cache; KV bytes
     are one byte per element."""
-    d = wl.fp8_workload(n)
+    d = wl.fp8_workload(name)
     q = dev(d["q"])
     kp, vp = dev(d["k_pages"]), dev(d["v_pages"])
     bt, kl = dev(d["block_table"]), dev(d["kv_lens"])
@@ -306,16 +306,17 @@ def bench_decode_fp8(n, steps, warmup):
     nbytes = kv_bytes(d["kv_lens"], d["Hkv"], d["D"], elem=1)
     mean_ms = float(np.mean(durs))
     del kp, vp
-    return dict(workload=wl.FP8_WORKLOADS[n], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
+    return dict(workload=wl.FP8_WORKLOADS[name], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
                 mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
                 frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                 tokens_per_s=int(d["kv_lens"].sum()) * d["Hkv"] / (mean_ms * 1e-3))
 
 
 def bench_cascade(steps, warmup, fp8=False):
-    """Workload 5: prefix stage + suffix decode + merge on one stream, timed as
+    """Shared-prefix cascade decode (64 requests, 4096-token prefix, suffixes
+    U[128, 1024], H32 D128): prefix stage + suffix decode + merge on one stream, timed as
     one step.  With fp8 the cache is OCP E4M3 bytes with per-tensor scales."""
-    c = wl.fp8_workload(5) if fp8 else wl.workload(5)
+    c = wl.fp8_workload(wl.CASCADE) if fp8 else wl.workload(wl.CASCADE)
     q = dev(c["q"])
     kp, vp = dev(c["k_pages"]), dev(c["v_pages"])
     pp, st, sl = dev(c["prefix_pages"]), dev(c["suffix_table"]), dev(c["suffix_lens"])
@@ -357,7 +358,7 @@ def bench_cascade(steps, warmup, fp8=False):
     nbytes = (kv_bytes([c["prefix_len"]], c["Hkv"], D, elem=elem)
               + kv_bytes(c["suffix_lens"], c["Hkv"], D, elem=elem))
     mean_ms = float(np.mean(durs))
-    return dict(workload=(wl.FP8_WORKLOADS if fp8 else wl.WORKLOADS)[5], kv_bytes=nbytes,
+    return dict(workload=(wl.FP8_WORKLOADS if fp8 else wl.WORKLOADS)[wl.CASCADE], kv_bytes=nbytes,
                 mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
                 frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
 
@@ -451,7 +452,7 @@ def cpu_baseline(target_s=15.0):
     """The fp64 oracle on (b, h) pairs of the prefill workload, timed on the
     host cores; throughput in the bench's unit (algorithmic causal TFLOP/s)."""
     import oracle
-    inp = wl.workload(2)
+    inp = wl.workload(wl.PREFILL_CAUSAL)
     T, D = 1024, 128
     threads = oracle.default_threads()
     pairs, flops, t_used = 0, 0.0, 0.0
@@ -516,29 +517,29 @@ def main():
     noncausal = bench_prefill_noncausal(args.steps, args.warmup)
     log(f"  non-causal: {noncausal['tflops']:.1f} TFLOP/s")
     f32_mode = bench_prefill_f32(args.steps, args.warmup)
-    log(f"  fp32 test mode (workload 1): {f32_mode['us']:.1f} us per launch")
+    log(f"  fp32 test mode (B1 H1 T128 D64): {f32_mode['us']:.1f} us per launch")
     if not args.prefill_only:
         log("chunked prefill against the paged cache ...")
         paged_prefill = bench_prefill_paged(args.steps, args.warmup)
         log(f"  {paged_prefill['tflops']:.1f} TFLOP/s")
         torch.cuda.empty_cache()
-        for n in (3, 4):
-            log(f"decode workload {n} ...")
-            decode[f"workload{n}"] = bench_decode(n, args.steps, args.warmup)
-            log(f"  {decode[f'workload{n}']['gbs']:.0f} GB/s")
+        for name in (wl.DECODE_MHA, wl.DECODE_GQA):
+            log(f"{name} ...")
+            decode[name] = bench_decode(name, args.steps, args.warmup)
+            log(f"  {decode[name]['gbs']:.0f} GB/s")
             torch.cuda.empty_cache()
-        for n in (3, 4):
-            log(f"decode workload {n}, FP8 cache ...")
-            decode[f"workload{n}_fp8"] = bench_decode_fp8(n, args.steps, args.warmup)
-            log(f"  {decode[f'workload{n}_fp8']['gbs']:.0f} GB/s")
+        for name in (wl.DECODE_MHA, wl.DECODE_GQA):
+            log(f"{name}, FP8 cache ...")
+            decode[name + "_fp8"] = bench_decode_fp8(name, args.steps, args.warmup)
+            log(f"  {decode[name + '_fp8']['gbs']:.0f} GB/s")
             torch.cuda.empty_cache()
-        log("cascade workload 5 ...")
-        decode["workload5"] = bench_cascade(args.steps, args.warmup)
-        log(f"  {decode['workload5']['gbs']:.0f} GB/s")
+        log(f"{wl.CASCADE} ...")
+        decode[wl.CASCADE] = bench_cascade(args.steps, args.warmup)
+        log(f"  {decode[wl.CASCADE]['gbs']:.0f} GB/s")
         torch.cuda.empty_cache()
-        log("cascade workload 5, FP8 cache ...")
-        decode["workload5_fp8"] = bench_cascade(args.steps, args.warmup, fp8=True)
-        log(f"  {decode['workload5_fp8']['gbs']:.0f} GB/s")
+        log(f"{wl.CASCADE}, FP8 cache ...")
+        decode[wl.CASCADE + "_fp8"] = bench_cascade(args.steps, args.warmup, fp8=True)
+        log(f"  {decode[wl.CASCADE + '_fp8']['gbs']:.0f} GB/s")
         for key, B, lr in (("decode_step_graph_b1", 1, (256, 1024)),
                            ("decode_step_graph_b4", 4, (1024, 4096))):
             log(f"8-layer decode step B{B}, eager vs graph replay ...")

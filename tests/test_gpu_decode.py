@@ -142,13 +142,14 @@ def test_decode_equals_last_prefill_row():
     assert_close(lse[0], host(pl)[0, :, 0], "f32", "decode vs prefill lse")
 
 
-@pytest.mark.parametrize("n", [3, 4])
-def test_decode_workloads_full_size_sampled(n):
-    """Workloads 3 (MHA, B32) and 4 (GQA 32/8, B128, chunks of 512) at full
-    size in the bench's launch configuration; the oracle checks a sample of
-    sequences element by element."""
+@pytest.mark.parametrize("name", [wl.DECODE_MHA, wl.DECODE_GQA])
+def test_decode_workloads_full_size_sampled(name):
+    """The MHA (B32 H32, L~U[512,8192]) and GQA (B128 32/8, L~logU[1024,32768],
+    chunks of 512) decode workloads at full size in the bench's launch
+    configuration; the oracle checks a sample of sequences element by
+    element."""
     require_gpu()
-    d = wl.workload(n)
+    d = wl.workload(name)
     o, lse = run_decode(d, split_tokens=d.get("split_tokens", 0))
     rows = [0, 1, int(np.argmax(d["kv_lens"])), int(np.argmin(d["kv_lens"])), d["B"] - 1]
     ro, rl = oracle_decode(d, rows)
@@ -232,10 +233,10 @@ def test_cascade_small_fp32():
     assert_close(lse, rl, "f32", "cascade lse")
 
 
-def test_cascade_workload5_full_size():
+def test_cascade_r64_prefix4096_full_size():
     """64 requests sharing a 4096-token prefix, suffixes U[128, 1024]."""
     require_gpu()
-    c = wl.workload(5)
+    c = wl.workload(wl.CASCADE)
     o, lse = run_cascade(c)
     rows = [0, 1, 31, 63]
     sub = dict(c, q=c["q"][rows], suffix_table=c["suffix_table"][rows],
@@ -247,12 +248,12 @@ def test_cascade_workload5_full_size():
     assert_close(lse[rows], rl, "bf16", "cascade lse")
 
 
-def test_cascade_two_streams_workload5():
+def test_cascade_two_streams():
     """The prefix stage on a second stream, concurrent with the suffix decode
     on the first (the two stages share nothing but the read-only cache), then
     the merge once both are done: the same result as one stream."""
     require_gpu()
-    c = wl.workload(5)
+    c = wl.workload(wl.CASCADE)
     q = dev(c["q"])
     kp, vp = dev(c["k_pages"]), dev(c["v_pages"])
     R, H, D = q.shape

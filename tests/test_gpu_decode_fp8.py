@@ -142,13 +142,13 @@ def test_fp8_page_placement_invariance():
     assert np.array_equal(oa, ob) and np.array_equal(la, lb), "placement changed the result"
 
 
-@pytest.mark.parametrize("n", [3, 4])
-def test_fp8_workloads_full_size_sampled(n):
-    """The shapes of workloads 3 (MHA, B32) and 4 (GQA 32/8, B128, chunks of
-    512) over FP8 caches at full size, in the bench's launch configuration;
-    the oracle checks a sample of sequences element by element."""
+@pytest.mark.parametrize("name", [wl.DECODE_MHA, wl.DECODE_GQA])
+def test_fp8_workloads_full_size_sampled(name):
+    """The MHA (B32) and GQA (32/8, B128, chunks of 512) decode shapes over
+    FP8 caches at full size, in the bench's launch configuration; the oracle
+    checks a sample of sequences element by element."""
     require_gpu()
-    d = wl.fp8_workload(n)
+    d = wl.fp8_workload(name)
     o, lse = run_fp8(d, split_tokens=d.get("split_tokens", 0))
     rows = [0, 1, int(np.argmax(d["kv_lens"])), int(np.argmin(d["kv_lens"])), d["B"] - 1]
     ro, rl = oracle_fp8(d, rows)
@@ -202,12 +202,12 @@ def run_cascade_fp8(c):
     return host(o_p), host(l_p)
 
 
-def test_fp8_cascade_workload5_full_size():
-    """Workload 5's shape over an FP8 cache (64 requests, 4096-token prefix,
+def test_fp8_cascade_r64_prefix4096_full_size():
+    """The cascade shape over an FP8 cache (64 requests, 4096-token prefix,
     suffixes U[128, 1024]): prefix stage, suffix decode and merge against the
     plain decode of each request's whole key sequence."""
     require_gpu()
-    c = wl.fp8_workload(5)
+    c = wl.fp8_workload(wl.CASCADE)
     o, lse = run_cascade_fp8(c)
     rows = [0, 1, 31, 63]
     npre = len(c["prefix_pages"])

@@ -38,10 +38,10 @@ def check(inp, causal, bh_sample=None):
         assert_close(lse, rl, inp["dtype"], "lse")
 
 
-def test_workload1_fp32_noncausal():
+def test_prefill_f32_b1h1t128d64_noncausal():
     """B1 H1 T128 D64 fp32, non-causal: max-abs <= 1e-5."""
     require_gpu()
-    check(wl.workload(1), causal=False)
+    check(wl.workload(wl.PREFILL_F32), causal=False)
 
 
 @pytest.mark.parametrize("shape", [
@@ -74,11 +74,11 @@ def test_bf16_shapes(shape, causal):
     check(wl.prefill_inputs(B, Hq, Hkv, Tq, Tk, D, "bf16", 11 + Tq), causal)
 
 
-def test_workload2_full_size_sampled():
+def test_prefill_causal_b4h32t1024d128_full_size_sampled():
     """Causal B4 H32 T1024 D128 bf16 at full size, as launched by the bench;
     the oracle checks a sample of (b, h) pairs element by element."""
     require_gpu()
-    inp = wl.workload(2)
+    inp = wl.workload(wl.PREFILL_CAUSAL)
     check(inp, causal=True, bh_sample=[(0, 0), (1, 17), (2, 31), (3, 8)])
 
 

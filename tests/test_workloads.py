@@ -39,7 +39,7 @@ def test_paged_layout():
 
 
 def test_workload_shapes():
-    w1 = wl.workload(1)
+    w1 = wl.workload(wl.PREFILL_F32)
     assert w1["q"].shape == (1, 1, 128, 64) and w1["q"].dtype == np.float32
     c = wl.cascade_inputs(4, 2, 8, "bf16", 9, prefix_len=64, suffix_range=(1, 33))
     assert len(c["prefix_pages"]) == 4

@@ -34,7 +34,11 @@
 // addresses).  V is transposed while it is written (V^T: one row per head
 // dimension) with the keys of each 16-key group ordered so that the 8 keys
 // one MFMA lane needs are 16 contiguous bytes; the 80-byte V^T row stride
-// makes the 16-row reads conflict-free.
+// makes the 16-row reads conflict-free.  Even dimensions 2i take rows i and
+// odd ones 2i + 1 rows D/2 + i: a thread that loads the dimension pair
+// (2i, 2i + 1) then writes rows 80 bytes apart across the wavefront (16 bank
+// offsets, a 2-way conflict) instead of 160 (8 offsets, 4-way).  O^T
+// inherits the row order; the epilogue interleaves the two halves.
 //
 // The running max is raised (and O, l rescaled) only when a row's max grows
 // by more than 2^8; otherwise exponentials are taken against the stale max.
@@ -183,9 +187,9 @@ __device__ __forceinline__ void store_stage(const Stage& st, unsigned char* kbuf
         const uint32_t e23 = __builtin_amdgcn_perm(v3, v2, 0x05040100u);
         const uint32_t o01 = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
         const uint32_t o23 = __builtin_amdgcn_perm(v3, v2, 0x07060302u);
-        unsigned char* row = vbuf + C::K_BYTES + (2 * dp) * C::VT_STRIDE + vt_pos(4 * kb4) * 2;
-        *(u32x2*)row = u32x2{e01, e23};
-        *(u32x2*)(row + C::VT_STRIDE) = u32x2{o01, o23};
+        unsigned char* row = vbuf + C::K_BYTES + dp * C::VT_STRIDE + vt_pos(4 * kb4) * 2;
+        *(u32x2*)row = u32x2{e01, e23};                             // dim 2dp: row dp
+        *(u32x2*)(row + (D / 2) * C::VT_STRIDE) = u32x2{o01, o23};  // dim 2dp + 1: row D/2 + dp
     }
 }
 
@@ -430,14 +434,21 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < Tq) {
+        // O^T row p = 32 db + 8 g + 4 hi + j holds dimension 2p (p < D/2) or
+        // 2(p - D/2) + 1: rows p of block db and p + D/2 of block db + DB/2
+        // give dimensions 2p and 2p + 1, so 4 rows make 16 contiguous bytes.
         uint16_t* op = o + ((size_t)bh * Tq + qrow) * D;
 #pragma unroll
-        for (int db = 0; db < C::DB; db++)
+        for (int db = 0; db < C::DB / 2; db++)
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                const int d0 = 32 * db + 8 * g + 4 * hi;
-                *(u32x2*)(op + d0) = u32x2{pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                                           pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                const int p0 = 32 * db + 8 * g + 4 * hi;
+                constexpr int H = C::DB / 2;
+                uint32_t w[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    w[j] = pack_bf16x2(oacc[db][4 * g + j] * inv, oacc[db + H][4 * g + j] * inv);
+                *(u32x4*)(op + 2 * p0) = u32x4{w[0], w[1], w[2], w[3]};
             }
         if (lse && hi == 0)
             lse[(size_t)bh * Tq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;

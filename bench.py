@@ -179,7 +179,7 @@ def bench_prefill(steps, warmup):
 
 
 def bench_prefill_noncausal(steps, warmup):
-    """The workload-2 shape without the mask (B4 H32 T1024 D128 bf16): every
+    """The causal prefill shape without the mask (B4 H32 T1024 D128 bf16): every
     (query, key) pair attended, 4 D flop each; three input sets rotate."""
     sets = []
     for s in range(3):

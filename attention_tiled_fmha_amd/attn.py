@@ -100,6 +100,17 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _workspace(need, device, stream):
+    """A workspace of ``need`` bytes for one call.  It is allocated on the
+    stream the call is enqueued on: torch's caching allocator hands a freed
+    block only to later work of the stream it was allocated on, which runs
+    after this call's kernels, so releasing it on return is safe."""
+    if stream is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(need, dtype=torch.uint8, device=device)
+
+
 def _dense(t, name):
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous device tensor")
@@ -204,7 +215,7 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse=None, ma
     scale = D ** -0.5 if scale is None else scale
     need = attn_decode_workspace_bytes(B, Hq, Hkv, D, max_kv_len, split_tokens)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if fallback_count is not None:
         _dense(fallback_count, "fallback_count")
@@ -247,7 +258,7 @@ def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, kv
     scale = D ** -0.5 if scale is None else scale
     need = attn_decode_workspace_bytes(B, Hq, Hkv, D, max_kv_len, split_tokens)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     opts = DecodeOpts(split_tokens=int(split_tokens))
     _check(load().attn_decode_paged_fp8(
@@ -300,7 +311,7 @@ def attn_decode_shared_prefix(q, k_pages, v_pages, prefix_pages, prefix_len, o, 
     scale = D ** -0.5 if scale is None else scale
     need = attn_shared_prefix_workspace_bytes(B, Hq, Hkv, D, prefix_len, dt)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().attn_decode_shared_prefix(
         _p(q), _p(k_pages), _p(v_pages), _p(prefix_pages), int(prefix_len), _p(o), _p(lse),
@@ -333,7 +344,7 @@ def attn_decode_shared_prefix_fp8(q, k_pages, v_pages, k_scale, v_scale, prefix_
     scale = D ** -0.5 if scale is None else scale
     need = attn_shared_prefix_workspace_bytes(B, Hq, Hkv, D, prefix_len, FP8_E4M3)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().attn_decode_shared_prefix_fp8(
         _p(q), _p(k_pages), _p(v_pages), float(k_scale), float(v_scale), _p(prefix_pages),
@@ -379,7 +390,7 @@ def attn_flat_gemm(a, w, c, splits=0, rows_per_workgroup=0, waves_per_workgroup=
         raise TypeError("a and w must be bf16")
     need = attn_flat_gemm_workspace_bytes(m, n, k, splits, rows_per_workgroup, waves_per_workgroup)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+        workspace = _workspace(need, a.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().attn_flat_gemm(_p(a), _p(w), _p(c), m, n, k, BF16, _dtype(c), _p(workspace),
                                  ws_bytes, _stream(stream),

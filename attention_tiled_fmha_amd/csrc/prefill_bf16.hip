@@ -230,8 +230,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int qw0 = q0 + rb * 32;        // this wavefront's first row
     const int qrow = qw0 + li;           // the query row of this lane
     // paged: the sequence's own key count (its chunk of Tq queries is its
-    // last Tq positions, so the causal diagonal sits at kv_len - Tq)
-    const int Tk = PAGED ? __builtin_amdgcn_readfirstlane(kv_lens[b]) : Tk_dense;
+    // last Tq positions, so the causal diagonal sits at kv_len - Tq), clamped
+    // to what its block-table row can map so no page index leaves the row
+    const int Tk = PAGED ? __builtin_amdgcn_readfirstlane(max(0, min(kv_lens[b], bt_stride * 16)))
+                         : Tk_dense;
     const int diag = Tk - Tq;
 
     const uint16_t* qp = q + (size_t)bh * Tq * D;

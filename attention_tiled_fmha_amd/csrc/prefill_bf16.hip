@@ -1,44 +1,50 @@
-// Dense prefill FMHA, bf16 in/out, on gfx950 bf16 MFMA with fp32 accumulation.
+// Dense and paged prefill FMHA, bf16 in/out, on gfx950 bf16 MFMA with fp32
+// accumulation.
 //
 // Method: the fused, tiled attention of the TensorRT-LLM FMHA page
 // (zyxy.net/?p=24414, section 2: score, softmax and weighted sum fused in one
 // kernel, tiles staged on chip, a bank-conflict-free on-chip layout, stable
 // softmax) with the online softmax update of FlashAttention (FlashDecoding++
 // summary, wenjunhu.com/d/2311396.html, section 1), so the T x T score matrix
-// never leaves registers.  K/V tiles are double-buffered in LDS: the next
-// tile is fetched while the current one is consumed (the ping-pong buffer of
-// the same summary, section 4).
+// never leaves registers.  K/V tiles are double-buffered in LDS and the next
+// ones are in flight from HBM while the current ones are consumed (the
+// ping-pong buffering of the same summary, section 4).
 //
 // gfx950 mapping
 // --------------
-// A workgroup is 8 wavefronts = 256 query rows of one (batch, head); each
-// wavefront owns 32 rows.  Per key tile of BN = 32 keys a wavefront does
+// A workgroup is 4 wavefronts, one per SIMD, and owns 256 query rows of one
+// (batch, head).  Each wavefront holds two 32-row blocks of queries (blocks w
+// and 7 - w of the 8 in the tile, which gives every wavefront the same share
+// of the causal diagonal).  Per key tile of 32 keys a wavefront computes, for
+// both blocks,
 //
-//   S^T = K Q^T     8 x v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q held in
-//                   VGPRs for the whole kernel.  Computing S^T rather than S
-//                   gives lane l the scores of query row l % 32 for 16 of the
-//                   32 keys (the other 16 sit in lane l ^ 32): row max and
-//                   row sum are lane-local plus one v_permlane32_swap.
+//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q held in
+//                   VGPRs.  S^T puts one query row per lane and 16 of the 32
+//                   keys in its registers (the rest in lane l ^ 32): row max
+//                   and row sum are lane-local plus one v_permlane32_swap.
 //   softmax         exp2 of the scaled scores against the running max, P
-//                   rounded to bf16 (already in B-operand order for PV).
-//   O^T += V^T P^T  8 MFMAs, A = V^T from LDS.
+//                   rounded to bf16, already in B-operand order for PV.
+//   O^T += V^T P^T  A = V^T read from the row-major V tile with the gfx950
+//                   transposing LDS read ds_read_b64_tr_b16.
 //
-// MFMA and VALU work of one wavefront do not overlap on gfx950; those of two
-// wavefronts on one SIMD do.  So the eight wavefronts form two groups (one
-// wavefront of each per SIMD) that run half a tile apart: while group 0
-// issues the MFMAs of tile t (PV of t-1, then S of t), group 1 runs the
-// softmax of tile t-1, and the other way round.  A workgroup barrier
-// separates the phases.  Each wavefront stays under 256 VGPRs (two per SIMD).
+// Every K or V fragment read from LDS feeds both blocks' MFMAs, so a
+// wavefront reads half as many LDS bytes per MFMA as with 32-row
+// wavefronts.  On gfx950 an MFMA and VALU work share the SIMD's issue
+// capacity whether they come from one wavefront or two, so the three jobs of
+// a step run interleaved in one instruction stream: step t issues the MFMAs
+// of S(t+1) and of O += P(t-1) V(t-1) while the VALU runs the softmax of
+// S(t).  The softmax is branch-free (the running max is selected, not
+// branched on); O is rescaled in a short branch at the end of the step,
+// after the PV MFMAs that still belong to the old max.
 //
-// LDS: K row-major with a 16-byte row pad (conflict-free 16-row reads, affine
-// addresses).  V is transposed while it is written (V^T: one row per head
-// dimension) with the keys of each 16-key group ordered so that the 8 keys
-// one MFMA lane needs are 16 contiguous bytes; the 80-byte V^T row stride
-// makes the 16-row reads conflict-free.  Even dimensions 2i take rows i and
-// odd ones 2i + 1 rows D/2 + i: a thread that loads the dimension pair
-// (2i, 2i + 1) then writes rows 80 bytes apart across the wavefront (16 bank
-// offsets, a 2-way conflict) instead of 160 (8 offsets, 4-way).  O^T
-// inherits the row order; the epilogue interleaves the two halves.
+// K/V tiles go HBM -> VGPRs -> LDS: the loads of step t + 1's tile pair are
+// issued at the start of step t into one of two register sets, the set
+// loaded during step t - 1 is written to LDS at the end of step t, and one
+// workgroup barrier per step hands the tiles over.  LDS rows are
+// 16-byte-granule XOR swizzled: the 16 rows one K read spans and the 4 rows x
+// 4 granules one transposed V read spans each hit 16 distinct granule
+// positions of the 64 banks, and each wavefront's 16-byte writes are 1 KiB
+// contiguous.
 //
 // The running max is raised (and O, l rescaled) only when a row's max grows
 // by more than 2^8; otherwise exponentials are taken against the stale max.
@@ -47,10 +53,12 @@
 // bf16-rounded P that the MFMA multiplies with V.
 //
 // Causal masking (key j visible to query i iff j <= i + Tk - Tq) is applied
-// only on tiles that cross the diagonal; tiles wholly above a wavefront's
-// rows are skipped.  Workgroups are issued heaviest (longest key range)
-// first, and all query tiles of one (b, h) land on one XCD so their shared
-// K/V stay in that XCD's L2.
+// only on tiles that cross a block's diagonal.  When there are at least two
+// query tiles per CU, a workgroup takes query tiles p and n - 1 - p of one
+// (b, h) (equal causal work per workgroup), lighter first, and the
+// workgroups of one (b, h) sit on one XCD at the same time, so each K/V tile
+// is fetched from HBM about once and hit in that XCD's L2 afterwards.
+// Otherwise every workgroup takes one query tile, heaviest first.
 #include <type_traits>
 
 #include "common.h"
@@ -60,175 +68,177 @@ namespace attn {
 
 namespace {
 
-constexpr int kWaves = 8;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = kWaves * 32;         // 256 query rows per workgroup
-constexpr int kBN = 32;                  // keys per tile
+constexpr int kBM = 256;                 // query rows per query tile (8 blocks of 32)
+constexpr int kBN = 32;                  // keys per K/V tile
 constexpr float kRescaleThresh = 8.0f;   // log2 units
 
 template <int D>
 struct Cfg {
-    static constexpr int KS = D / 16;                    // MFMA k-steps of K Q^T
-    static constexpr int DB = D / 32;                    // 32-row blocks of O^T (dims)
-    static constexpr int CPR = D / 8;                    // 16-byte chunks per K row
-    static constexpr int K_STRIDE = D * 2 + 16;          // K row + 16-byte pad
-    static constexpr int K_BYTES = kBN * K_STRIDE;
-    static constexpr int VT_STRIDE = kBN * 2 + 16;       // V^T row (32 keys) + pad
-    static constexpr int V_BYTES = D * VT_STRIDE;
-    static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-    static constexpr int K_CHUNKS = kBN * CPR;           // 16-byte chunks per K tile
-    static constexpr int V_UNITS = (kBN / 4) * (D / 2);  // 4-key x 2-dim V units
+    static constexpr int KS = D / 16;              // k-steps of S^T = K Q^T
+    static constexpr int DB = D / 32;              // 32-dim blocks of O^T
+    static constexpr int GPR = D / 8;              // 16-byte granules per row
+    static constexpr int ROW = 2 * D;              // bytes per K/V row
+    static constexpr int TILE = kBN * ROW;         // bytes per K or V tile
+    static constexpr int LPT = kBN * GPR / kThreads;  // 16-byte loads per thread per K or V tile
 };
 
-// V^T position of key k (0..31) in its row: in each 16-key group the 4-key
-// blocks 1 and 2 trade places, so keys 16s + {0..3, 8..11} (MFMA lanes 0-31)
-// and 16s + {4..7, 12..15} (lanes 32-63) are each contiguous.
-__device__ __forceinline__ int vt_pos(int key) {
-    const int a = (key >> 2) & 3;
-    return (key & ~15) | ((((a & 1) << 1) | (a >> 1)) << 2) | (key & 3);
-}
+// Granule positions.  K (read 16 rows x one granule per instruction):
+// D = 128 rows are 256 bytes, position c ^ (r mod 16); D = 64 rows are 128
+// bytes (two per bank sweep), position c ^ (r/2 mod 8).  V (read 4 rows x 4
+// granules per 32 lanes): D = 128 position c ^ 4(r mod 4); D = 64
+// c ^ 4(r/2 mod 2).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
-// One thread's share of a tile in flight: a 16-byte K chunk and a 4-key x
-// 2-dim V unit (4 dwords).
-struct Stage {
-    u32x4 k;
-    u32x4 v;
-};
-
-// Raw buffer resource over the rows [k0, min(k0 + kBN, Tk)) of one (b, h) K or
-// V slice.  Buffer loads past its end return 0 without touching memory, so
-// tail tiles, tiles past the key range and the idle threads of D = 64 need no
-// branch and no address clamp; the descriptor is built with scalar ALU only.
+// Raw buffer resource over `bytes` bytes from base.  Loads at or past the
+// size return zeros without touching memory, so tail tiles, tiles past the
+// key range and pages past a sequence's length need no branch; the
+// descriptor is built with scalar ALU only.
 constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data, no swizzle
-template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int k0, int Tk) {
-    // (the clamp lowers to a vector op; readfirstlane keeps the descriptor scalar)
-    const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(kBN, Tk - k0)) * D * 2);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)k0 * D), (short)0, bytes,
-                                             kRsrcWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 
-// Byte offsets of this thread's K chunk and V unit inside a tile (fixed for
-// the whole kernel).  Threads past the tile's chunk count land past the
-// descriptor's end and read zeros.
-template <int D>
-struct LoadOffsets {
-    int k, v;
-    __device__ explicit LoadOffsets(int tid) {
-        constexpr int CPR = Cfg<D>::CPR;
-        k = (tid / CPR) * D * 2 + 16 * (tid % CPR);
-        v = 4 * (tid / (D / 2)) * D * 2 + 4 * (tid % (D / 2));   // keys 4kb4.., dims 2dp, 2dp+1
-    }
-};
-
-template <int D>
-__device__ __forceinline__ void load_stage(Stage& st, const uint16_t* __restrict__ kp,
-                                           const uint16_t* __restrict__ vp, int k0k, int k0v,
-                                           int Tk, const LoadOffsets<D>& off) {
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kp, k0k, Tk);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vp, k0v, Tk);
-    st.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 4; j++) st.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, off.v + j * D * 2, 0, 0);
-}
-
-// Paged K/V (prefill against a paged cache, [pages][Hkv][16][D]): within a
-// 32-key tile, the K rows of one wavefront's chunks (4 for D = 128, 8 for
-// D = 64) and the keys of its V units (the same) lie in one 16-token page,
-// slot 0 or 1 of the tile, so each wavefront loads through a descriptor
-// over that page alone: its base from the sequence's block-table entry, its
-// size the page's valid rows (a page at or past the sequence's length has
-// none and reads zeros without touching memory).
-struct PagedKV {
-    const uint16_t* kpool;
-    const uint16_t* vpool;
-    const int32_t* table;   // this sequence's block-table row
+// Where the K/V of one (b, kv head) live: a dense [Tk][D] slice, or a
+// sequence's block-table row over the paged pools [pages][Hkv][16][D].
+struct KVSrc {
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* table;   // paged: this sequence's block-table row
     int Hkv, kvh, Tk;
-    int slot_k, slot_v;     // this wavefront's page within a tile, -1 = no rows
 };
 
+// One thread's share of a K/V tile pair in flight: LPT granules of K and of V.
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* pool, const PagedKV& pk,
-                                                            int k0, int slot) {
-    const int p = k0 / 16 + max(slot, 0);
-    const int valid = slot < 0 ? 0 : max(0, min(16, pk.Tk - p * 16));
-    const int bytes = __builtin_amdgcn_readfirstlane(valid * D * 2);
-    const uint16_t* base = pool;
-    if (bytes > 0) {
-        const int phys = __builtin_amdgcn_readfirstlane(pk.table[p]);
-        base = pool + ((size_t)phys * pk.Hkv + pk.kvh) * 16 * D;
-    }
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kRsrcWord3);
-}
+struct Stage {
+    u32x4 k[Cfg<D>::LPT], v[Cfg<D>::LPT];
+};
 
+// Thread tid's granules of a tile: g = tid + 256 j lands at byte 16 g of the
+// LDS tile (row g / GPR, swizzled position g % GPR), so it fetches global
+// granule (g % GPR) ^ swz(row) of that row.  goff is its byte offset within
+// the tile (dense) or within its 16-row page (paged); a wavefront's load j
+// covers rows of one page.
 template <int D>
-__device__ __forceinline__ void load_stage_paged(Stage& st, const PagedKV& pk, int k0k, int k0v,
-                                                 const LoadOffsets<D>& off) {
-    const __amdgpu_buffer_rsrc_t rk = page_rsrc<D>(pk.kpool, pk, k0k, pk.slot_k);
-    const __amdgpu_buffer_rsrc_t rv = page_rsrc<D>(pk.vpool, pk, k0v, pk.slot_v);
-    st.k = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k, 0, 0);
+struct LoadPlan {
+    int goff_k[Cfg<D>::LPT], goff_v[Cfg<D>::LPT];
+    __device__ LoadPlan(int tid, bool paged) {
+        using C = Cfg<D>;
 #pragma unroll
-    for (int j = 0; j < 4; j++) st.v[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, off.v + j * D * 2, 0, 0);
+        for (int j = 0; j < C::LPT; j++) {
+            const int g = tid + kThreads * j, r = g / C::GPR, p = g % C::GPR;
+            const int rr = paged ? (r & 15) : r;
+            goff_k[j] = rr * C::ROW + 16 * (p ^ k_swz<D>(r));
+            goff_v[j] = rr * C::ROW + 16 * (p ^ v_swz<D>(r));
+        }
+    }
+};
+
+// Issue this thread's loads of K tile kt and V tile vt.  Tiles below 0 or
+// past Tk are empty (zero-sized descriptors), so every call issues the same
+// number of loads and none is conditional.
+template <int D, bool PAGED>
+__device__ __forceinline__ void load_pair(Stage<D>& st, const KVSrc& src, const LoadPlan<D>& lp,
+                                          int wave, int kt, int vt) {
+    using C = Cfg<D>;
+#pragma unroll
+    for (int j = 0; j < C::LPT; j++) {
+        const uint16_t* kb;
+        const uint16_t* vb;
+        int kbytes, vbytes;
+        if constexpr (PAGED) {
+            // rows of load j of this wavefront: one 16-token page of the tile
+            const int slot = (kThreads * j + 64 * wave) / C::GPR / 16;
+            auto page = [&](const uint16_t* pool, int t, const uint16_t*& base, int& bytes) {
+                const int p = t * (kBN / 16) + slot;
+                const int valid = t < 0 ? 0 : max(0, min(16, src.Tk - p * 16));
+                base = pool;
+                if (__builtin_amdgcn_readfirstlane(valid) > 0) {
+                    const int phys = __builtin_amdgcn_readfirstlane(src.table[p]);
+                    base = pool + ((size_t)phys * src.Hkv + src.kvh) * 16 * D;
+                }
+                bytes = valid * C::ROW;
+            };
+            page(src.k, kt, kb, kbytes);
+            page(src.v, vt, vb, vbytes);
+        } else {
+            auto rows = [&](int t) { return t < 0 ? 0 : max(0, min(kBN, src.Tk - t * kBN)); };
+            kb = src.k + (size_t)max(kt, 0) * kBN * D;
+            vb = src.v + (size_t)max(vt, 0) * kBN * D;
+            kbytes = rows(kt) * C::ROW;
+            vbytes = rows(vt) * C::ROW;
+        }
+        st.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(kb, kbytes), lp.goff_k[j], 0, 0);
+        st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(vb, vbytes), lp.goff_v[j], 0, 0);
+    }
 }
 
+// Write a staged pair: thread tid's granule j goes to byte 16 (tid + 256 j)
+// of the LDS K and V tiles (1 KiB contiguous per wavefront store).
 template <int D>
-__device__ __forceinline__ void store_stage(const Stage& st, unsigned char* kbuf,
-                                            unsigned char* vbuf, int tid, bool do_k, bool do_v) {
-    using C = Cfg<D>;
-    if (do_k && tid < C::K_CHUNKS) {
-        const int row = tid / C::CPR, ch = tid % C::CPR;
-        *(u32x4*)(kbuf + row * C::K_STRIDE + 16 * ch) = st.k;
+__device__ __forceinline__ void store_pair(const Stage<D>& st, unsigned char LDS_AS* kt,
+                                           unsigned char LDS_AS* vt, int tid) {
+#pragma unroll
+    for (int j = 0; j < Cfg<D>::LPT; j++) {
+        *(u32x4 LDS_AS*)(kt + 16 * (tid + kThreads * j)) = st.k[j];
+        *(u32x4 LDS_AS*)(vt + 16 * (tid + kThreads * j)) = st.v[j];
     }
-    if (do_v && tid < C::V_UNITS) {
-        const int dp = tid % (D / 2), kb4 = tid / (D / 2);
-        // st.v[j] = (dim 2dp, dim 2dp+1) of key 4kb4 + j -> two V^T rows of 4 keys
-        const uint32_t v0 = st.v[0], v1 = st.v[1], v2 = st.v[2], v3 = st.v[3];
-        const uint32_t e01 = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
-        const uint32_t e23 = __builtin_amdgcn_perm(v3, v2, 0x05040100u);
-        const uint32_t o01 = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
-        const uint32_t o23 = __builtin_amdgcn_perm(v3, v2, 0x07060302u);
-        unsigned char* row = vbuf + C::K_BYTES + dp * C::VT_STRIDE + vt_pos(4 * kb4) * 2;
-        *(u32x2*)row = u32x2{e01, e23};                             // dim 2dp: row dp
-        *(u32x2*)(row + (D / 2) * C::VT_STRIDE) = u32x2{o01, o23};  // dim 2dp + 1: row D/2 + dp
-    }
+}
+
+__device__ __forceinline__ bf16x8 tr_read_pair(const unsigned char LDS_AS* p0,
+                                               const unsigned char LDS_AS* p1) {
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)p0);
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)p1);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Workgroup barrier that also orders LDS: this wavefront's LDS accesses are
+// complete and no LDS access moves across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int D, bool CAUSAL, bool PAGED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                          float* __restrict__ lse, int BH, int Hq, int Hkv, int Tq, int Tk_dense,
-                         int n_qtiles, float scale_log2, const int32_t* __restrict__ block_table,
+                         int n_qtiles, int paired, float scale_log2,
+                         const int32_t* __restrict__ block_table,
                          const int32_t* __restrict__ kv_lens, int bt_stride) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF_BYTES];
+    // two K tiles, then two V tiles
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[4 * C::TILE];
+    __shared__ int flags[kWaves];
+    unsigned char LDS_AS* smem = (unsigned char LDS_AS*)smem_raw;
+    unsigned char LDS_AS* const sK[2] = {smem, smem + C::TILE};
+    unsigned char LDS_AS* const sV[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
     const int li = lane & 31, hi = lane >> 5;
-    // Wavefront w runs on SIMD w % 4; group 1 (waves 4-7) runs one phase
-    // behind group 0.  Row blocks alternate between the groups so both see
-    // the same share of the causal diagonal.
-    const int grp = wave >> 2;
-    const int rb = 2 * (wave & 3) + grp;
+    const int rb0 = wave, rb1 = 7 - wave;   // this wavefront's two 32-row blocks
 
-    // Heaviest query tiles first.  Workgroups are dealt to the 8 XCDs
-    // round-robin, so id % 8 picks the XCD: with slot = id % BH, the kv group
-    // kg = slot % (B * Hkv) and the head within the group g = slot / (B * Hkv),
-    // every query tile of every head that reads one kv head's K/V lands on
-    // one XCD (and its L2) when BH and B * Hkv are multiples of 8.  Without
-    // grouped heads this is the identity, slot = b * Hq + h.
+    // Workgroups are dealt to the 8 XCDs round-robin, so id % 8 picks the
+    // XCD.  slot = id % BH: kv group kg = slot % (B * Hkv), head within the
+    // group g = slot / (B * Hkv), so every query tile of every head that reads
+    // one kv head's K/V lands on one XCD when BH and B * Hkv are multiples of
+    // 8 (without grouped heads slot = b * Hq + h).  Paired: unit p = id / BH
+    // holds query tiles p and n - 1 - p; otherwise query tile n - 1 - id / BH.
     const int id = blockIdx.x;
-    const int slot = id % BH;
-    const int qt = n_qtiles - 1 - id / BH;
+    const int slot = id % BH, unit = id / BH;
     const int KG = (BH / Hq) * Hkv;      // (batch, kv head) groups
     const int kg = slot % KG, g_in = slot / KG;
     const int b = kg / Hkv, kvh = kg % Hkv, h = kvh * (Hq / Hkv) + g_in;
     const int bh = b * Hq + h;
-    const int q0 = qt * kBM;
-    const int qw0 = q0 + rb * 32;        // this wavefront's first row
-    const int qrow = qw0 + li;           // the query row of this lane
     // paged: the sequence's own key count (its chunk of Tq queries is its
     // last Tq positions, so the causal diagonal sits at kv_len - Tq), clamped
     // to what its block-table row can map so no page index leaves the row
@@ -237,224 +247,378 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int diag = Tk - Tq;
 
     const uint16_t* qp = q + (size_t)bh * Tq * D;
-    const uint16_t* kp = PAGED ? k : k + (size_t)(b * Hkv + kvh) * Tk * D;
-    const uint16_t* vp = PAGED ? v : v + (size_t)(b * Hkv + kvh) * Tk * D;
+    KVSrc src;
+    src.k = PAGED ? k : k + (size_t)(b * Hkv + kvh) * Tk * D;
+    src.v = PAGED ? v : v + (size_t)(b * Hkv + kvh) * Tk * D;
+    src.table = PAGED ? block_table + (size_t)b * bt_stride : nullptr;
+    src.Hkv = Hkv;
+    src.kvh = kvh;
+    src.Tk = Tk;
+    const LoadPlan<D> lp(tid, PAGED);
 
-    // Q fragments (B operand of S^T = K Q^T): row qrow, dims 16s + 8hi .. +7.
-    // Loaded unconditionally (clamped row, zeroed past Tq) so that no
-    // exec-masked load is pending when the main loop starts.
-    bf16x8 qf[C::KS];
+    // Per-lane LDS offsets of the MFMA operands within a K or V tile.
+    // K (A of S^T = K Q^T): row li, dims 16s + 8hi .. +7.  V^T (A of
+    // O^T = V^T P^T) via transposing reads: within each 16-lane group g, lane
+    // j addresses key row kbase + j/4 and 4 dims; lane i then holds dims d(i)
+    // of keys kbase .. kbase + 3.  The dims are chosen so that O^T register r
+    // of lane l is dim 32db + 16(r/8) + 8hi + r%8, which makes the epilogue's
+    // stores 16 contiguous bytes.
+    int koff[C::KS], voff[C::DB];
+#pragma unroll
+    for (int s = 0; s < C::KS; s++) koff[s] = li * C::ROW + 16 * ((2 * s + hi) ^ k_swz<D>(li));
     {
-        const int qr = min(qrow, max(Tq - 1, 0));
+        const int g = lane >> 4, j = lane & 15;
+        const int vx = D == 128 ? (j >> 2) : ((j >> 3) & 1);    // v_swz(row) / 4
 #pragma unroll
-        for (int s = 0; s < C::KS; s++) {
-            u32x4 w = *(const u32x4*)(qp + (size_t)qr * D + 16 * s + 8 * hi);
-            if (qrow >= Tq) w = u32x4{0, 0, 0, 0};
-            qf[s] = __builtin_bit_cast(bf16x8, w);
-        }
+        for (int db = 0; db < C::DB; db++)
+            voff[db] = (4 * (g >> 1) + (j >> 2)) * C::ROW + 16 * (2 * (g & 1) + (j & 1)) +
+                       64 * (db ^ vx) + 8 * ((j >> 1) & 1);
     }
 
-    // key range of the workgroup and of this wavefront
-    int kend = Tk, kend_w = Tk;
-    if (CAUSAL) {
-        kend = max(0, min(Tk, q0 + kBM + diag));
-        kend_w = max(0, min(Tk, qw0 + 32 + diag));
-    }
-    const int n_tiles = (kend + kBN - 1) / kBN;
-    const int n_tiles_w = (kend_w + kBN - 1) / kBN;   // tiles with a visible key for this wavefront
-
-    f32x16 oacc[C::DB];
-#pragma unroll
-    for (int db = 0; db < C::DB; db++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) oacc[db][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16 sacc;
-    bf16x8 pf[2];
-
-    // Global phase p: group 0 runs its MFMA step t at p = 2t and its softmax
-    // step t at p = 2t + 1; group 1 runs each one phase later.  K(t) lives in
-    // buffer t % 2 during phases 2t and 2t+1 (the two groups' S(t)); V(t)
-    // lives in buffer t % 2 during phases 2t+2 and 2t+3 (their PV(t)).  The
-    // pair (K(t+1), V(t)) is loaded into register stage t % 2 at the start of
-    // phase 2t - 2 and written to LDS at the end of phase 2t + 1, so every
-    // load has four phases to arrive.
-    // PV at t = 0 multiplies P = 0 with the V region of buffer 1: zero both so
-    // that it adds exact zeros.
-    pf[0] = pf[1] = bf16x8{};
-    for (int i = tid; i < C::V_BYTES / 16; i += kThreads)
-        *(u32x4*)(smem + C::BUF_BYTES + C::K_BYTES + 16 * i) = u32x4{0, 0, 0, 0};
-    LoadOffsets<D> off(tid);
-    PagedKV pk{};
-    if constexpr (PAGED) {
-        // first K row / V key of this wavefront's share of a tile
-        const int rowk = (wave * 64) / C::CPR, rowv = 4 * ((wave * 64) / (D / 2));
-        pk = PagedKV{kp, vp, block_table + (size_t)b * bt_stride, Hkv, kvh, Tk,
-                     rowk < kBN ? rowk / 16 : -1, rowv < kBN ? rowv / 16 : -1};
-        off.k -= max(pk.slot_k, 0) * 16 * D * 2;   // offsets within the page
-        off.v -= max(pk.slot_v, 0) * 16 * D * 2;
-    }
-    Stage st0, st1;
-    auto load_pair = [&](Stage& st, int t) {  // K(t+1), V(t)
-        if constexpr (PAGED) load_stage_paged<D>(st, pk, (t + 1) * kBN, t * kBN, off);
-        else load_stage<D>(st, kp, vp, (t + 1) * kBN, t * kBN, Tk, off);
+    const int n_my = paired ? ((n_qtiles - 1 - unit) == unit ? 1 : 2) : 1;
+    auto tile_of = [&](int u) {
+        return paired ? (u == 0 ? unit : n_qtiles - 1 - unit) : n_qtiles - 1 - unit;
     };
-    auto store_pair = [&](const Stage& st, int t) {
-        if (t < n_tiles)
-            store_stage<D>(st, smem + ((t + 1) & 1) * C::BUF_BYTES, smem + (t & 1) * C::BUF_BYTES,
-                           tid, t + 1 < n_tiles, true);
+    // Q fragments (B operand of S^T = K Q^T) of the current query tile: row
+    // qrow, dims 16s + 8hi .. +7, loaded unconditionally (clamped row, zeroed
+    // past Tq).  pro0 / pro1 / stg[0]: the first K/V tiles of a pass (K(0),
+    // K(1), then K(2) with V(0)), loaded ahead of it.
+    bf16x8 qf[2][C::KS];
+    Stage<D> pro0, pro1, stg[2];
+    auto issue_kv_head = [&]() {
+        load_pair<D, PAGED>(pro0, src, lp, wave, 0, -1);
+        load_pair<D, PAGED>(pro1, src, lp, wave, 1, -1);
+        load_pair<D, PAGED>(stg[0], src, lp, wave, 2, 0);
     };
-    if (n_tiles > 0) {
-        if constexpr (PAGED) load_stage_paged<D>(st0, pk, 0, 0, off);
-        else load_stage<D>(st0, kp, vp, 0, 0, Tk, off);
-        store_stage<D>(st0, smem, smem, tid, true, false);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // Q and the first K tile have landed
-    load_pair(st0, 0);
-    __syncthreads();
-
-    // One step t of group G: its MFMA phase, then its softmax phase.  Every
-    // global load is unconditional, so the wait before each LDS store covers
-    // only the stage being stored, not the loads issued after it.
-    // cur = stage t % 2 (pair t), nxt = stage (t + 1) % 2 (pair t + 1).
-    auto step = [&](int t, Stage& cur, Stage& nxt, auto G) {
-        constexpr int g = decltype(G)::value;
-        // ---- MFMA step t (phase 2t for group 0, 2t+1 for group 1):
-        //      O^T += V^T P^T for tile t-1 and S^T = K Q^T for tile t.
-        if (g == 0) load_pair(nxt, t + 1);
-        if (t <= n_tiles_w) {
-            // All 16 LDS operands are requested first, V and K alternating in
-            // the order the MFMAs consume them; PV(t-1) and S(t) MFMAs then
-            // alternate too, so each waits only for its own operand and the S
-            // chain's dependences are covered by PV MFMAs.  At t = 0 PV adds
-            // P = 0 times the zeroed V buffer; at t = n_tiles_w S is computed
-            // and not used.
-            bf16x8 vf[C::KS], kf[C::KS];
-            const unsigned char* sV = smem + ((t - 1) & 1) * C::BUF_BYTES + C::K_BYTES +
-                                      li * C::VT_STRIDE + 16 * hi;
-            const unsigned char* sK = smem + (t & 1) * C::BUF_BYTES + li * C::K_STRIDE + 16 * hi;
+    auto issue_tile = [&](int u) {
+        const int q0u = tile_of(u) * kBM;
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const int qrow = q0u + 32 * (a ? rb1 : rb0) + li;
+            const int qr = min(qrow, max(Tq - 1, 0));
 #pragma unroll
             for (int s = 0; s < C::KS; s++) {
-                // V^T rows 32db + li; keys key(hi, 0..7) of step ps at positions 16ps + 8hi
-                const int ps = s / C::DB, db = s % C::DB;
-                vf[s] = *(const bf16x8*)(sV + 32 * db * C::VT_STRIDE + 32 * ps);
-                kf[s] = *(const bf16x8*)(sK + 32 * s);
+                u32x4 w = *(const u32x4*)(qp + (size_t)qr * D + 16 * s + 8 * hi);
+                if (qrow >= Tq) w = u32x4{0, 0, 0, 0};
+                qf[a][s] = __builtin_bit_cast(bf16x8, w);
             }
+        }
+        issue_kv_head();
+    };
+    issue_tile(0);
+    for (int u = 0; u < n_my; u++) {
+        const int qt = tile_of(u);
+        const int q0 = qt * kBM;
+        const int qa0 = q0 + 32 * rb0, qa1 = q0 + 32 * rb1;     // first rows of the blocks
+        const int qrow0 = qa0 + li, qrow1 = qa1 + li;
+
+        // key tiles of the query tile (the later block's range bounds both)
+        const int kend = CAUSAL ? max(0, min(Tk, q0 + kBM + diag)) : Tk;
+        const int n = (kend + kBN - 1) / kBN;
+        // first tile that needs a mask for either block: the one holding key
+        // Tk (partial tile) or, causal, the first key past the earlier block's
+        // first row
+        const int t_mask = CAUSAL ? max(0, min(Tk, qa0 + diag + 1)) / kBN : Tk / kBN;
+        // per-block last visible key of this lane's row
+        const int lim0 = CAUSAL ? min(Tk - 1, qrow0 + diag) : Tk - 1;
+        const int lim1 = CAUSAL ? min(Tk - 1, qrow1 + diag) : Tk - 1;
+
+        f32x16 oacc[2][C::DB];
+        float m_ref[2], l_run[2];
+        f32x16 sacc[2][2];      // [parity][block]
+        bf16x8 pf[2][2][2];     // [parity][block][16-key step]; pf[1] starts as P(-1) = 0
+
+        // S^T(t) for both blocks from K tile t (LDS stage t % 2) into sacc[t % 2]
+        auto s_mfma = [&](auto PAR) {
+            constexpr int P = decltype(PAR)::value;
+            const unsigned char LDS_AS* sk = sK[P];
 #pragma unroll
             for (int s = 0; s < C::KS; s++) {
-                const int ps = s / C::DB, db = s % C::DB;
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], pf[ps], oacc[db], 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], s == 0 ? f32x16{} : sacc,
-                                                               0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::KS, 0);  // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::KS, 0);  // then MFMAs
-        }
-        if (g == 1) store_pair(cur, t);
-        __syncthreads();
-
-        // ---- softmax step t (phase 2t+1 for group 0, 2t+2 for group 1)
-        if (g == 1) load_pair(cur, t + 2);
-        if (t < n_tiles_w) {
-            const int k0 = t * kBN;
-            // sacc[r] is the score of key k0 + 8(r/4) + 4hi + r%4
-            if (k0 + kBN > Tk || (CAUSAL && k0 + kBN - 1 > qw0 + diag)) {
+                const bf16x8 kf = *(const bf16x8 LDS_AS*)(sk + koff[s]);
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int kj = k0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if (kj >= Tk || (CAUSAL && kj > qrow + diag)) sacc[r] = -INFINITY;
+                for (int a = 0; a < 2; a++)
+                    sacc[P][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        kf, qf[a][s], s == 0 ? f32x16{} : sacc[P][a], 0, 0, 0);
+            }
+        };
+        // mask the scores of tile t: key k0 + 4hi + e (e = 8(r/4) + r%4) is
+        // visible iff e <= the lane's last visible key - k0 - 4hi
+        int t_cur = 0;   // tile whose scores the mask applies to
+        auto mask_tile = [&](f32x16& x, int a) {
+            const int lim = (a ? lim1 : lim0) - t_cur * kBN - 4 * hi;
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (8 * (r >> 2) + (r & 3) > lim) x[r] = -INFINITY;
+        };
+        auto row_max = [&](const f32x16& x) {
+            float a0 = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), x[2]);
+            float a1 = __builtin_fmaxf(__builtin_fmaxf(x[3], x[4]), x[5]);
+            float a2 = __builtin_fmaxf(__builtin_fmaxf(x[6], x[7]), x[8]);
+            float a3 = __builtin_fmaxf(__builtin_fmaxf(x[9], x[10]), x[11]);
+            float a4 = __builtin_fmaxf(__builtin_fmaxf(x[12], x[13]), x[14]);
+            a0 = __builtin_fmaxf(__builtin_fmaxf(a0, a1), a2);
+            a3 = __builtin_fmaxf(__builtin_fmaxf(a3, a4), x[15]);
+            const float m = half_swap_max(__builtin_fmaxf(a0, a3));
+            return (m == -INFINITY) ? -INFINITY : m * scale_log2;
+        };
+        // One step as a fixed sequence of NS slots (a scheduling barrier after
+        // each, so the compiler keeps the order): slot i issues one MFMA (S and
+        // PV alternate, so each S MFMA's dependence on the previous one of its
+        // chain is four slots back), one stage of the softmax (the fma of
+        // score i, the exp2 of score i - 1, and every second slot the bf16 pack
+        // and row sum of the pair before), and the LDS reads of the operands
+        // needed LA slots later.  MFMA and VALU work share the SIMD's issue
+        // capacity, so a steady mix keeps both busy.
+        constexpr int NS = 4 * C::KS;       // MFMAs per step (2 KS for S, 2 KS for PV)
+        constexpr int SPS = 32 / NS;        // softmax scores per slot
+        constexpr int LA = 6;               // read lookahead in slots
+        auto step_body = [&](auto PAR, auto MASK, auto FIRST) -> bool {
+            constexpr int P = decltype(PAR)::value, NP = P ^ 1;
+            const unsigned char LDS_AS* sk = sK[NP];
+            const unsigned char LDS_AS* sv = sV[NP];
+            bool big = false;
+            float m_eff[2];
+            int limt[2];   // masked steps: register r of block a is visible iff 8(r/4) + r%4 <= limt[a]
+#pragma unroll
+            for (int a = 0; a < 2; a++) {
+                limt[a] = (a ? lim1 : lim0) - t_cur * kBN - 4 * hi;
+                if constexpr (decltype(FIRST)::value) {
+                    mask_tile(sacc[P][a], a);
+                    m_ref[a] = row_max(sacc[P][a]);
                 }
+                m_eff[a] = (m_ref[a] == -INFINITY) ? 0.f : m_ref[a];
             }
-            float mx;
-            {   // max tree of depth 4 (v_max3)
-                float t0 = __builtin_fmaxf(__builtin_fmaxf(sacc[0], sacc[1]), sacc[2]);
-                float t1 = __builtin_fmaxf(__builtin_fmaxf(sacc[3], sacc[4]), sacc[5]);
-                float t2 = __builtin_fmaxf(__builtin_fmaxf(sacc[6], sacc[7]), sacc[8]);
-                float t3 = __builtin_fmaxf(__builtin_fmaxf(sacc[9], sacc[10]), sacc[11]);
-                float t4 = __builtin_fmaxf(__builtin_fmaxf(sacc[12], sacc[13]), sacc[14]);
-                t0 = __builtin_fmaxf(__builtin_fmaxf(t0, t1), t2);
-                t3 = __builtin_fmaxf(__builtin_fmaxf(t3, t4), sacc[15]);
-                mx = half_swap_max(__builtin_fmaxf(t0, t3));
-            }
-            mx = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
-            const float m_new = fmaxf(m_run, mx);
-            if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThresh)) {
-                const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-                l_run *= alpha;
+            // slot of the MFMA that first uses K fragment s / V fragment (ps, db)
+            auto k_slot = [](int s2) { return 4 * s2; };
+            auto v_slot = [](int ps, int db) { return 4 * (C::DB * ps + db) + 1; };
+            bf16x8 kf[C::KS], vf[2][C::DB];
+            auto read_k = [&](int s2) { kf[s2] = *(const bf16x8 LDS_AS*)(sk + koff[s2]); };
+            auto read_v = [&](int ps, int db) {
+                const unsigned char LDS_AS* a0 = sv + 16 * ps * C::ROW + voff[db];
+                vf[ps][db] = tr_read_pair(a0, a0 + 8 * C::ROW);
+            };
+            // reads needed before slot LA
 #pragma unroll
-                for (int db = 0; db < C::DB; db++) oacc[db] *= alpha;
-                m_run = m_new;
-            }
-            const float m_eff = (m_run == -INFINITY) ? 0.f : m_run;
-            float l0 = l_run, l1 = 0.f;   // two row-sum chains
+            for (int s2 = 0; s2 < C::KS; s2++)
+                if (k_slot(s2) < LA) read_k(s2);
 #pragma unroll
-            for (int ps = 0; ps < 2; ps++) {
-                uint32_t w[4];
+            for (int ps = 0; ps < 2; ps++)
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const float p0 = fast_exp2(__builtin_fmaf(sacc[8 * ps + 2 * e], scale_log2, -m_eff));
-                    const float p1 = fast_exp2(__builtin_fmaf(sacc[8 * ps + 2 * e + 1], scale_log2, -m_eff));
-                    w[e] = pack_bf16x2(p0, p1);
-                    float& acc = (e & 1) ? l1 : l0;
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]),
-                                                          __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+                for (int db = 0; db < C::DB; db++)
+                    if (v_slot(ps, db) < LA) read_v(ps, db);
+            float pe[32];                      // exp2 results awaiting their pack
+            float lsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+            uint32_t pw[2][2][4];
+            auto sm_fma = [&](int j) {         // score j: block j / 16, register j % 16
+                const int a = j >> 4, r = j & 15;
+                const float y = __builtin_fmaf(sacc[P][a][r], scale_log2, -m_eff[a]);
+                pe[j] = (decltype(MASK)::value && 8 * (r >> 2) + (r & 3) > limt[a]) ? -INFINITY : y;
+            };
+            auto sm_exp = [&](int j) { pe[j] = fast_exp2(pe[j]); };
+            auto sm_pack = [&](int j) {        // pair (j, j + 1), j even
+                const int a = j >> 4, r = j & 15, ps = r >> 3, e = (r & 7) >> 1;
+                const uint32_t w = pack_bf16x2(pe[j], pe[j + 1]);
+                pw[a][ps][e] = w;
+                float& acc = lsum[a][e & 1];
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                                      __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+            };
+#pragma unroll
+            for (int i = 0; i < NS; i++) {
+                if (i % 2 == 0) {   // S MFMA: k-step s of block a
+                    const int s2 = i / 4, a = (i / 2) % 2;
+                    sacc[NP][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        kf[s2], qf[a][s2], s2 == 0 ? f32x16{} : sacc[NP][a], 0, 0, 0);
+                } else {            // PV MFMA: 16-key step ps, dim block db, block a
+                    const int k2 = i / 2, ps = k2 / (2 * C::DB), db = (k2 / 2) % C::DB, a = k2 % 2;
+                    oacc[a][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        vf[ps][db], pf[NP][a][ps], oacc[a][db], 0, 0, 0);
                 }
-                pf[ps] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+#pragma unroll
+                for (int q2 = 0; q2 < SPS; q2++) {
+                    const int j = i * SPS + q2;
+                    sm_fma(j);
+                    if (j >= 1) sm_exp(j - 1);
+                    if (j >= 3 && (j & 1)) sm_pack(j - 3);
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < C::KS; s2++)
+                    if (k_slot(s2) == i + LA) read_k(s2);
+#pragma unroll
+                for (int ps = 0; ps < 2; ps++)
+#pragma unroll
+                    for (int db = 0; db < C::DB; db++)
+                        if (v_slot(ps, db) == i + LA) read_v(ps, db);
             }
-            l_run = l0 + l1;
-        }
-        if (g == 0) store_pair(cur, t);
-        __syncthreads();
-    };
-    // The two groups run separate copies of the loop (the branch on grp is
-    // wave-uniform); both pass the same number of barriers.
-    // Steps run t = 0 .. n_tiles; the loop takes them in pairs (the stages
-    // swap roles) and an odd last step runs after it, so that inside the
-    // loop both steps are unconditional and the waits stay exact.
-    if (grp == 0) {
-        const std::integral_constant<int, 0> G0;
-        int t = 0;
-        for (; t + 1 <= n_tiles; t += 2) {
-            step(t, st0, st1, G0);
-            step(t + 1, st1, st0, G0);
-        }
-        if (t == n_tiles) step(t, st0, st1, G0);
-        __syncthreads();  // group 1's last phase
-    } else {
-        const std::integral_constant<int, 1> G1;
-        load_pair(st1, 1);  // phase 0: group 0 computes S(0); group 1 only loads
-        __syncthreads();
-        int t = 0;
-        for (; t + 1 <= n_tiles; t += 2) {
-            step(t, st0, st1, G1);
-            step(t + 1, st1, st0, G1);
-        }
-        if (t == n_tiles) step(t, st0, st1, G1);
-    }
+            __builtin_amdgcn_iglp_opt(3);
+            // the slots packed pairs 0 .. 28 (slot j packs pair j - 3); pair 30 remains
+            sm_exp(31);
+            sm_pack(30);
+#pragma unroll
+            for (int a = 0; a < 2; a++) {
+#pragma unroll
+                for (int ps = 0; ps < 2; ps++)
+                    pf[P][a][ps] = __builtin_bit_cast(bf16x8, u32x4{pw[a][ps][0], pw[a][ps][1],
+                                                                   pw[a][ps][2], pw[a][ps][3]});
+                const float lt = lsum[a][0] + lsum[a][1];
+                l_run[a] += lt;
+                big |= !(lt <= 1048576.f);   // also catches inf and NaN sums
+            }
+            return __builtin_amdgcn_ballot_w64(big) != 0;
+        };
 
-    // ---- epilogue: O = O / l, lse = m ln2 + ln l ----------------------------
-    const float l_tot = half_swap_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < Tq) {
-        // O^T row p = 32 db + 8 g + 4 hi + j holds dimension 2p (p < D/2) or
-        // 2(p - D/2) + 1: rows p of block db and p + D/2 of block db + DB/2
-        // give dimensions 2p and 2p + 1, so 4 rows make 16 contiguous bytes.
-        uint16_t* op = o + ((size_t)bh * Tq + qrow) * D;
+        // One pass over the key tiles.  Step t: S(t+1), softmax(t), PV(t-1);
+        // pair t (K(t+2), V(t)) goes from registers to LDS and pair t + 1 is
+        // loaded.  LDS: S(t+1) reads K stage (t+1)%2, PV(t-1) reads V stage
+        // (t-1)%2; the stores go to stages t%2, last read in step t-1.  Every
+        // step runs all three jobs: PV(-1) multiplies P = 0 with the zeroed V
+        // stage 1, S(n) and S(n+1) read tiles past the key range (zeros) and
+        // are not used, and the softmax of step n sees only masked keys (P = 0).
+        // Steps from t_mask on apply the mask.  GIVEN: m_ref holds the exact
+        // row maxima (the recompute pass), else it is taken from tile 0.
+        // Returns whether any wavefront saw a too-low reference.
+        auto pass = [&](auto GIVEN) -> bool {
+            constexpr bool G = decltype(GIVEN)::value;
+            const std::integral_constant<bool, true> Y;
+            const std::integral_constant<bool, false> N;
+            const std::integral_constant<int, 0> P0;
+            const std::integral_constant<int, 1> P1;
 #pragma unroll
-        for (int db = 0; db < C::DB / 2; db++)
+            for (int a = 0; a < 2; a++) {
+                l_run[a] = 0.f;
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int p0 = 32 * db + 8 * g + 4 * hi;
-                constexpr int H = C::DB / 2;
-                uint32_t w[4];
+                for (int db = 0; db < C::DB; db++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
-                    w[j] = pack_bf16x2(oacc[db][4 * g + j] * inv, oacc[db + H][4 * g + j] * inv);
-                *(u32x4*)(op + 2 * p0) = u32x4{w[0], w[1], w[2], w[3]};
+                    for (int r = 0; r < 16; r++) oacc[a][db][r] = 0.f;
+#pragma unroll
+                for (int ps = 0; ps < 2; ps++) pf[1][a][ps] = bf16x8{};
             }
-        if (lse && hi == 0)
-            lse[(size_t)bh * Tq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+            bool flag = false;
+            auto step = [&](int t, auto PAR, auto MASK, auto FIRST) {
+                constexpr int P = decltype(PAR)::value;          // t % 2
+                load_pair<D, PAGED>(stg[P ^ 1], src, lp, wave, t + 3, t + 1);
+                t_cur = t;
+                const bool big = step_body(PAR, MASK, FIRST);
+                if constexpr (!G) flag |= big;
+                store_pair<D>(stg[P], sK[P], sV[P], tid);
+                lds_barrier();
+            };
+            // prologue (its loads were issued ahead): K(0) and K(1) into LDS,
+            // zeros into V stage 1, pair 0 (K(2), V(0)) in flight; then S(0)
+            store_pair<D>(pro0, sK[0], sV[1], tid);
+            store_pair<D>(pro1, sK[1], sV[1], tid);
+            lds_barrier();
+            s_mfma(P0);
+            lds_barrier();                    // K stage 0 is rewritten in step 0
+            // Step 0 (masked, which is exact for any tile), then pairs of steps
+            // (t odd, t + 1) so that the register sets keep their roles:
+            // unmasked pairs while both steps precede t_mask, then masked pairs
+            // up to step n (masking a tile that needs none, or running a step
+            // past n, changes nothing).
+            step(0, P0, Y, std::integral_constant<bool, !G>{});
+            int t = 1;
+            for (; t + 2 <= t_mask; t += 2) {
+                step(t, P1, N, N);
+                step(t + 1, P0, N, N);
+            }
+            for (; t <= n; t += 2) {
+                step(t, P1, Y, N);
+                step(t + 1, P0, Y, N);
+            }
+            return flag;
+        };
+
+        if (n > 0) {
+            bool flag = pass(std::integral_constant<bool, false>{});
+            // any wavefront's flag makes the whole workgroup recompute
+            if (lane == 0) flags[wave] = flag;
+            lds_barrier();
+            flag = flags[0] | flags[1] | flags[2] | flags[3];
+            lds_barrier();
+            if (flag) {
+                // exact row maxima over every visible key, then the same pass
+                // against them (every P <= 1)
+                m_ref[0] = m_ref[1] = -INFINITY;
+                for (int t = 0; t < n; t++) {
+                    Stage<D> s0;
+                    load_pair<D, PAGED>(s0, src, lp, wave, t, -1);
+                    store_pair<D>(s0, sK[0], sV[1], tid);
+                    lds_barrier();
+                    s_mfma(std::integral_constant<int, 0>{});
+#pragma unroll
+                    for (int a = 0; a < 2; a++) {
+                        t_cur = t;
+                        mask_tile(sacc[0][a], a);
+                        m_ref[a] = fmaxf(m_ref[a], row_max(sacc[0][a]));
+                    }
+                    lds_barrier();
+                }
+                issue_kv_head();
+                pass(std::integral_constant<bool, true>{});
+            }
+        } else {
+            m_ref[0] = m_ref[1] = -INFINITY;
+            l_run[0] = l_run[1] = 0.f;
+#pragma unroll
+            for (int a = 0; a < 2; a++)
+#pragma unroll
+                for (int db = 0; db < C::DB; db++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) oacc[a][db][r] = 0.f;
+        }
+
+        // the next query tile's Q and first K/V tiles load during this epilogue
+        if (u + 1 < n_my) issue_tile(u + 1);
+
+        // ---- epilogue: O = O / l, lse = m ln2 + ln l ------------------------
+#pragma unroll
+        for (int a = 0; a < 2; a++) {
+            const int qrow = a ? qrow1 : qrow0;
+            const float l_tot = half_swap_sum(l_run[a]);
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            if (qrow < Tq) {
+                uint16_t* op = o + ((size_t)bh * Tq + qrow) * D;
+#pragma unroll
+                for (int db = 0; db < C::DB; db++)
+#pragma unroll
+                    for (int jj = 0; jj < 2; jj++) {
+                        uint32_t w[4];
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            w[e] = pack_bf16x2(oacc[a][db][8 * jj + 2 * e] * inv,
+                                               oacc[a][db][8 * jj + 2 * e + 1] * inv);
+                        *(u32x4*)(op + 32 * db + 16 * jj + 8 * hi) = u32x4{w[0], w[1], w[2], w[3]};
+                    }
+                if (lse && hi == 0)
+                    lse[(size_t)bh * Tq + qrow] =
+                        l_tot > 0.f ? (m_ref[a] + __log2f(l_tot)) * kLn2 : -INFINITY;
+            }
+        }
+        // the next query tile's prologue rewrites every stage
+        lds_barrier();
     }
+}
+
+// CU count of the current device, read once per device.
+int device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Pair query tiles p and n - 1 - p in one workgroup when that still leaves
+// at least one workgroup per CU.
+void grid_of(int BH, int n_qtiles, dim3* grid, int* paired) {
+    *paired = (long)BH * n_qtiles >= 2L * device_cus() && n_qtiles >= 2;
+    *grid = dim3(BH * (*paired ? (n_qtiles + 1) / 2 : n_qtiles));
 }
 
 }  // namespace
@@ -464,12 +628,14 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                bool causal, float scale, hipStream_t stream) {
     const int BH = B * Hq;
     const int n_qtiles = (Tq + kBM - 1) / kBM;
-    const dim3 grid(BH * n_qtiles);
+    dim3 grid;
+    int paired;
+    grid_of(BH, n_qtiles, &grid, &paired);
     const float sl2 = scale * kLog2e;
     auto go = [&](auto kern) {
         kern<<<grid, kThreads, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k,
                                             (const uint16_t*)v, (uint16_t*)o, lse, BH, Hq, Hkv,
-                                            Tq, Tk, n_qtiles, sl2, nullptr, nullptr, 0);
+                                            Tq, Tk, n_qtiles, paired, sl2, nullptr, nullptr, 0);
     };
     if (D == 64)
         causal ? go(prefill_bf16_kernel<64, true, false>) : go(prefill_bf16_kernel<64, false, false>);
@@ -484,12 +650,14 @@ hipError_t launch_prefill_paged_bf16(const void* q, const void* k_pages, const v
                                      int bt_stride, bool causal, float scale, hipStream_t stream) {
     const int BH = B * Hq;
     const int n_qtiles = (Tq + kBM - 1) / kBM;
-    const dim3 grid(BH * n_qtiles);
+    dim3 grid;
+    int paired;
+    grid_of(BH, n_qtiles, &grid, &paired);
     const float sl2 = scale * kLog2e;
     auto go = [&](auto kern) {
         kern<<<grid, kThreads, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k_pages,
                                             (const uint16_t*)v_pages, (uint16_t*)o, lse, BH, Hq,
-                                            Hkv, Tq, 0, n_qtiles, sl2, block_table, kv_lens,
+                                            Hkv, Tq, 0, n_qtiles, paired, sl2, block_table, kv_lens,
                                             bt_stride);
     };
     if (D == 64)

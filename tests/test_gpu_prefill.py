@@ -178,3 +178,25 @@ def test_prefill_long_sequence_sampled_rows(causal):
                                       inp["v"][:, kvh:kvh + 1, :n], False, inp["scale"])
             assert_close(o[0, h, i], ro[0, 0, 0], "bf16", f"O (h={h}, row {i})")
             assert_close(lse[0, h, i:i + 1], rl[0, 0], "bf16", f"lse (h={h}, row {i})")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_late_dominant_key_bf16(causal, D):
+    """The bf16 kernel takes each row's exponent reference from its first key
+    tile; a key later in the sequence whose score is far above that reference
+    (here key 700, scores 23 to 32 above the others) makes the kernel recompute
+    the query tile against the exact row maxima.  Rows that see the key, rows
+    that do not (causal rows before 700), and tiles without it must all match
+    the oracle."""
+    require_gpu()
+    B, H, T = 1, 2, 1000
+    inp = wl.prefill_inputs(B, H, H, T, T, D, "bf16", 90 + D + int(causal))
+    kf = wl.bf16_to_f32(inp["k"])
+    qf = wl.bf16_to_f32(inp["q"])
+    kf[0, :, 700] = 0.0
+    kf[0, :, 700, 0] = 16.0                # key 700 = 16 e_0
+    qf[0, :, 300:, 0] = 16.0               # rows 300..: score 256 / sqrt(D) on it,
+    #                                        over 30 log2 units above the rest
+    inp["k"], inp["q"] = wl.bf16_bits(kf), wl.bf16_bits(qf)
+    check(inp, causal)

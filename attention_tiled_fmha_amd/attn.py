@@ -42,7 +42,11 @@ SIGNATURES = {
     "attn_flat_gemm_plan": (_i, [_i, _i, _i, _i, _vp, _ip, _ip]),
     "attn_flat_gemm_workspace_bytes": (_sz, [_i, _i, _i, _vp]),
     "attn_flat_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
+    "attn_decode_paged_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                       _i, _i, _i, _i, _f, _vp]),
 }
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class AttnError(RuntimeError):
@@ -228,6 +232,39 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse=None, ma
         B, Hq, Hkv, D, page, block_table.shape[1], int(max_kv_len), dt, _dtype(o),
         float(scale), _p(workspace), ws_bytes, _stream(stream), ctypes.byref(opts)),
         "attn_decode_paged")
+
+
+def attn_decode_paged_noalloc(q, k_pages, v_pages, block_table, kv_lens, o, lse=None,
+                              max_kv_len=None, scale=None, stream=None):
+    """attn_decode_paged without a workspace: the split partials go to the
+    library's fixed device array (NOALLOC_SCRATCH_BYTES per GPU; larger plans
+    raise AttnError with ATTN_E_SCRATCH).  Calls that overlap on one GPU
+    share that array and race."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"),
+                 (block_table, "block_table"), (kv_lens, "kv_lens"), (o, "o")):
+        _dense(t, n)
+    if max_kv_len is None:
+        raise ValueError("max_kv_len (host-side bound of kv_lens) is required")
+    B, Hq, D = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    if o.shape != q.shape or v_pages.shape != k_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if block_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
+        raise TypeError("block_table and kv_lens must be int32")
+    if block_table.shape[0] != B or kv_lens.shape != (B,):
+        raise ValueError("block_table / kv_lens shape mismatch")
+    if lse is not None:
+        _dense(lse, "lse")
+        if lse.shape != (B, Hq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, Hq]")
+    dt = _dtype(q)
+    if not (_dtype(k_pages) == _dtype(v_pages) == dt):
+        raise TypeError("q and the pages must share one element type")
+    scale = D ** -0.5 if scale is None else scale
+    _check(load().attn_decode_paged_noalloc(
+        _p(q), _p(k_pages), _p(v_pages), _p(block_table), _p(kv_lens), _p(o), _p(lse),
+        B, Hq, Hkv, D, page, block_table.shape[1], int(max_kv_len), dt, _dtype(o),
+        float(scale), _stream(stream)), "attn_decode_paged_noalloc")
 
 
 def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, kv_lens, o,

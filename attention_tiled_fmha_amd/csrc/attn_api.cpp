@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -59,6 +60,31 @@ size_t decode_ws_bytes(int batch, int heads_q, int head_dim, int max_splits) {
 }
 
 int check_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+// The device scratch of attn_decode_paged_noalloc: the split partials of one
+// call, in a fixed array that each GPU the library runs on holds until the
+// process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: the array is reached only through the per-device address
+// that hipGetSymbolAddress returns (taken once per device, with that device
+// current).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// Address of the current device's scratch array, or NULL on error.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
 
 // Flat GEMM planning, from sweeps of (rows, wavefronts, k slices) over the
 // four decode projections of a Llama2-7B layer (n x k = 12288 x 4096,
@@ -155,7 +181,8 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
                   int head_dim, int page_size, int max_pages_per_seq, int max_kv_len, int dtype,
                   int o_dtype, float scale, void* workspace, size_t workspace_bytes,
                   void* stream, int requested_split, bool unified = false, float phi = 0.f,
-                  int* fallback_count = nullptr, float k_scale = 1.f, float v_scale = 1.f) {
+                  int* fallback_count = nullptr, float k_scale = 1.f, float v_scale = 1.f,
+                  bool use_scratch = false) {
     // dtype ATTN_FP8_E4M3: bf16 queries over an FP8 cache (matrix-core kernel only)
     const bool fp8 = dtype == ATTN_FP8_E4M3;
     if ((!fp8 && !dtype_ok(dtype)) || !dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
@@ -178,6 +205,11 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
     const int rc = plan(batch, heads_kv, max_kv_len, kPlanCUs, requested_split, &split, &max_splits);
     if (rc != ATTN_OK) return rc;
     const size_t need = decode_ws_bytes(batch, heads_q, head_dim, max_splits);
+    if (use_scratch && need > 0) {   // attn_decode_paged_noalloc
+        if (need > kScratchBytes) return ATTN_E_SCRATCH;
+        if (!(workspace = device_scratch())) return ATTN_E_HIP;
+        workspace_bytes = kScratchBytes;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
 
     attn::DecodeArgs a{};
@@ -230,6 +262,8 @@ const char* attn_status_str(int status) {
         case ATTN_E_WORKSPACE: return "workspace missing or too small";
         case ATTN_E_HIP: return "HIP launch error";
         case ATTN_E_ARG: return "argument value out of domain or misaligned pointer";
+        case ATTN_E_SCRATCH:
+            return "the call needs more scratch than the library's fixed device array holds";
         default: return "unknown status";
     }
 }
@@ -313,6 +347,19 @@ int attn_decode_paged_ex(const void* q, const void* k_pages, const void* v_pages
                          lse, batch, heads_q, heads_kv, head_dim, page_size, max_pages_per_seq,
                          max_kv_len, dtype, o_dtype, scale, workspace, workspace_bytes, stream,
                          requested, unified, phi, opts ? opts->fallback_count : nullptr);
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* kv_lens, void* o,
+                              float* lse, int batch, int heads_q, int heads_kv, int head_dim,
+                              int page_size, int max_pages_per_seq, int max_kv_len, int dtype,
+                              int o_dtype, float scale, void* stream) {
+    if (!dtype_ok(dtype)) return ATTN_E_UNSUPPORTED;
+    if (batch > 0 && !kv_lens) return ATTN_E_NULL;
+    return decode_common(q, k_pages, v_pages, block_table, max_pages_per_seq, kv_lens, 0, o, lse,
+                         batch, heads_q, heads_kv, head_dim, page_size, max_pages_per_seq,
+                         max_kv_len, dtype, o_dtype, scale, nullptr, 0, stream, 0, false, 0.f,
+                         nullptr, 1.f, 1.f, true);
 }
 
 int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_pages,

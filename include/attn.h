@@ -55,8 +55,10 @@ typedef enum {
     ATTN_E_UNSUPPORTED = 3, /* well-formed but not implemented (head_dim, ...)  */
     ATTN_E_WORKSPACE = 4,   /* workspace missing or smaller than required       */
     ATTN_E_HIP = 5,         /* the HIP runtime reported an error on launch      */
-    ATTN_E_ARG = 6          /* a value outside its domain (scale <= 0 or NaN,
+    ATTN_E_ARG = 6,         /* a value outside its domain (scale <= 0 or NaN,
                                a misaligned pointer)                            */
+    ATTN_E_SCRATCH = 7      /* attn_decode_paged_noalloc: the call needs more
+                               scratch than the library's fixed array holds     */
 } attn_status;
 
 /* ATTN_FP8_E4M3 names an FP8 KV cache (OCP E4M3 bytes); it is accepted only
@@ -235,6 +237,31 @@ int attn_decode_paged_ex(const void *q, const void *k_pages, const void *v_pages
                          int dtype, int o_dtype, float scale,
                          void *workspace, size_t workspace_bytes, void *stream,
                          const attn_decode_opts *opts);
+
+/*
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, types, layouts,
+ * preconditions and results, minus the workspace.  The split partials go to
+ * a file-scope device array of the library, ATTN_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) per GPU, held from the call that first needs it on a GPU until
+ * the process ends; the call itself allocates nothing.  The planner's split
+ * is used (as attn_decode_paged).  A shape whose partials exceed the array
+ * (attn_decode_workspace_bytes(...) > ATTN_NOALLOC_SCRATCH_BYTES) returns
+ * ATTN_E_SCRATCH and launches nothing.  Every call on one GPU shares that
+ * GPU's array: calls that can overlap on one GPU (different streams, or
+ * several host threads) race and must be serialised by the caller.  The
+ * current device must be the stream's device.
+ * Errors: those of attn_decode_paged, ATTN_E_SCRATCH; ATTN_E_HIP also when
+ * the array's device address cannot be obtained.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_decode_paged_noalloc(const void *q, const void *k_pages, const void *v_pages,
+                              const int32_t *block_table, const int32_t *kv_lens,
+                              void *o, float *lse,
+                              int batch, int heads_q, int heads_kv, int head_dim,
+                              int page_size, int max_pages_per_seq, int max_kv_len,
+                              int dtype, int o_dtype, float scale, void *stream);
 
 /*
  * attn_decode_paged_fp8 -- attn_decode_paged over an FP8 KV cache.

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -16,7 +17,6 @@
 namespace {
 
 constexpr int kPageSize = 16;
-constexpr int kPlanCUs = 256;      // MI355X compute units (planning only)
 constexpr int kMaxSplit = 1024;    // longest chunk one workgroup takes
 constexpr int kMinSplit = 64;      // 4 wavefronts x one 16-token page
 constexpr int kGridYZ = 65535;
@@ -33,7 +33,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int plan(int batch, int heads_kv, int max_kv_len, int num_cus, int requested, int* split,
          int* max_splits) {
     if (batch < 0 || heads_kv <= 0 || max_kv_len < 0) return ATTN_E_SHAPE;
-    if (num_cus <= 0) num_cus = kPlanCUs;
+    if (num_cus <= 0) num_cus = attn::device_cus();
     int s;
     if (requested > 0) {
         s = (requested + kMinSplit - 1) / kMinSplit * kMinSplit;
@@ -119,7 +119,7 @@ int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* 
         return ATTN_E_UNSUPPORTED;
     if (o && o->waves_per_workgroup && o->waves_per_workgroup != 4 && o->waves_per_workgroup != 8)
         return ATTN_E_UNSUPPORTED;
-    if (num_cus <= 0) num_cus = kPlanCUs;
+    if (num_cus <= 0) num_cus = attn::device_cus();
     const int nw = (o && o->waves_per_workgroup) ? o->waves_per_workgroup : kFgWaves;
     int rb;
     if (o && o->rows_per_workgroup)
@@ -168,7 +168,7 @@ size_t flat_gemm_ws_bytes(int m, int n, int splits) {
 void prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int* chunk, int* n_chunks) {
     const long rows = (long)batch * (heads_q / heads_kv);
     const long per_chunk = (long)heads_kv * ((rows + 31) / 32);
-    const long want = std::max(1L, (1L * kPlanCUs + per_chunk - 1) / per_chunk);
+    const long want = std::max(1L, (1L * attn::device_cus() + per_chunk - 1) / per_chunk);
     long c = (prefix_len + want - 1) / want;
     c = std::min(1024L, std::max(64L, (c + 63) / 64 * 64));
     *chunk = (int)c;
@@ -202,7 +202,7 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
         return ATTN_E_ARG;
     if (batch > kGridYZ || heads_kv > kGridYZ) return ATTN_E_UNSUPPORTED;
     int split = 0, max_splits = 0;
-    const int rc = plan(batch, heads_kv, max_kv_len, kPlanCUs, requested_split, &split, &max_splits);
+    const int rc = plan(batch, heads_kv, max_kv_len, 0, requested_split, &split, &max_splits);
     if (rc != ATTN_OK) return rc;
     const size_t need = decode_ws_bytes(batch, heads_q, head_dim, max_splits);
     if (use_scratch && need > 0) {   // attn_decode_paged_noalloc
@@ -250,6 +250,26 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
 }
 
 }  // namespace
+
+namespace attn {
+
+int device_cus() {
+    constexpr int kFallback = 256, kMax = 64;
+    static std::atomic<int> cached[kMax];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMax) return kFallback;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = kFallback;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+}  // namespace attn
+
 
 extern "C" {
 
@@ -325,7 +345,7 @@ size_t attn_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int hea
                                    int max_kv_len, int split_tokens) {
     int split = 0, max_splits = 0;
     if (heads_q <= 0 || head_dim <= 0 ||
-        plan(batch, heads_kv, max_kv_len, kPlanCUs, split_tokens, &split, &max_splits) != ATTN_OK)
+        plan(batch, heads_kv, max_kv_len, 0, split_tokens, &split, &max_splits) != ATTN_OK)
         return 0;
     return decode_ws_bytes(batch, heads_q, head_dim, max_splits);
 }
@@ -412,7 +432,7 @@ size_t attn_shared_prefix_workspace_bytes(int batch, int heads_q, int heads_kv, 
         return decode_ws_bytes(batch, heads_q, head_dim, n_chunks);
     }
     int split = 0, max_splits = 0;
-    if (plan(batch, heads_kv, prefix_len, kPlanCUs, 0, &split, &max_splits) != ATTN_OK) return 0;
+    if (plan(batch, heads_kv, prefix_len, 0, 0, &split, &max_splits) != ATTN_OK) return 0;
     return decode_ws_bytes(batch, heads_q, head_dim, max_splits);
 }
 
@@ -526,7 +546,7 @@ int attn_flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_o
 
 size_t attn_flat_gemm_workspace_bytes(int m, int n, int k, const attn_flat_gemm_opts* opts) {
     int s = 0, sps = 0, rb = 0, nw = 0;
-    if (flat_gemm_plan(m, n, k, kPlanCUs, opts, &s, &sps, &rb, &nw) != ATTN_OK) return 0;
+    if (flat_gemm_plan(m, n, k, 0, opts, &s, &sps, &rb, &nw) != ATTN_OK) return 0;
     return flat_gemm_ws_bytes(m, n, s);
 }
 
@@ -535,7 +555,7 @@ int attn_flat_gemm(const void* a, const void* w, void* c, int m, int n, int k, i
                    const attn_flat_gemm_opts* opts) {
     if (dtype != ATTN_BF16 || !dtype_ok(c_dtype)) return ATTN_E_UNSUPPORTED;
     int s = 0, sps = 0, rb = 0, nw = 0;
-    const int rc = flat_gemm_plan(m, n, k, kPlanCUs, opts, &s, &sps, &rb, &nw);
+    const int rc = flat_gemm_plan(m, n, k, 0, opts, &s, &sps, &rb, &nw);
     if (rc != ATTN_OK) return rc;
     if (m == 0 || n == 0) return ATTN_OK;
     if (!c || (k > 0 && (!a || !w))) return ATTN_E_NULL;

@@ -9,6 +9,10 @@
 
 namespace attn {
 
+// Compute units of the current device, read once per device; 256 (MI355X)
+// when no device can be queried, so host-only planning calls still answer.
+int device_cus();
+
 // Dense prefill, bf16 in/out, bf16 MFMA with fp32 accumulation.
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o,
                                float* lse, int B, int Hq, int Hkv, int Tq, int Tk,

@@ -599,21 +599,6 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     }
 }
 
-// CU count of the current device, read once per device.
-int device_cus() {
-    static int cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] <= 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 // Pair query tiles p and n - 1 - p in one workgroup when that still leaves
 // at least one workgroup per CU.
 void grid_of(int BH, int n_qtiles, dim3* grid, int* paired) {

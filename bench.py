@@ -28,7 +28,10 @@ through three input sets so the 256 MB last-level cache cannot hold the
 working set; the cascade flushes it before every timed repetition.
 
 The CPU baseline runs the fp64 oracle on a bounded sample of the same
-workload (a few (b, h) pairs, ~10-30 s of CPU work) on the host's cores.
+workload (a few (b, h) pairs, ~10-30 s of CPU work) on the host's cores; the
+MHA, GQA and cascade decode sections time it on their sequences too
+(~4 s each, in KV GB/s), reported under cpu_baseline["decode"].  Every
+line carries the p10/p50/p90 of its per-launch durations (launch_us).
 """
 import argparse
 import hashlib
@@ -92,9 +95,10 @@ def time_launches(fn, steps, warmup, before=None):
     (spin_up) runs before the W warm-up steps.
 
     Without a per-step ``before`` the K steps are enqueued back to back
-    between one pair of events (per-step events would add their own gaps), so
-    every duration is span / K.  With ``before`` (e.g. a cache flush) each step
-    gets its own event pair and ``before`` stays outside the timed spans."""
+    between one pair of events (the span; the mean is span / K), then K more
+    with an event after each for the distribution.  With ``before`` (e.g. a
+    cache flush) each step gets its own event pair and ``before`` stays
+    outside the timed spans."""
     spin_up(fn, before)
     for i in range(warmup):
         if before:
@@ -110,7 +114,17 @@ def time_launches(fn, steps, warmup, before=None):
         end.record()
         torch.cuda.synchronize()
         span = start.elapsed_time(end)
-        return [span / steps] * steps, span, time.perf_counter() - t0
+        wall = time.perf_counter() - t0
+        # a second pass of K launches with an event between each two gives
+        # the per-launch distribution (the events add small gaps, so the
+        # mean stays the back-to-back span / K)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record()
+        for i in range(steps):
+            fn(i)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        return [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)], span, wall
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
@@ -122,6 +136,22 @@ def time_launches(fn, steps, warmup, before=None):
     wall = time.perf_counter() - t0
     durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return durs, float(np.sum(durs)), wall
+
+
+def percentiles_us(durs):
+    p10, p50, p90 = np.percentile(np.asarray(durs, np.float64) * 1e3, [10, 50, 90])
+    return dict(p10=round(float(p10), 2), p50=round(float(p50), 2), p90=round(float(p90), 2))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def source_digest(*names):
@@ -164,12 +194,12 @@ def bench_prefill(steps, warmup):
 
     durs, span, wall = time_launches(step, steps, warmup)
     flops = 4.0 * D * (T * (T + 1) / 2) * B * H
-    mean_ms = float(np.mean(durs))
+    mean_ms = span / steps
     achieved = flops / (mean_ms * 1e-3) / 1e12
     digest = source_digest("prefill_bf16.hip", "common.h")
     traffic = measured_traffic("prefill_bf16_causal_b4h32t1024d128", digest)
     return dict(
-        ms_per_step=span / steps, mean_launch_ms=mean_ms, median_launch_ms=float(np.median(durs)),
+        ms_per_step=span / steps, mean_launch_ms=mean_ms, launch_us=percentiles_us(durs),
         tflops=flops / (span / steps * 1e-3) / 1e12, flops=flops, wall_s=wall,
         roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -197,6 +227,7 @@ def bench_prefill_noncausal(steps, warmup):
     flops = 4.0 * D * T * T * B * H
     mean_ms = span / steps
     return dict(workload="non-causal prefill B4 H32 T1024 D128 bf16", mean_ms=mean_ms,
+                launch_us=percentiles_us(durs),
                 tflops=round(flops / (mean_ms * 1e-3) / 1e12, 2),
                 frac_mfma=round(flops / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
 
@@ -248,7 +279,8 @@ def bench_prefill_paged(steps, warmup):
     mean_ms = span / steps
     return dict(workload="chunked prefill B4 Hq32 Hkv8 D128 bf16, 512-token chunk against a "
                          "paged cache, kv_len U[2048,8192], causal (bottom-right), page 16",
-                mean_ms=mean_ms, tflops=round(mean_flops / (mean_ms * 1e-3) / 1e12, 2),
+                mean_ms=mean_ms, launch_us=percentiles_us(durs),
+                tflops=round(mean_flops / (mean_ms * 1e-3) / 1e12, 2),
                 frac_mfma=round(mean_flops / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
 
 
@@ -256,7 +288,68 @@ def kv_bytes(lengths, hkv, d, elem=2):
     return int(np.sum(np.asarray(lengths, np.int64))) * hkv * d * 2 * elem
 
 
-def bench_decode(name, steps, warmup):
+DECODE_SOURCES = ("decode_mfma.hip", "decode.hip", "common.h")
+
+
+def hbm_roofline(nbytes, mean_ms, kernels, counters, digest):
+    """Roofline object of an HBM-bound step: ``nbytes`` algorithmic bytes
+    over the mean step duration; traffic from the committed counters of the
+    same source (None when absent or stale)."""
+    achieved = nbytes / (mean_ms * 1e-3) / 1e9
+    return dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic(counters, digest),
+                kernel=kernels, algorithmic_bytes=int(nbytes), source_digest=digest)
+
+
+def decode_kernels(D, fp8, max_splits):
+    k = f"decode_mfma_kernel<{D},{'true' if fp8 else 'false'}>"
+    return k + (f" + decode_combine_kernel<{D}>" if max_splits > 1 else "")
+
+
+def cpu_decode_sample(d, target_s, prefix_len=0):
+    """The fp64 oracle on the sequences of a decode workload in order (one
+    call per batch of sequences, sized from the rate so far to end near
+    ``target_s``; the workload starts over when it runs out), in KV GB/s:
+    each sampled sequence's K+V bytes (bf16) over the oracle's time.  With
+    ``prefix_len`` (the cascade) each request attends the shared prefix + its
+    suffix, and the rate is the whole workload's bytes (prefix once) over
+    the sample's time scaled to every request."""
+    import oracle
+    threads = oracle.default_threads()
+    if prefix_len:
+        lens, run = d["suffix_lens"], lambda sl: oracle.cascade_decode(
+            d["q"][sl], d["k_pages"], d["v_pages"], d["prefix_pages"], prefix_len,
+            d["suffix_table"][sl], d["suffix_lens"][sl], d["scale"], threads=threads)
+    else:
+        lens, run = d["kv_lens"], lambda sl: oracle.decode_paged(
+            d["q"][sl], d["k_pages"], d["v_pages"], d["block_table"][sl], d["kv_lens"][sl],
+            d["scale"], threads=threads)
+    B, Hkv, D = len(lens), d["Hkv"], d["D"]
+    done, tokens, t_used, n = 0, 0, 0.0, 1
+    t0 = time.perf_counter()
+    while t_used < target_s:
+        lo = done % B
+        sl = slice(lo, min(B, lo + n))
+        run(sl)
+        done += sl.stop - lo
+        tokens += int(np.sum(lens[sl]))
+        t_used = time.perf_counter() - t0
+        n = max(1, int((target_s - t_used) / (t_used / done)))
+    if prefix_len:
+        nbytes = kv_bytes([prefix_len], Hkv, D) + kv_bytes(lens, Hkv, D)
+        rate = nbytes / (t_used * B / done) / 1e9
+        what = (f"{done} requests (the workload's {B} in order, repeated; each the "
+                f"{prefix_len}-token prefix + its suffix), {t_used:.1f} s, fp64, "
+                f"rate scaled to one pass over the {B}")
+    else:
+        rate = tokens * Hkv * D * 2 * 2 / t_used / 1e9
+        what = (f"{done} sequences (the workload's {B} in order, repeated; {tokens} KV "
+                f"tokens), {t_used:.1f} s, fp64")
+    return dict(value=round(rate, 4), unit="GB/s", cores=threads, kind="oracle", sample=what,
+                seconds=round(t_used, 2))
+
+
+def bench_decode(name, steps, warmup, cpu_s=0.0):
     d = wl.workload(name)
     q = dev(d["q"])
     kp, vp = dev(d["k_pages"]), dev(d["v_pages"])
@@ -274,13 +367,20 @@ def bench_decode(name, steps, warmup):
 
     durs, span, _ = time_launches(step, steps, warmup)
     nbytes = kv_bytes(d["kv_lens"], d["Hkv"], d["D"])
-    mean_ms = float(np.mean(durs))
+    mean_ms = span / steps
     split_used, nsplit = attn.attn_decode_plan(d["B"], d["Hkv"], maxlen, 0, split)
     del kp, vp
-    return dict(workload=wl.WORKLOADS[name], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
-                mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
-                frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                split_tokens=split_used, max_splits=nsplit)
+    digest = source_digest(*DECODE_SOURCES)
+    r = dict(workload=wl.WORKLOADS[name], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
+             mean_ms=mean_ms, launch_us=percentiles_us(durs),
+             gbs=nbytes / (mean_ms * 1e-3) / 1e9,
+             frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             split_tokens=split_used, max_splits=nsplit,
+             roofline=hbm_roofline(nbytes, mean_ms, decode_kernels(d["D"], False, nsplit),
+                                   name, digest))
+    if cpu_s > 0:
+        r["cpu_oracle"] = cpu_decode_sample(d, cpu_s)
+    return r
 
 
 def bench_decode_fp8(name, steps, warmup):
@@ -304,15 +404,19 @@ def bench_decode_fp8(name, steps, warmup):
 
     durs, span, _ = time_launches(step, steps, warmup)
     nbytes = kv_bytes(d["kv_lens"], d["Hkv"], d["D"], elem=1)
-    mean_ms = float(np.mean(durs))
+    mean_ms = span / steps
+    _, nsplit = attn.attn_decode_plan(d["B"], d["Hkv"], maxlen, 0, split)
     del kp, vp
     return dict(workload=wl.FP8_WORKLOADS[name], kv_bytes=nbytes, sum_kv_len=int(d["kv_lens"].sum()),
-                mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
+                mean_ms=mean_ms, launch_us=percentiles_us(durs),
+                gbs=nbytes / (mean_ms * 1e-3) / 1e9,
                 frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                tokens_per_s=int(d["kv_lens"].sum()) * d["Hkv"] / (mean_ms * 1e-3))
+                tokens_per_s=int(d["kv_lens"].sum()) * d["Hkv"] / (mean_ms * 1e-3),
+                roofline=hbm_roofline(nbytes, mean_ms, decode_kernels(d["D"], True, nsplit),
+                                      name + "_fp8", source_digest(*DECODE_SOURCES)))
 
 
-def bench_cascade(steps, warmup, fp8=False):
+def bench_cascade(steps, warmup, fp8=False, cpu_s=0.0):
     """Shared-prefix cascade decode (64 requests, 4096-token prefix, suffixes
     U[128, 1024], H32 D128): prefix stage + suffix decode + merge on one stream, timed as
     one step.  With fp8 the cache is OCP E4M3 bytes with per-tensor scales."""
@@ -358,9 +462,20 @@ def bench_cascade(steps, warmup, fp8=False):
     nbytes = (kv_bytes([c["prefix_len"]], c["Hkv"], D, elem=elem)
               + kv_bytes(c["suffix_lens"], c["Hkv"], D, elem=elem))
     mean_ms = float(np.mean(durs))
-    return dict(workload=(wl.FP8_WORKLOADS if fp8 else wl.WORKLOADS)[wl.CASCADE], kv_bytes=nbytes,
-                mean_ms=mean_ms, gbs=nbytes / (mean_ms * 1e-3) / 1e9,
-                frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    _, nsplit = attn.attn_decode_plan(R, c["Hkv"], maxlen, 0, 0)
+    kernels = (f"prefix_mfma_kernel<{D},{'true' if fp8 else 'false'}> + "
+               f"decode_combine_kernel<{D}> (prefix chunks) + "
+               + decode_kernels(D, fp8, nsplit) + " + merge_states_kernel")
+    r = dict(workload=(wl.FP8_WORKLOADS if fp8 else wl.WORKLOADS)[wl.CASCADE], kv_bytes=nbytes,
+             mean_ms=mean_ms, launch_us=percentiles_us(durs),
+             gbs=nbytes / (mean_ms * 1e-3) / 1e9,
+             frac_hbm=round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             roofline=hbm_roofline(nbytes, mean_ms, kernels, wl.CASCADE + ("_fp8" if fp8 else ""),
+                                   source_digest("prefix_mfma.hip", "merge.hip",
+                                                 *DECODE_SOURCES)))
+    if cpu_s > 0 and not fp8:
+        r["cpu_oracle"] = cpu_decode_sample(c, cpu_s, prefix_len=c["prefix_len"])
+    return r
 
 
 def bench_graph_decode(steps, warmup, B, length_range, layers=8):
@@ -448,7 +563,11 @@ def bench_flat_gemm(steps, warmup, ms=(1, 16, 64)):
                          "down 4096x11008), bf16, m tokens", results=out)
 
 
-def cpu_baseline(target_s=15.0):
+GRAPH_CASES = (("decode_step_graph_b1", 1, (256, 1024)), ("decode_step_graph_b4", 4, (1024, 4096)))
+DECODE_CPU_S = 4.0   # seconds of oracle time per decode workload sample
+
+
+def cpu_baseline(target_s=10.0):
     """The fp64 oracle on (b, h) pairs of the prefill workload, timed on the
     host cores; throughput in the bench's unit (algorithmic causal TFLOP/s)."""
     import oracle
@@ -457,9 +576,10 @@ def cpu_baseline(target_s=15.0):
     threads = oracle.default_threads()
     pairs, flops, t_used = 0, 0.0, 0.0
     t0 = time.perf_counter()
-    while t_used < target_s and pairs < 128:
-        n = max(1, min(threads, 128 - pairs))
-        idx = [(p // 32, p % 32) for p in range(pairs, pairs + n)]
+    while t_used < target_s:
+        # (b, h) pairs in order, starting over after all 128
+        n = max(1, min(threads, 128 - pairs % 128))
+        idx = [((p % 128) // 32, p % 32) for p in range(pairs, pairs + n)]
         q = np.stack([inp["q"][b, h] for b, h in idx])[:, None]
         k = np.stack([inp["k"][b, h] for b, h in idx])[:, None]
         v = np.stack([inp["v"][b, h] for b, h in idx])[:, None]
@@ -468,9 +588,14 @@ def cpu_baseline(target_s=15.0):
         flops += n * 4.0 * D * T * (T + 1) / 2
         t_used = time.perf_counter() - t0
     return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=f"{pairs} of 128 (b,h) pairs of the causal B4 H32 T1024 D128 prefill, "
-                       f"{t_used:.1f} s, fp64, full score matrix",
+                sample=f"{pairs} (b,h) pairs (the workload's 128 in order, repeated) of the "
+                       f"causal B4 H32 T1024 D128 prefill, {t_used:.1f} s, fp64, full score matrix",
                 seconds=round(t_used, 2))
+
+
+SECTIONS = ("prefill", "prefill_noncausal", "prefill_f32", "prefill_paged", "decode_mha",
+            "decode_gqa", "decode_mha_fp8", "decode_gqa_fp8", "cascade", "cascade_fp8", "graph",
+            "flat_gemm")
 
 
 def main():
@@ -482,6 +607,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--flat-gemm-only", action="store_true",
                     help="time only the flat GEMM of the decode projections (prints its JSON)")
+    ap.add_argument("--only", choices=SECTIONS,
+                    help="time one section and print its JSON instead of the bench line "
+                         "(for profiling one workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write elementwise kernel, "
                          "the reference for scaling HBM byte counters")
@@ -501,58 +629,76 @@ def main():
         del src, dst
         log("copy calibration: 3 x (1 GiB read + 1 GiB write)")
 
+    K, W = args.steps, args.warmup
     if args.flat_gemm_only:
-        flat = bench_flat_gemm(args.steps, args.warmup)
-        for mk, r in flat["results"].items():
-            log(f"  {mk}: layer {r['layer']['us']:.1f} us, {r['layer']['gbs']:.0f} GB/s")
-        print(json.dumps(flat), flush=True)
+        args.only = "flat_gemm"
+    if args.only:
+        run = {
+            "prefill": lambda: bench_prefill(K, W),
+            "prefill_noncausal": lambda: bench_prefill_noncausal(K, W),
+            "prefill_f32": lambda: bench_prefill_f32(K, W),
+            "prefill_paged": lambda: bench_prefill_paged(K, W),
+            "decode_mha": lambda: bench_decode(wl.DECODE_MHA, K, W),
+            "decode_gqa": lambda: bench_decode(wl.DECODE_GQA, K, W),
+            "decode_mha_fp8": lambda: bench_decode_fp8(wl.DECODE_MHA, K, W),
+            "decode_gqa_fp8": lambda: bench_decode_fp8(wl.DECODE_GQA, K, W),
+            "cascade": lambda: bench_cascade(K, W),
+            "cascade_fp8": lambda: bench_cascade(K, W, fp8=True),
+            "graph": lambda: {k: bench_graph_decode(K, W, B, lr) for k, B, lr in GRAPH_CASES},
+            "flat_gemm": lambda: bench_flat_gemm(K, W),
+        }[args.only]
+        log(f"{args.only} ...")
+        print(json.dumps(run()), flush=True)
         return
 
+    cpu_s = 0.0 if args.no_cpu_baseline else DECODE_CPU_S
     log("prefill B4 H32 T1024 D128 causal bf16 ...")
-    pre = bench_prefill(args.steps, args.warmup)
+    pre = bench_prefill(K, W)
     log(f"  {pre['tflops']:.1f} TFLOP/s, mean launch {pre['mean_launch_ms'] * 1e3:.1f} us")
     decode = {}
     paged_prefill = None
     flat = None
-    noncausal = bench_prefill_noncausal(args.steps, args.warmup)
+    noncausal = bench_prefill_noncausal(K, W)
     log(f"  non-causal: {noncausal['tflops']:.1f} TFLOP/s")
-    f32_mode = bench_prefill_f32(args.steps, args.warmup)
+    f32_mode = bench_prefill_f32(K, W)
     log(f"  fp32 test mode (B1 H1 T128 D64): {f32_mode['us']:.1f} us per launch")
     if not args.prefill_only:
         log("chunked prefill against the paged cache ...")
-        paged_prefill = bench_prefill_paged(args.steps, args.warmup)
+        paged_prefill = bench_prefill_paged(K, W)
         log(f"  {paged_prefill['tflops']:.1f} TFLOP/s")
         torch.cuda.empty_cache()
         for name in (wl.DECODE_MHA, wl.DECODE_GQA):
             log(f"{name} ...")
-            decode[name] = bench_decode(name, args.steps, args.warmup)
+            decode[name] = bench_decode(name, K, W, cpu_s=cpu_s)
             log(f"  {decode[name]['gbs']:.0f} GB/s")
             torch.cuda.empty_cache()
         for name in (wl.DECODE_MHA, wl.DECODE_GQA):
             log(f"{name}, FP8 cache ...")
-            decode[name + "_fp8"] = bench_decode_fp8(name, args.steps, args.warmup)
+            decode[name + "_fp8"] = bench_decode_fp8(name, K, W)
             log(f"  {decode[name + '_fp8']['gbs']:.0f} GB/s")
             torch.cuda.empty_cache()
         log(f"{wl.CASCADE} ...")
-        decode[wl.CASCADE] = bench_cascade(args.steps, args.warmup)
+        decode[wl.CASCADE] = bench_cascade(K, W, cpu_s=cpu_s)
         log(f"  {decode[wl.CASCADE]['gbs']:.0f} GB/s")
         torch.cuda.empty_cache()
         log(f"{wl.CASCADE}, FP8 cache ...")
-        decode[wl.CASCADE + "_fp8"] = bench_cascade(args.steps, args.warmup, fp8=True)
+        decode[wl.CASCADE + "_fp8"] = bench_cascade(K, W, fp8=True)
         log(f"  {decode[wl.CASCADE + '_fp8']['gbs']:.0f} GB/s")
-        for key, B, lr in (("decode_step_graph_b1", 1, (256, 1024)),
-                           ("decode_step_graph_b4", 4, (1024, 4096))):
+        for key, B, lr in GRAPH_CASES:
             log(f"8-layer decode step B{B}, eager vs graph replay ...")
-            decode[key] = bench_graph_decode(args.steps, args.warmup, B, lr)
+            decode[key] = bench_graph_decode(K, W, B, lr)
             log(f"  eager {decode[key]['eager_us']:.1f} us, graph {decode[key]['graph_us']:.1f} us")
         log("flat GEMM, Llama2-7B decode projections ...")
-        flat = bench_flat_gemm(args.steps, args.warmup)
+        flat = bench_flat_gemm(K, W)
         for mk, r in flat["results"].items():
             log(f"  {mk}: layer {r['layer']['us']:.1f} us, {r['layer']['gbs']:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle) ...")
         cpu = cpu_baseline()
+        cpu["cpu_model"] = cpu_model()
+        # the decode workloads' oracle samples, timed in their own sections
+        cpu["decode"] = {k: v.pop("cpu_oracle") for k, v in decode.items() if "cpu_oracle" in v}
         log(f"  {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
 
     line = {
@@ -560,10 +706,11 @@ def main():
         "value": round(pre["tflops"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": W,
         "spinup_s_per_section": SPINUP_S,
         "ms_per_step": round(pre["ms_per_step"], 5),
+        "launch_us": pre["launch_us"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -139,7 +139,8 @@ int attn_prefill_paged(const void *q, const void *k_pages, const void *v_pages,
  * FlashDecoding++ summary, section 5).
  *
  * attn_decode_plan: host-only.  Given the shape, the host-side upper bound
- * max_kv_len and the device's compute-unit count (num_cus <= 0: 256),
+ * max_kv_len and the compute-unit count (num_cus <= 0: the current
+ * device's, 256 when no device can be queried),
  * returns in *split_tokens the chunk length (a multiple of 64, at most 1024)
  * and in *max_splits the number of chunks of the longest sequence.
  * requested_split > 0 forces that chunk length (rounded up to a multiple of
@@ -401,7 +402,7 @@ int attn_decode_shared_prefix_fp8(const void *q, const void *k_pages, const void
  * ATTN_E_ARG (alignment), ATTN_E_HIP.
  *
  * attn_flat_gemm_plan: host-only.  The planner's choice for this shape on
- * num_cus compute units (<= 0: 256): rows of w per workgroup (16 for
+ * num_cus compute units (<= 0: the current device's, else 256): rows of w per workgroup (16 for
  * m <= 8, and for m <= 16 on weights of at most 2^24 elements; 32 for
  * m <= 32 on weights with at least 1.25 blocks of 64 rows per CU; else 64,
  * so that one A fragment serves four row blocks) and k slices across

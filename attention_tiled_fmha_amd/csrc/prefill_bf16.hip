@@ -22,8 +22,9 @@
 //                   VGPRs.  S^T puts one query row per lane and 16 of the 32
 //                   keys in its registers (the rest in lane l ^ 32): row max
 //                   and row sum are lane-local plus one v_permlane32_swap.
-//   softmax         exp2 of the scaled scores against the running max, P
-//                   rounded to bf16, already in B-operand order for PV.
+//   softmax         exp2 of the scaled scores against a fixed per-row
+//                   reference, P rounded to bf16, already in B-operand
+//                   order for PV.
 //   O^T += V^T P^T  A = V^T read from the row-major V tile with the gfx950
 //                   transposing LDS read ds_read_b64_tr_b16.
 //
@@ -33,32 +34,38 @@
 // capacity whether they come from one wavefront or two, so the three jobs of
 // a step run interleaved in one instruction stream: step t issues the MFMAs
 // of S(t+1) and of O += P(t-1) V(t-1) while the VALU runs the softmax of
-// S(t).  The softmax is branch-free (the running max is selected, not
-// branched on); O is rescaled in a short branch at the end of the step,
-// after the PV MFMAs that still belong to the old max.
+// S(t).
 //
 // K/V tiles go HBM -> VGPRs -> LDS: the loads of step t + 1's tile pair are
-// issued at the start of step t into one of two register sets, the set
-// loaded during step t - 1 is written to LDS at the end of step t, and one
-// workgroup barrier per step hands the tiles over.  LDS rows are
-// 16-byte-granule XOR swizzled: the 16 rows one K read spans and the 4 rows x
-// 4 granules one transposed V read spans each hit 16 distinct granule
-// positions of the 64 banks, and each wavefront's 16-byte writes are 1 KiB
-// contiguous.
+// issued in step t into one of two register sets, the set loaded during
+// step t - 1 is written to LDS at the end of step t, and one workgroup
+// barrier per step hands the tiles over.  LDS rows are 16-byte-granule XOR
+// swizzled: the 16 rows one K read spans and the 4 rows x 4 granules one
+// transposed V read spans each hit 16 distinct granule positions of the 64
+// banks, and each wavefront's 16-byte writes are 1 KiB contiguous.
 //
-// The running max is raised (and O, l rescaled) only when a row's max grows
-// by more than 2^8; otherwise exponentials are taken against the stale max.
-// Results are identical in exact arithmetic (numerator and denominator share
-// the reference) and every exponential stays <= 2^8.  The row sum adds the
-// bf16-rounded P that the MFMA multiplies with V.
+// Softmax reference.  Each row's exponentials are taken against the row max
+// of its first key tile, held for the whole pass, so no running max is kept
+// and O and l are never rescaled: numerator and denominator share the
+// reference, which is exact in exact arithmetic.  A later key far above the
+// reference would overflow, so every step checks that the tile's row sum
+// stays <= 2^20; if any row of any wavefront exceeds it, the workgroup
+// computes the exact row maxima over every visible key and runs the pass
+// again against them (every P <= 1).  The row sum adds the bf16-rounded P
+// that the MFMA multiplies with V.
 //
 // Causal masking (key j visible to query i iff j <= i + Tk - Tq) is applied
-// only on tiles that cross a block's diagonal.  When there are at least two
-// query tiles per CU, a workgroup takes query tiles p and n - 1 - p of one
-// (b, h) (equal causal work per workgroup), lighter first, and the
-// workgroups of one (b, h) sit on one XCD at the same time, so each K/V tile
-// is fetched from HBM about once and hit in that XCD's L2 afterwards.
-// Otherwise every workgroup takes one query tile, heaviest first.
+// only on tiles that cross a block's diagonal.  Once a wavefront's earlier
+// block is past its last visible key tile, its steps run on the later block
+// alone (half the MFMAs and softmax), which removes most of the work above
+// the diagonal.  When there are at least two query tiles per CU, a
+// workgroup takes query tiles p and n - 1 - p of one (b, h) (equal causal
+// work per workgroup), in an order that alternates between neighbouring
+// heads so that the workgroups switch tiles (Q load, O store) at four
+// different times rather than two, and the workgroups of one (b, h) sit on
+// one XCD at the same time, so each K/V tile is fetched from HBM about once
+// and hit in that XCD's L2 afterwards.  Otherwise every workgroup takes one
+// query tile, heaviest first.
 #include <type_traits>
 
 #include "common.h"
@@ -84,6 +91,14 @@ struct Cfg {
     static constexpr int ROW = 2 * D;              // bytes per K/V row
     static constexpr int TILE = kBN * ROW;         // bytes per K or V tile
     static constexpr int LPT = kBN * GPR / kThreads;  // 16-byte loads per thread per K or V tile
+};
+
+// The blocks each of a step's three jobs (S of the next key tile, softmax
+// of the current one, PV of the previous one) covers: 2 both of the
+// wavefront's row blocks, 1 only the later one (rb1), 0 none.
+template <int S, int M, int V>
+struct Jobs {
+    static constexpr int s = S, m = M, v = V;
 };
 
 // Granule positions.  K (read 16 rows x one granule per instruction):
@@ -276,8 +291,11 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     }
 
     const int n_my = paired ? ((n_qtiles - 1 - unit) == unit ? 1 : 2) : 1;
+    // half of the pairs run their heavier tile first, so that the tile
+    // switches (Q load, O store) of the workgroups are spread over four times
+    const int first = (slot & 1) ? n_qtiles - 1 - unit : unit;
     auto tile_of = [&](int u) {
-        return paired ? (u == 0 ? unit : n_qtiles - 1 - unit) : n_qtiles - 1 - unit;
+        return paired ? (u == 0 ? first : n_qtiles - 1 - first) : n_qtiles - 1 - unit;
     };
     // Q fragments (B operand of S^T = K Q^T) of the current query tile: row
     // qrow, dims 16s + 8hi .. +7, loaded unconditionally (clamped row, zeroed
@@ -370,10 +388,13 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         // needed LA slots later.  MFMA and VALU work share the SIMD's issue
         // capacity, so a steady mix keeps both busy.
         constexpr int NS = 4 * C::KS;       // MFMAs per step (2 KS for S, 2 KS for PV)
-        constexpr int SPS = 32 / NS;        // softmax scores per slot
         constexpr int LA = 6;               // read lookahead in slots
-        auto step_body = [&](auto PAR, auto MASK, auto FIRST) -> bool {
+        auto step_body = [&](auto PAR, auto MASK, auto FIRST, auto JOBS) -> bool {
             constexpr int P = decltype(PAR)::value, NP = P ^ 1;
+            using J = decltype(JOBS);
+            constexpr int SB = J::s, MB = J::m, VB = J::v;
+            // the active scores: those of block 1 (16 .. 31), or of both
+            constexpr int SC0 = 32 - 16 * MB, SCN = 16 * MB;
             const unsigned char LDS_AS* sk = sK[NP];
             const unsigned char LDS_AS* sv = sV[NP];
             bool big = false;
@@ -400,12 +421,12 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             // reads needed before slot LA
 #pragma unroll
             for (int s2 = 0; s2 < C::KS; s2++)
-                if (k_slot(s2) < LA) read_k(s2);
+                if (SB > 0 && k_slot(s2) < LA) read_k(s2);
 #pragma unroll
             for (int ps = 0; ps < 2; ps++)
 #pragma unroll
                 for (int db = 0; db < C::DB; db++)
-                    if (v_slot(ps, db) < LA) read_v(ps, db);
+                    if (VB > 0 && v_slot(ps, db) < LA) read_v(ps, db);
             float pe[32];                      // exp2 results awaiting their pack
             float lsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
             uint32_t pw[2][2][4];
@@ -427,35 +448,39 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             for (int i = 0; i < NS; i++) {
                 if (i % 2 == 0) {   // S MFMA: k-step s of block a
                     const int s2 = i / 4, a = (i / 2) % 2;
-                    sacc[NP][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        kf[s2], qf[a][s2], s2 == 0 ? f32x16{} : sacc[NP][a], 0, 0, 0);
+                    if (a >= 2 - SB)
+                        sacc[NP][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            kf[s2], qf[a][s2], s2 == 0 ? f32x16{} : sacc[NP][a], 0, 0, 0);
                 } else {            // PV MFMA: 16-key step ps, dim block db, block a
                     const int k2 = i / 2, ps = k2 / (2 * C::DB), db = (k2 / 2) % C::DB, a = k2 % 2;
-                    oacc[a][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        vf[ps][db], pf[NP][a][ps], oacc[a][db], 0, 0, 0);
+                    if (a >= 2 - VB)
+                        oacc[a][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            vf[ps][db], pf[NP][a][ps], oacc[a][db], 0, 0, 0);
                 }
+                // the active scores spread evenly over the slots
 #pragma unroll
-                for (int q2 = 0; q2 < SPS; q2++) {
-                    const int j = i * SPS + q2;
+                for (int j = SC0 + i * SCN / NS; j < SC0 + (i + 1) * SCN / NS; j++) {
                     sm_fma(j);
-                    if (j >= 1) sm_exp(j - 1);
-                    if (j >= 3 && (j & 1)) sm_pack(j - 3);
+                    if (j - 1 >= SC0) sm_exp(j - 1);
+                    if (j - 3 >= SC0 && (j & 1)) sm_pack(j - 3);
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < C::KS; s2++)
-                    if (k_slot(s2) == i + LA) read_k(s2);
+                    if (SB > 0 && k_slot(s2) == i + LA) read_k(s2);
 #pragma unroll
                 for (int ps = 0; ps < 2; ps++)
 #pragma unroll
                     for (int db = 0; db < C::DB; db++)
-                        if (v_slot(ps, db) == i + LA) read_v(ps, db);
+                        if (VB > 0 && v_slot(ps, db) == i + LA) read_v(ps, db);
             }
             __builtin_amdgcn_iglp_opt(3);
-            // the slots packed pairs 0 .. 28 (slot j packs pair j - 3); pair 30 remains
-            sm_exp(31);
-            sm_pack(30);
+            if constexpr (MB > 0) {
+                // the slots packed pairs up to 28; pair 30 remains
+                sm_exp(31);
+                sm_pack(30);
+            }
 #pragma unroll
-            for (int a = 0; a < 2; a++) {
+            for (int a = 2 - MB; a < 2; a++) {
 #pragma unroll
                 for (int ps = 0; ps < 2; ps++)
                     pf[P][a][ps] = __builtin_bit_cast(bf16x8, u32x4{pw[a][ps][0], pw[a][ps][1],
@@ -477,6 +502,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         // Steps from t_mask on apply the mask.  GIVEN: m_ref holds the exact
         // row maxima (the recompute pass), else it is taken from tile 0.
         // Returns whether any wavefront saw a too-low reference.
+        // last key tile of this wavefront's block 0 (the one that holds the
+        // last key its last row sees; -1 when it sees none)
+        const int T0 = CAUSAL ? (min(Tk - 1, qa0 + 31 + diag) >= 0 ? min(Tk - 1, qa0 + 31 + diag) / kBN : -1)
+                              : n - 1;
         auto pass = [&](auto GIVEN) -> bool {
             constexpr bool G = decltype(GIVEN)::value;
             const std::integral_constant<bool, true> Y;
@@ -494,11 +523,11 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                 for (int ps = 0; ps < 2; ps++) pf[1][a][ps] = bf16x8{};
             }
             bool flag = false;
-            auto step = [&](int t, auto PAR, auto MASK, auto FIRST) {
+            auto step = [&](int t, auto PAR, auto MASK, auto FIRST, auto JOBS) {
                 constexpr int P = decltype(PAR)::value;          // t % 2
                 load_pair<D, PAGED>(stg[P ^ 1], src, lp, wave, t + 3, t + 1);
                 t_cur = t;
-                const bool big = step_body(PAR, MASK, FIRST);
+                const bool big = step_body(PAR, MASK, FIRST, JOBS);
                 if constexpr (!G) flag |= big;
                 store_pair<D>(stg[P], sK[P], sV[P], tid);
                 lds_barrier();
@@ -515,15 +544,26 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             // unmasked pairs while both steps precede t_mask, then masked pairs
             // up to step n (masking a tile that needs none, or running a step
             // past n, changes nothing).
-            step(0, P0, Y, std::integral_constant<bool, !G>{});
+            const Jobs<2, 2, 2> BOTH;
+            step(0, P0, Y, std::integral_constant<bool, !G>{}, BOTH);
             int t = 1;
             for (; t + 2 <= t_mask; t += 2) {
-                step(t, P1, N, N);
-                step(t + 1, P0, N, N);
+                step(t, P1, N, N, BOTH);
+                step(t + 1, P0, N, N, BOTH);
             }
-            for (; t <= n; t += 2) {
-                step(t, P1, Y, N);
-                step(t + 1, P0, Y, N);
+            // causal: once block 0 is past its last key tile T0 (from step
+            // T0 + 2 on it has no S, softmax or PV left), the pairs run on
+            // block 1 alone
+            const int t_half = CAUSAL ? T0 + 2 : n + 2;
+            for (; t <= n && t < t_half; t += 2) {
+                step(t, P1, Y, N, BOTH);
+                step(t + 1, P0, Y, N, BOTH);
+            }
+            if constexpr (CAUSAL) {
+                for (; t <= n; t += 2) {
+                    step(t, P1, Y, N, Jobs<1, 1, 1>{});
+                    step(t + 1, P0, Y, N, Jobs<1, 1, 1>{});
+                }
             }
             return flag;
         };

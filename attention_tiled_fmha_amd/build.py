@@ -29,8 +29,11 @@ FLAGS = [
 
 # Per-file extras: the prefill and shared-prefix softmax never see NaN
 # (scores are finite or -inf, and the cache tail past the prefix reads as
-# zeros), so fmax needs no NaN canonicalisation there.
-FILE_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"], "prefix_mfma.hip": ["-fno-honor-nans"]}
+# zeros), so fmax needs no NaN canonicalisation there.  The prefill selects
+# the VGPR form of the MFMA instructions, so that the softmax reads the
+# score accumulators without copying them out of AGPRs.
+FILE_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "prefix_mfma.hip": ["-fno-honor-nans"]}
 
 
 def sources():

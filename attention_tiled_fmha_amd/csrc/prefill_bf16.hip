@@ -36,13 +36,21 @@
 // of S(t+1) and of O += P(t-1) V(t-1) while the VALU runs the softmax of
 // S(t).
 //
-// K/V tiles go HBM -> VGPRs -> LDS: the loads of step t + 1's tile pair are
-// issued in step t into one of two register sets, the set loaded during
-// step t - 1 is written to LDS at the end of step t, and one workgroup
-// barrier per step hands the tiles over.  LDS rows are 16-byte-granule XOR
-// swizzled: the 16 rows one K read spans and the 4 rows x 4 granules one
-// transposed V read spans each hit 16 distinct granule positions of the 64
-// banks, and each wavefront's 16-byte writes are 1 KiB contiguous.
+// K/V tiles go from HBM straight into LDS (buffer loads with the LDS
+// destination, no VGPR staging): step t issues the loads of its tile pair
+// into the stage that step t - 1 finished reading, each wavefront waits for
+// its own loads at the end of the step, and the step's workgroup barrier
+// hands the tiles over.  Each stage is its own LDS object, so the compiler
+// orders reads of one stage only after the loads into that stage.  LDS rows
+// are 16-byte-granule XOR swizzled: the 16 rows one K read spans and the 4
+// rows x 4 granules one transposed V read spans each hit 16 distinct granule
+// positions of the 64 banks; a wavefront's load fills 1 KiB contiguously.
+//
+// Registers: the MFMAs write VGPRs (the library builds this file with the
+// VGPR form of the matrix instructions), so the softmax reads S without
+// copies, and the Q fragments, which only the S MFMAs read, are placed in
+// AGPRs; the 512 registers of one wavefront per SIMD then hold both blocks'
+// O and S, Q, P and the LDS reads issued several MFMAs ahead.
 //
 // Softmax reference.  Each row's exponentials are taken against the row max
 // of its first key tile, held for the whole pass, so no running max is kept
@@ -130,12 +138,6 @@ struct KVSrc {
     int Hkv, kvh, Tk;
 };
 
-// One thread's share of a K/V tile pair in flight: LPT granules of K and of V.
-template <int D>
-struct Stage {
-    u32x4 k[Cfg<D>::LPT], v[Cfg<D>::LPT];
-};
-
 // Thread tid's granules of a tile: g = tid + 256 j lands at byte 16 g of the
 // LDS tile (row g / GPR, swizzled position g % GPR), so it fetches global
 // granule (g % GPR) ^ swz(row) of that row.  goff is its byte offset within
@@ -156,12 +158,24 @@ struct LoadPlan {
     }
 };
 
-// Issue this thread's loads of K tile kt and V tile vt.  Tiles below 0 or
-// past Tk are empty (zero-sized descriptors), so every call issues the same
-// number of loads and none is conditional.
-template <int D, bool PAGED>
-__device__ __forceinline__ void load_pair(Stage<D>& st, const KVSrc& src, const LoadPlan<D>& lp,
-                                          int wave, int kt, int vt) {
+// One 16-byte global -> LDS load per lane: lane L of the wavefront writes
+// bytes dst + 16 L .. + 15 (the LDS address is the wavefront's M0 base).  A
+// lane whose offset lies past the descriptor's size writes zeros.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned char LDS_AS* dst,
+                                           int off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void LDS_AS*)dst, 16, off, 0, 0, 0);
+}
+
+// Issue this thread's direct-to-LDS loads of K tile kt into kdst and, with
+// V_TOO, of V tile vt into vdst: granule j of thread tid lands at byte
+// 16 (tid + 256 j) of the tile, i.e. wavefront w's load j fills the 1 KiB at
+// 1024 (w + 4 j).  Tiles below 0 or past Tk are empty (zero-sized
+// descriptors), so their LDS bytes become zeros and every call issues the
+// same number of loads.
+template <int D, bool PAGED, bool V_TOO>
+__device__ __forceinline__ void dma_tiles(unsigned char LDS_AS* kdst, unsigned char LDS_AS* vdst,
+                                          const KVSrc& src, const LoadPlan<D>& lp, int wave,
+                                          int kt, int vt) {
     using C = Cfg<D>;
 #pragma unroll
     for (int j = 0; j < C::LPT; j++) {
@@ -190,20 +204,9 @@ __device__ __forceinline__ void load_pair(Stage<D>& st, const KVSrc& src, const 
             kbytes = rows(kt) * C::ROW;
             vbytes = rows(vt) * C::ROW;
         }
-        st.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(kb, kbytes), lp.goff_k[j], 0, 0);
-        st.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(vb, vbytes), lp.goff_v[j], 0, 0);
-    }
-}
-
-// Write a staged pair: thread tid's granule j goes to byte 16 (tid + 256 j)
-// of the LDS K and V tiles (1 KiB contiguous per wavefront store).
-template <int D>
-__device__ __forceinline__ void store_pair(const Stage<D>& st, unsigned char LDS_AS* kt,
-                                           unsigned char LDS_AS* vt, int tid) {
-#pragma unroll
-    for (int j = 0; j < Cfg<D>::LPT; j++) {
-        *(u32x4 LDS_AS*)(kt + 16 * (tid + kThreads * j)) = st.k[j];
-        *(u32x4 LDS_AS*)(vt + 16 * (tid + kThreads * j)) = st.v[j];
+        const int dst = 1024 * (wave + 4 * j);
+        lds_load16(rsrc(kb, kbytes), kdst + dst, lp.goff_k[j]);
+        if constexpr (V_TOO) lds_load16(rsrc(vb, vbytes), vdst + dst, lp.goff_v[j]);
     }
 }
 
@@ -220,6 +223,13 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The same after this wavefront's direct-to-LDS loads (and every other
+// vector memory access it issued) have completed: after it, every
+// wavefront's tiles are in LDS.
+__device__ __forceinline__ void dma_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -229,12 +239,17 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                          const int32_t* __restrict__ block_table,
                          const int32_t* __restrict__ kv_lens, int bt_stride) {
     using C = Cfg<D>;
-    // two K tiles, then two V tiles
-    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[4 * C::TILE];
+    // two K and two V stages, each its own LDS object: the compiler then
+    // tracks the direct-to-LDS loads into one stage separately from reads of
+    // the others (a shared object would make every LDS read wait for every
+    // load in flight)
+    __shared__ __attribute__((aligned(1024))) unsigned char k_st0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char k_st1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_st0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_st1[C::TILE];
     __shared__ int flags[kWaves];
-    unsigned char LDS_AS* smem = (unsigned char LDS_AS*)smem_raw;
-    unsigned char LDS_AS* const sK[2] = {smem, smem + C::TILE};
-    unsigned char LDS_AS* const sV[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
+    unsigned char LDS_AS* const sK[2] = {(unsigned char LDS_AS*)k_st0, (unsigned char LDS_AS*)k_st1};
+    unsigned char LDS_AS* const sV[2] = {(unsigned char LDS_AS*)v_st0, (unsigned char LDS_AS*)v_st1};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -299,14 +314,12 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     };
     // Q fragments (B operand of S^T = K Q^T) of the current query tile: row
     // qrow, dims 16s + 8hi .. +7, loaded unconditionally (clamped row, zeroed
-    // past Tq).  pro0 / pro1 / stg[0]: the first K/V tiles of a pass (K(0),
-    // K(1), then K(2) with V(0)), loaded ahead of it.
+    // past Tq).  The first K tiles of a pass (K(0) and K(1), with zeros for
+    // V stage 1) go to LDS ahead of it.
     bf16x8 qf[2][C::KS];
-    Stage<D> pro0, pro1, stg[2];
     auto issue_kv_head = [&]() {
-        load_pair<D, PAGED>(pro0, src, lp, wave, 0, -1);
-        load_pair<D, PAGED>(pro1, src, lp, wave, 1, -1);
-        load_pair<D, PAGED>(stg[0], src, lp, wave, 2, 0);
+        dma_tiles<D, PAGED, true>(sK[0], sV[1], src, lp, wave, 0, -1);
+        dma_tiles<D, PAGED, false>(sK[1], sV[1], src, lp, wave, 1, -1);
     };
     auto issue_tile = [&](int u) {
         const int q0u = tile_of(u) * kBM;
@@ -318,6 +331,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             for (int s = 0; s < C::KS; s++) {
                 u32x4 w = *(const u32x4*)(qp + (size_t)qr * D + 16 * s + 8 * hi);
                 if (qrow >= Tq) w = u32x4{0, 0, 0, 0};
+                // an empty statement whose operand lives in AGPRs: Q stays
+                // there, as the B operand of the S MFMAs
+                asm("" : "+a"(w));
                 qf[a][s] = __builtin_bit_cast(bf16x8, w);
             }
         }
@@ -492,20 +508,19 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             return __builtin_amdgcn_ballot_w64(big) != 0;
         };
 
+        // last key tile of this wavefront's block 0 (the one that holds the
+        // last key its last row sees; -1 when it sees none)
+        const int T0 = CAUSAL ? (min(Tk - 1, qa0 + 31 + diag) >= 0 ? min(Tk - 1, qa0 + 31 + diag) / kBN : -1)
+                              : n - 1;
         // One pass over the key tiles.  Step t: S(t+1), softmax(t), PV(t-1);
-        // pair t (K(t+2), V(t)) goes from registers to LDS and pair t + 1 is
-        // loaded.  LDS: S(t+1) reads K stage (t+1)%2, PV(t-1) reads V stage
-        // (t-1)%2; the stores go to stages t%2, last read in step t-1.  Every
+        // pair t (K(t+2), V(t)) is loaded into LDS stage t%2, which step t - 1
+        // was the last to read; S(t+1) and PV(t-1) read stage (t+1)%2.  Every
         // step runs all three jobs: PV(-1) multiplies P = 0 with the zeroed V
         // stage 1, S(n) and S(n+1) read tiles past the key range (zeros) and
         // are not used, and the softmax of step n sees only masked keys (P = 0).
         // Steps from t_mask on apply the mask.  GIVEN: m_ref holds the exact
         // row maxima (the recompute pass), else it is taken from tile 0.
         // Returns whether any wavefront saw a too-low reference.
-        // last key tile of this wavefront's block 0 (the one that holds the
-        // last key its last row sees; -1 when it sees none)
-        const int T0 = CAUSAL ? (min(Tk - 1, qa0 + 31 + diag) >= 0 ? min(Tk - 1, qa0 + 31 + diag) / kBN : -1)
-                              : n - 1;
         auto pass = [&](auto GIVEN) -> bool {
             constexpr bool G = decltype(GIVEN)::value;
             const std::integral_constant<bool, true> Y;
@@ -525,18 +540,17 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             bool flag = false;
             auto step = [&](int t, auto PAR, auto MASK, auto FIRST, auto JOBS) {
                 constexpr int P = decltype(PAR)::value;          // t % 2
-                load_pair<D, PAGED>(stg[P ^ 1], src, lp, wave, t + 3, t + 1);
+                dma_tiles<D, PAGED, true>(sK[P], sV[P], src, lp, wave, t + 2, t);
+                // the loads go out first: they have the whole step to land
+                __builtin_amdgcn_sched_barrier(0);
                 t_cur = t;
                 const bool big = step_body(PAR, MASK, FIRST, JOBS);
                 if constexpr (!G) flag |= big;
-                store_pair<D>(stg[P], sK[P], sV[P], tid);
-                lds_barrier();
+                dma_barrier();
             };
-            // prologue (its loads were issued ahead): K(0) and K(1) into LDS,
-            // zeros into V stage 1, pair 0 (K(2), V(0)) in flight; then S(0)
-            store_pair<D>(pro0, sK[0], sV[1], tid);
-            store_pair<D>(pro1, sK[1], sV[1], tid);
-            lds_barrier();
+            // prologue (its loads were issued ahead): K(0) and K(1) in LDS,
+            // zeros in V stage 1; then S(0)
+            dma_barrier();
             s_mfma(P0);
             lds_barrier();                    // K stage 0 is rewritten in step 0
             // Step 0 (masked, which is exact for any tile), then pairs of steps
@@ -580,10 +594,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                 // against them (every P <= 1)
                 m_ref[0] = m_ref[1] = -INFINITY;
                 for (int t = 0; t < n; t++) {
-                    Stage<D> s0;
-                    load_pair<D, PAGED>(s0, src, lp, wave, t, -1);
-                    store_pair<D>(s0, sK[0], sV[1], tid);
-                    lds_barrier();
+                    dma_tiles<D, PAGED, false>(sK[0], sV[1], src, lp, wave, t, -1);
+                    dma_barrier();
                     s_mfma(std::integral_constant<int, 0>{});
 #pragma unroll
                     for (int a = 0; a < 2; a++) {

@@ -200,3 +200,23 @@ def test_prefill_late_dominant_key_bf16(causal, D):
     #                                        over 30 log2 units above the rest
     inp["k"], inp["q"] = wl.bf16_bits(kf), wl.bf16_bits(qf)
     check(inp, causal)
+
+
+@pytest.mark.parametrize("Tk", [300, 700])
+def test_prefill_paired_tiles_with_empty_rows(Tk):
+    """B4 H32 Tq1024 D128 causal bf16 with fewer keys than queries
+    (bottom-right diagonal at Tk - Tq): 512 query tiles, so each workgroup
+    takes two, and with Tk = 300 both tiles of some workgroups see no key at
+    all while others pair an empty tile with a full one.  Rows before
+    Tq - Tk are O = 0 with lse = -inf; sampled (b, h) pairs match the
+    oracle."""
+    require_gpu()
+    B, H, Tq, D = 4, 32, 1024, 128
+    inp = wl.prefill_inputs(B, H, H, Tq, Tk, D, "bf16", 71 + Tk)
+    o, lse = run_prefill(inp, causal=True)
+    assert np.all(o[:, :, :Tq - Tk] == 0) and np.all(np.isneginf(lse[:, :, :Tq - Tk]))
+    for b, h in [(0, 0), (1, 5), (2, 17), (3, 30), (3, 31)]:
+        ro, rl = oracle.attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
+                                  inp["v"][b:b + 1, h:h + 1], True, inp["scale"])
+        assert_close(o[b, h], ro[0, 0], "bf16", f"O (b={b},h={h})")
+        assert_close(lse[b, h], rl[0, 0], "bf16", f"lse (b={b},h={h})")

@@ -318,17 +318,23 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     __shared__ f32x4 s_o[NG][LPR];
     const long row = blockIdx.x;
     const int b = (int)(row / a.Hq);
-    const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
-    const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
-    if (nsplit <= 1) return;  // written directly by the split kernel (uniform per workgroup)
     const int grp = threadIdx.x / LPR, dl = threadIdx.x % LPR;
     const float* ls = a.ws_lse + row * a.max_splits;
     const f32x4* os = (const f32x4*)(a.ws_o + row * a.max_splits * D) + dl;
+    // the group's first chunk is loaded together with the sequence length
+    // (chunk grp < max_splits lies in the workspace; it is used only if the
+    // sequence has that many chunks), so the two latencies overlap
+    const bool pre = grp < a.max_splits;
+    const float l0 = pre ? ls[grp] : -INFINITY;
+    const f32x4 o0 = pre ? os[(size_t)grp * LPR] : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
+    const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
+    if (nsplit <= 1) return;  // written directly by the split kernel (uniform per workgroup)
     float m = -INFINITY, l = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c = grp; c < nsplit; c += NG) {
-        const float lc = ls[c];
-        const f32x4 oc = os[(size_t)c * LPR];
+        const float lc = c == grp ? l0 : ls[c];
+        const f32x4 oc = c == grp ? o0 : os[(size_t)c * LPR];
         const float mn = fmaxf(m, lc);
         const float sa = (m == -INFINITY) ? 0.f : expf(m - mn);
         const float sb = (lc == -INFINITY) ? 0.f : expf(lc - mn);

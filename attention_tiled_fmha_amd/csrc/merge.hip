@@ -42,7 +42,11 @@ __global__ __launch_bounds__(256) void merge_states_kernel(T* o_a, float* lse_a,
     const long row = gid / per_row;
     const int c = (int)(gid - row * per_row);
     if (row >= rows) return;
+    // all four loads are issued before any of them is used (one memory
+    // latency per thread, not two)
+    const size_t off = (size_t)row * D + 4 * c;
     const float la = lse_a[row], lb = lse_b[row];
+    const f32x4 oa = Quad<T>::load(o_a + off), ob = Quad<T>::load(o_b + off);
     const float M = fmaxf(la, lb);
     float wa = 0.f, wb = 0.f, lse = -INFINITY;
     if (M != -INFINITY) {
@@ -51,10 +55,10 @@ __global__ __launch_bounds__(256) void merge_states_kernel(T* o_a, float* lse_a,
         lse = M + logf(wa + wb);
     }
     const float inv = (wa + wb) > 0.f ? 1.f / (wa + wb) : 0.f;
-    const size_t off = (size_t)row * D + 4 * c;
-    f32x4 r = {0.f, 0.f, 0.f, 0.f};
-    if (wa > 0.f) r += wa * Quad<T>::load(o_a + off);
-    if (wb > 0.f) r += wb * Quad<T>::load(o_b + off);
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; e++)   // selects, so an empty side's o (even NaN) adds nothing
+        r[e] = (wa > 0.f ? wa * oa[e] : 0.f) + (wb > 0.f ? wb * ob[e] : 0.f);
     Quad<T>::store(o_a + off, r * inv);
     if (c == 0) lse_a[row] = lse;
 }

@@ -146,6 +146,10 @@ int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* 
     } else if (rblocks * 8 < 5L * num_cus) {
         s = 4;
         while (s > 1 && nsteps / ((long)s * nw) < 2 * U) s /= 2;
+    } else if (rblocks > num_cus && rblocks < 2L * num_cus && nsteps / (2L * nw) >= 2 * U) {
+        // between one and two rounds of row blocks (e.g. gate_up at m = 64:
+        // 344 on 256 CUs) two k slices even the rounds out: 72 against 79 us
+        s = 2;
     }
     s = std::max(1, std::min(s, std::max(nsteps, 1)));
     const int sps = std::max(1, (nsteps + s - 1) / s);

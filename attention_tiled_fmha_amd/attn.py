@@ -44,6 +44,8 @@ SIGNATURES = {
     "attn_flat_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "attn_decode_paged_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                        _i, _i, _i, _i, _f, _vp]),
+    "attn_probe_block_bytes": (_i, []),
+    "attn_probe_hbm_read": (_i, [_vp, _vp, _i, _vp, _vp]),
 }
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -433,3 +435,23 @@ def attn_flat_gemm(a, w, c, splits=0, rows_per_workgroup=0, waves_per_workgroup=
                                  ws_bytes, _stream(stream),
                                  _fg_opts(splits, rows_per_workgroup, waves_per_workgroup)),
            "attn_flat_gemm")
+
+
+def attn_probe_hbm_read(buf, order=None, sink=None, stream=None):
+    """Read the uint8 device tensor buf (a multiple of attn_probe_block_bytes()
+    bytes) as 4 KiB blocks in the int32 order (None: in place order); one
+    kernel on the stream, for timing with events."""
+    _dense(buf, "buf")
+    blk = load().attn_probe_block_bytes()
+    nbytes = buf.numel() * buf.element_size()
+    if nbytes % blk:
+        raise ValueError(f"buf must be a multiple of {blk} bytes")
+    n = nbytes // blk
+    if order is not None:
+        _dense(order, "order")
+        if order.dtype != torch.int32 or order.numel() != n:
+            raise ValueError("order must be int32 with one entry per block")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(load().attn_probe_hbm_read(_p(buf), _p(order), int(n), _p(sink), _stream(stream)),
+           "attn_probe_hbm_read")

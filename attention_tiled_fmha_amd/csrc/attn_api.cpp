@@ -583,4 +583,15 @@ int attn_flat_gemm(const void* a, const void* w, void* c, int m, int n, int k, i
     return check_hip(attn::launch_flat_gemm(p, (hipStream_t)stream));
 }
 
+int attn_probe_block_bytes(void) { return attn::hbm_probe_block_bytes(); }
+
+int attn_probe_hbm_read(const void* buf, const int32_t* order, int n_blocks, uint32_t* sink,
+                        void* stream) {
+    if (n_blocks < 0) return ATTN_E_SHAPE;
+    if (n_blocks == 0) return ATTN_OK;
+    if (!buf || !sink) return ATTN_E_NULL;
+    if (!al16(buf) || !al4(sink) || (order && !al4(order))) return ATTN_E_ARG;
+    return check_hip(attn::launch_hbm_read(buf, order, n_blocks, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

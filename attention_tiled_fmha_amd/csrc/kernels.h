@@ -13,6 +13,12 @@ namespace attn {
 // when no device can be queried, so host-only planning calls still answer.
 int device_cus();
 
+// HBM read-rate probe: n_blocks blocks of hbm_probe_block_bytes() bytes, in
+// `order` (or in place order when null).
+int hbm_probe_block_bytes();
+hipError_t launch_hbm_read(const void* buf, const int32_t* order, int n_blocks, uint32_t* sink,
+                           hipStream_t stream);
+
 // Dense prefill, bf16 in/out, bf16 MFMA with fp32 accumulation.
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o,
                                float* lse, int B, int Hq, int Hkv, int Tq, int Tk,

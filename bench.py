@@ -563,6 +563,38 @@ def bench_flat_gemm(steps, warmup, ms=(1, 16, 64)):
                          "down 4096x11008), bf16, m tokens", results=out)
 
 
+def bench_hbm_read(reps=10):
+    """The HBM read rate plain 16-byte loads reach on this GPU (a read-only
+    kernel of the library over 4 GiB): 4 KiB blocks in place order and in a
+    seeded random order (the scattered pages of a paged cache).  The
+    memory-bound lines are also given as a fraction of the random-order rate."""
+    blk = attn.load().attn_probe_block_bytes()
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    n = nbytes // blk
+    order = torch.from_numpy(np.random.default_rng(2024).permutation(n).astype(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for key, o in (("in_order_4k_blocks", None), ("random_4k_blocks", order)):
+        attn.attn_probe_hbm_read(buf, o, sink)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            attn.attn_probe_hbm_read(buf, o, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        med = float(np.median(ts))
+        out[key] = dict(gbs=round(nbytes / (med * 1e-3) / 1e9, 1),
+                        frac_hbm=round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        us=round(med * 1e3, 1))
+    del buf, order
+    torch.cuda.empty_cache()
+    return dict(workload="read-only kernel, 4 GiB as 4 KiB blocks, 16-byte loads, "
+                         "two blocks per wavefront in flight, median of 10", **out)
+
+
 GRAPH_CASES = (("decode_step_graph_b1", 1, (256, 1024)), ("decode_step_graph_b4", 4, (1024, 4096)))
 DECODE_CPU_S = 4.0   # seconds of oracle time per decode workload sample
 
@@ -595,7 +627,7 @@ def cpu_baseline(target_s=10.0):
 
 SECTIONS = ("prefill", "prefill_noncausal", "prefill_f32", "prefill_paged", "decode_mha",
             "decode_gqa", "decode_mha_fp8", "decode_gqa_fp8", "cascade", "cascade_fp8", "graph",
-            "flat_gemm")
+            "flat_gemm", "hbm_read")
 
 
 def main():
@@ -646,6 +678,7 @@ def main():
             "cascade_fp8": lambda: bench_cascade(K, W, fp8=True),
             "graph": lambda: {k: bench_graph_decode(K, W, B, lr) for k, B, lr in GRAPH_CASES},
             "flat_gemm": lambda: bench_flat_gemm(K, W),
+            "hbm_read": lambda: bench_hbm_read(),
         }[args.only]
         log(f"{args.only} ...")
         print(json.dumps(run()), flush=True)
@@ -662,7 +695,12 @@ def main():
     log(f"  non-causal: {noncausal['tflops']:.1f} TFLOP/s")
     f32_mode = bench_prefill_f32(K, W)
     log(f"  fp32 test mode (B1 H1 T128 D64): {f32_mode['us']:.1f} us per launch")
+    ceiling = None
     if not args.prefill_only:
+        log("HBM read rate of plain loads (4 GiB, 4 KiB blocks) ...")
+        ceiling = bench_hbm_read()
+        log(f"  in order {ceiling['in_order_4k_blocks']['gbs']:.0f} GB/s, "
+            f"random {ceiling['random_4k_blocks']['gbs']:.0f} GB/s")
         log("chunked prefill against the paged cache ...")
         paged_prefill = bench_prefill_paged(K, W)
         log(f"  {paged_prefill['tflops']:.1f} TFLOP/s")
@@ -701,6 +739,15 @@ def main():
         cpu["decode"] = {k: v.pop("cpu_oracle") for k, v in decode.items() if "cpu_oracle" in v}
         log(f"  {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
 
+    if ceiling is not None:
+        top = ceiling["random_4k_blocks"]["gbs"]
+        for v in decode.values():
+            if "gbs" in v:
+                v["frac_of_read_ceiling"] = round(v["gbs"] / top, 4)
+        if flat is not None:
+            for r in flat["results"].values():
+                r["layer"]["frac_of_read_ceiling"] = round(r["layer"]["gbs"] / top, 4)
+
     line = {
         "metric": "prefill attn TFLOP/s + decode attn KV GB/s, % of MI355X roofline",
         "value": round(pre["tflops"], 2),
@@ -727,6 +774,7 @@ def main():
         "prefill_noncausal": noncausal,
         "prefill_f32_test_mode": f32_mode,
         "flat_gemm": flat,
+        "hbm_read_ceiling": ceiling,
     }
     print(json.dumps(line), flush=True)
 

@@ -425,6 +425,28 @@ int attn_flat_gemm(const void *a, const void *w, void *c, int m, int n, int k, i
                    int c_dtype, void *workspace, size_t workspace_bytes, void *stream,
                    const attn_flat_gemm_opts *opts);
 
+/*
+ * attn_probe_hbm_read -- measurement aid, not part of the attention path: a
+ * kernel that only reads, used to measure the HBM read rate that plain
+ * 16-byte vector loads reach on this GPU, the practical ceiling of the
+ * memory-bound paths above (decode, cascade, flat GEMM; "FlashInfer kernel
+ * library", section 7: profile to find the memory bottleneck).
+ *
+ *   buf      : device, n_blocks * attn_probe_block_bytes() bytes (4096),
+ *              16-byte aligned, read only
+ *   order    : device int32 [n_blocks] or NULL; block i of the walk is the
+ *              one at byte order[i] * 4096 (entries outside [0, n_blocks)
+ *              are clamped into it), NULL reads the blocks in place order
+ *   sink     : device, one uint32; written only when the XOR of all words
+ *              read equals one fixed value, so the loads cannot be elided
+ * Launches one kernel on `stream`; time it with events around the call.
+ * Errors: ATTN_E_SHAPE (n_blocks < 0), ATTN_E_NULL, ATTN_E_ARG (alignment),
+ * ATTN_E_HIP.
+ */
+int attn_probe_block_bytes(void);
+int attn_probe_hbm_read(const void *buf, const int32_t *order, int n_blocks, uint32_t *sink,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

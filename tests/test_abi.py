@@ -340,3 +340,14 @@ def test_flat_gemm_plan(lib):
     assert plan(1, 1, 0) == (1, 16)
     with pytest.raises(attn.AttnError):
         plan(65, 64, 256)
+
+
+def test_probe_checks(lib):
+    assert lib.attn_probe_block_bytes() == 4096
+    sink = ctypes.c_void_p(0x2000)
+    assert lib.attn_probe_hbm_read(FAKE, None, -1, sink, None) == E_SHAPE
+    assert lib.attn_probe_hbm_read(None, None, 0, None, None) == OK    # nothing to read
+    assert lib.attn_probe_hbm_read(None, None, 4, sink, None) == E_NULL
+    assert lib.attn_probe_hbm_read(FAKE, None, 4, None, None) == E_NULL
+    assert lib.attn_probe_hbm_read(ctypes.c_void_p(0x1008), None, 4, sink, None) == E_ARG
+    assert lib.attn_probe_hbm_read(FAKE, ctypes.c_void_p(0x3002), 4, sink, None) == E_ARG

@@ -39,7 +39,7 @@ SIGNATURES = {
                                _i, _i, _f, _vp]),
     "attn_decode_shared_prefix_fp8": (_i, [_vp, _vp, _vp, _f, _f, _vp, _i, _vp, _vp, _i, _i, _i,
                                            _i, _i, _i, _f, _vp, _sz, _vp]),
-    "attn_flat_gemm_plan": (_i, [_i, _i, _i, _i, _vp, _ip, _ip]),
+    "attn_flat_gemm_plan": (_i, [_i, _i, _i, _i, _vp, _ip, _ip, _ip]),
     "attn_flat_gemm_workspace_bytes": (_sz, [_i, _i, _i, _vp]),
     "attn_flat_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "attn_decode_paged_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
@@ -393,29 +393,37 @@ def attn_decode_shared_prefix_fp8(q, k_pages, v_pages, k_scale, v_scale, prefix_
 
 class FlatGemmOpts(ctypes.Structure):
     _fields_ = [("splits", ctypes.c_int), ("rows_per_workgroup", ctypes.c_int),
-                ("waves_per_workgroup", ctypes.c_int), ("reserved", ctypes.c_int * 5)]
+                ("waves_per_workgroup", ctypes.c_int), ("kernel", ctypes.c_int),
+                ("reserved", ctypes.c_int * 4)]
 
 
-def _fg_opts(splits, rows, waves=0):
-    return ctypes.byref(FlatGemmOpts(int(splits), int(rows), int(waves)))
+# attn_flat_gemm_opts.kernel
+FG_REGISTER, FG_LDS = 1, 2
 
 
-def attn_flat_gemm_plan(m, n, k, num_cus=0, splits=0, rows_per_workgroup=0):
-    """Host-only: (k slices, rows of W per workgroup) the planner picks for
-    C = A W^T."""
-    s, r = ctypes.c_int(0), ctypes.c_int(0)
-    _check(load().attn_flat_gemm_plan(m, n, k, num_cus, _fg_opts(splits, rows_per_workgroup),
-                                      ctypes.byref(s), ctypes.byref(r)), "attn_flat_gemm_plan")
-    return s.value, r.value
+def _fg_opts(splits, rows, waves=0, kernel=0):
+    return ctypes.byref(FlatGemmOpts(int(splits), int(rows), int(waves), int(kernel)))
 
 
-def attn_flat_gemm_workspace_bytes(m, n, k, splits=0, rows_per_workgroup=0, waves_per_workgroup=0):
+def attn_flat_gemm_plan(m, n, k, num_cus=0, splits=0, rows_per_workgroup=0, kernel=0):
+    """Host-only: (k slices, rows of W per workgroup, kernel) the planner
+    picks for C = A W^T (kernel FG_REGISTER or FG_LDS)."""
+    s, r, kn = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().attn_flat_gemm_plan(m, n, k, num_cus,
+                                      _fg_opts(splits, rows_per_workgroup, 0, kernel),
+                                      ctypes.byref(s), ctypes.byref(r), ctypes.byref(kn)),
+           "attn_flat_gemm_plan")
+    return s.value, r.value, kn.value
+
+
+def attn_flat_gemm_workspace_bytes(m, n, k, splits=0, rows_per_workgroup=0, waves_per_workgroup=0,
+                                   kernel=0):
     return load().attn_flat_gemm_workspace_bytes(
-        m, n, k, _fg_opts(splits, rows_per_workgroup, waves_per_workgroup))
+        m, n, k, _fg_opts(splits, rows_per_workgroup, waves_per_workgroup, kernel))
 
 
 def attn_flat_gemm(a, w, c, splits=0, rows_per_workgroup=0, waves_per_workgroup=0,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, kernel=0):
     """C = A W^T: a bf16 [m, k], w bf16 [n, k], c bf16 or fp32 [m, n]."""
     for t, nm in ((a, "a"), (w, "w"), (c, "c")):
         _dense(t, nm)
@@ -427,13 +435,14 @@ def attn_flat_gemm(a, w, c, splits=0, rows_per_workgroup=0, waves_per_workgroup=
         raise ValueError("shape mismatch")
     if a.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
         raise TypeError("a and w must be bf16")
-    need = attn_flat_gemm_workspace_bytes(m, n, k, splits, rows_per_workgroup, waves_per_workgroup)
+    need = attn_flat_gemm_workspace_bytes(m, n, k, splits, rows_per_workgroup, waves_per_workgroup,
+                                          kernel)
     if workspace is None and need:
         workspace = _workspace(need, a.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().attn_flat_gemm(_p(a), _p(w), _p(c), m, n, k, BF16, _dtype(c), _p(workspace),
                                  ws_bytes, _stream(stream),
-                                 _fg_opts(splits, rows_per_workgroup, waves_per_workgroup)),
+                                 _fg_opts(splits, rows_per_workgroup, waves_per_workgroup, kernel)),
            "attn_flat_gemm")
 
 

@@ -105,21 +105,78 @@ void* device_scratch() {
 //    batch of 32-wide k steps (two with 64 rows).
 constexpr int kFgMaxM = 64;
 constexpr int kFgMaxK = 1 << 22;
+constexpr int kFgLdsMaxK = 1 << 20;   // LDS-tiled kernel: 256 rows x k x 2 bytes stay in one descriptor
 constexpr int kFgWaves = 4;
 constexpr int kFgResident = 4;     // 4-wavefront workgroups resident per CU
+constexpr int kFgChunk = 64;       // k per chunk of the LDS-tiled kernel
+
+// The LDS-tiled kernel (m > 16): rows of W per workgroup and k slices.
+// Measured on the Llama2-7B decode projections at m = 32, 48 and 64 (rows
+// 64 / 128 / 256 against 1 .. 16 slices): 64 rows, or 128 on the widest
+// weight (gate_up, n = 22016), with slices doubled until the grid holds at
+// least two workgroups per CU, were the fastest or within 4% of it (m = 64:
+// qkv 28.1 us with 4 slices, o 14.5 with 8, gate_up 45.9 with 128 rows and
+// 4, down 26.4 with 8).  Every slice keeps at least 4 chunks.
+void flat_gemm_lds_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* o,
+                        int* rows, int* splits, int* chunks_per_split) {
+    const int nchunks = std::max(1, (k + kFgChunk - 1) / kFgChunk);
+    int tr = (o && o->rows_per_workgroup) ? o->rows_per_workgroup : 0;
+    if (!tr) tr = n >= 16384 ? 128 : 64;
+    const long tiles = (n + tr - 1) / tr;
+    int s = (o && o->splits) ? o->splits : 0;
+    if (!s) {
+        s = 1;
+        while (tiles * s < 2L * num_cus && s < nchunks / 4) s *= 2;
+        s = std::max(1, std::min(s, std::max(1, nchunks / 4)));
+    }
+    s = std::max(1, std::min(s, nchunks));
+    const int cps = (nchunks + s - 1) / s;
+    *rows = tr;
+    *chunks_per_split = cps;
+    *splits = (nchunks + cps - 1) / cps;
+    (void)m;
+}
 
 int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* o, int* splits,
-                   int* steps_per_split, int* row_blocks, int* waves) {
+                   int* steps_per_split, int* row_blocks, int* waves, int* lds_rows = nullptr,
+                   int* chunks_per_split = nullptr) {
     if (m < 0 || n < 0 || k < 0) return ATTN_E_SHAPE;
-    if (o && (o->splits < 0 || o->rows_per_workgroup < 0 || o->waves_per_workgroup < 0))
+    if (o && (o->splits < 0 || o->rows_per_workgroup < 0 || o->waves_per_workgroup < 0 ||
+              o->kernel < 0))
         return ATTN_E_SHAPE;
     if (m > kFgMaxM || k > kFgMaxK || k % 8) return ATTN_E_UNSUPPORTED;
-    if (o && o->rows_per_workgroup && o->rows_per_workgroup != 16 && o->rows_per_workgroup != 32 &&
-        o->rows_per_workgroup != 64)
-        return ATTN_E_UNSUPPORTED;
+    if (o && o->kernel > 2) return ATTN_E_UNSUPPORTED;
+    const int fr = o ? o->rows_per_workgroup : 0;
+    if (fr && fr != 16 && fr != 32 && fr != 64 && fr != 128 && fr != 256) return ATTN_E_UNSUPPORTED;
     if (o && o->waves_per_workgroup && o->waves_per_workgroup != 4 && o->waves_per_workgroup != 8)
         return ATTN_E_UNSUPPORTED;
     if (num_cus <= 0) num_cus = attn::device_cus();
+    // which kernel: forced, else the LDS-tiled one for m > 16 unless the
+    // options only fit the register-streaming one
+    const int fk = o ? o->kernel : 0;
+    const int fw = o ? o->waves_per_workgroup : 0;
+    bool lds;
+    if (fk == 2) {
+        if (m <= 16 || k > kFgLdsMaxK || (fr && fr < 64) || fw == 8) return ATTN_E_UNSUPPORTED;
+        lds = true;
+    } else if (fk == 1) {
+        if (fr > 64) return ATTN_E_UNSUPPORTED;
+        lds = false;
+    } else {
+        lds = fr > 64 || (m > 16 && k <= kFgLdsMaxK && !(fr && fr < 64) && fw != 8);
+    }
+    if (lds) {
+        int tr = 0, cps = 0;
+        flat_gemm_lds_plan(m, n, k, num_cus, o, &tr, splits, &cps);
+        *steps_per_split = 0;
+        *row_blocks = tr / 16;
+        *waves = 4;
+        if (lds_rows) *lds_rows = tr;
+        if (chunks_per_split) *chunks_per_split = cps;
+        return ATTN_OK;
+    }
+    if (lds_rows) *lds_rows = 0;
+    if (chunks_per_split) *chunks_per_split = 0;
     const int nw = (o && o->waves_per_workgroup) ? o->waves_per_workgroup : kFgWaves;
     int rb;
     if (o && o->rows_per_workgroup)
@@ -540,11 +597,14 @@ int attn_decode_shared_prefix_fp8(const void* q, const void* k_pages, const void
 }
 
 int attn_flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* opts,
-                        int* splits, int* rows_per_workgroup) {
+                        int* splits, int* rows_per_workgroup, int* kernel) {
     if (!splits || !rows_per_workgroup) return ATTN_E_NULL;
-    int sps = 0, rb = 0, nw = 0;
-    const int rc = flat_gemm_plan(m, n, k, num_cus, opts, splits, &sps, &rb, &nw);
-    if (rc == ATTN_OK) *rows_per_workgroup = 16 * rb;
+    int sps = 0, rb = 0, nw = 0, lr = 0, cps = 0;
+    const int rc = flat_gemm_plan(m, n, k, num_cus, opts, splits, &sps, &rb, &nw, &lr, &cps);
+    if (rc == ATTN_OK) {
+        *rows_per_workgroup = 16 * rb;
+        if (kernel) *kernel = lr > 0 ? 2 : 1;
+    }
     return rc;
 }
 
@@ -558,8 +618,8 @@ int attn_flat_gemm(const void* a, const void* w, void* c, int m, int n, int k, i
                    int c_dtype, void* workspace, size_t workspace_bytes, void* stream,
                    const attn_flat_gemm_opts* opts) {
     if (dtype != ATTN_BF16 || !dtype_ok(c_dtype)) return ATTN_E_UNSUPPORTED;
-    int s = 0, sps = 0, rb = 0, nw = 0;
-    const int rc = flat_gemm_plan(m, n, k, 0, opts, &s, &sps, &rb, &nw);
+    int s = 0, sps = 0, rb = 0, nw = 0, lr = 0, cps = 0;
+    const int rc = flat_gemm_plan(m, n, k, 0, opts, &s, &sps, &rb, &nw, &lr, &cps);
     if (rc != ATTN_OK) return rc;
     if (m == 0 || n == 0) return ATTN_OK;
     if (!c || (k > 0 && (!a || !w))) return ATTN_E_NULL;
@@ -579,6 +639,8 @@ int attn_flat_gemm(const void* a, const void* w, void* c, int m, int n, int k, i
     p.steps_per_split = sps;
     p.row_blocks = rb;
     p.waves = nw;
+    p.lds_rows = lr;
+    p.chunks_per_split = cps;
     p.out_f32 = c_dtype == ATTN_F32;
     return check_hip(attn::launch_flat_gemm(p, (hipStream_t)stream));
 }

@@ -39,6 +39,8 @@
 
 #include <algorithm>
 
+#define LDS_AS __attribute__((address_space(3)))
+
 namespace attn {
 
 namespace {
@@ -158,6 +160,207 @@ __global__ __launch_bounds__(NW * 64) void flat_gemm_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-tiled variant for m > 16 (two to four token tiles).
+//
+// With 64 rows of W per workgroup the register-streaming kernel above reads
+// as many bytes of A (from L2) as of W, and every W load instruction touches
+// 16 rows x 64 bytes; at m = 64 both keep it near 2.5 TB/s.  Here a
+// workgroup owns TR = 64, 128 or 256 rows of W (RBW 16-row blocks per
+// wavefront) and walks its k range in chunks of 64: the chunk's W tile
+// [TR][64] and A tile [64][64] go from HBM straight into LDS (buffer loads
+// with the LDS destination; each load instruction fills 1 KiB of LDS from
+// 16-byte granules of consecutive rows), double-buffered, and all four
+// wavefronts take their MFMA operands from the one A tile.  A is then read
+// once per TR rows, W in whole 128-byte row pieces.
+//
+// LDS rows are 128 bytes (8 granules of 16 bytes); granule p of row r sits
+// at position p ^ ((r / 2) mod 8), so the 16 rows one operand read spans hit
+// 16 distinct 16-byte bank groups.  The loads fetch the global granule that
+// belongs at each LDS position.  Granules past k (k is a multiple of 8, so a
+// granule is all in or all out), rows past n and tokens past m get an offset
+// beyond their descriptor and land as zeros.
+//
+// Per chunk a wavefront runs 2 k steps x RBW row blocks x MT token tiles of
+// v_mfma_f32_16x16x32_bf16 (A operand W from LDS, B operand A from LDS).
+// Each wavefront owns its rows outright, so it writes its results with no
+// cross-wavefront reduction: C (or, with k slices, fp32 partials that
+// flat_gemm_reduce_kernel adds in slice order).
+constexpr int kKC = 64;                  // k per chunk (two 32-wide MFMA steps)
+constexpr int kRowBytes = 2 * kKC;       // bytes of one row of a chunk tile
+
+__device__ __forceinline__ int fg_swz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ void fg_lds_load16(__amdgpu_buffer_rsrc_t r, unsigned char LDS_AS* dst,
+                                              int off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void LDS_AS*)dst, 16, off, 0, 0, 0);
+}
+
+template <int MT, int RBW, bool OUT_F32>
+__global__ __launch_bounds__(256) void flat_gemm_lds_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w, void* __restrict__ c,
+    float* __restrict__ ws, int m, int n, int k, int splits, int chunks_per_split) {
+    constexpr int TR = 64 * RBW;                  // rows of W per workgroup
+    constexpr int WT = TR * kRowBytes;            // bytes of a W chunk tile
+    constexpr int AT = 64 * kRowBytes;            // bytes of an A chunk tile (64 token rows)
+    constexpr int WL = WT / 4096;                 // W loads per thread per chunk
+    constexpr int AL = AT / 4096;                 // A loads per thread per chunk
+    // two stages, each its own LDS object, so that reads of one stage wait
+    // only for the loads into that stage
+    __shared__ __attribute__((aligned(1024))) unsigned char w_st0[WT];
+    __shared__ __attribute__((aligned(1024))) unsigned char w_st1[WT];
+    __shared__ __attribute__((aligned(1024))) unsigned char a_st0[AT];
+    __shared__ __attribute__((aligned(1024))) unsigned char a_st1[AT];
+    unsigned char LDS_AS* const sW[2] = {(unsigned char LDS_AS*)w_st0, (unsigned char LDS_AS*)w_st1};
+    unsigned char LDS_AS* const sA[2] = {(unsigned char LDS_AS*)a_st0, (unsigned char LDS_AS*)a_st1};
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g = lane >> 4;
+
+    const int tile = blockIdx.x / splits, split = blockIdx.x % splits;
+    const int n0 = tile * TR;
+    const int rows = min(TR, n - n0);
+    const int nchunks = (k + kKC - 1) / kKC;
+    const int c0 = split * chunks_per_split;
+    const int c1 = min(nchunks, c0 + chunks_per_split);
+
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(w + (size_t)n0 * k), (short)0, rows * k * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a, (short)0, m * k * 2, kRsrcWord3);
+
+    // this thread's granules: g = tid + 256 j sits at LDS byte 16 g (row g / 8,
+    // position g % 8) and holds global granule (g % 8) ^ swz(row) of the row
+    int w_row[WL], w_gp[WL], a_row[AL], a_gp[AL];
+#pragma unroll
+    for (int j = 0; j < WL; j++) {
+        const int gi = tid + 256 * j;
+        w_row[j] = gi >> 3;
+        w_gp[j] = (gi & 7) ^ fg_swz(gi >> 3);
+    }
+#pragma unroll
+    for (int j = 0; j < AL; j++) {
+        const int gi = tid + 256 * j;
+        a_row[j] = gi >> 3;
+        a_gp[j] = (gi & 7) ^ fg_swz(gi >> 3);
+    }
+    // loads of chunk ch into stage st (every thread issues WL + AL loads)
+    auto issue = [&](int ch, int st) {
+#pragma unroll
+        for (int j = 0; j < WL; j++) {
+            const int kk = ch * kKC + 8 * w_gp[j];
+            const int off = kk < k ? (w_row[j] * k + kk) * 2 : kOutOfRange;
+            fg_lds_load16(rw, sW[st] + 1024 * (wave + 4 * j), off);
+        }
+#pragma unroll
+        for (int j = 0; j < AL; j++) {
+            const int kk = ch * kKC + 8 * a_gp[j];
+            const int off = kk < k ? (a_row[j] * k + kk) * 2 : kOutOfRange;
+            fg_lds_load16(ra, sA[st] + 1024 * (wave + 4 * j), off);
+        }
+    };
+
+    f32x4 acc[RBW][MT];
+#pragma unroll
+    for (int r = 0; r < RBW; r++)
+#pragma unroll
+        for (int t = 0; t < MT; t++) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // operand reads: row block r of this wavefront (rows 16 (RBW wave + r) +
+    // col) and token tile t (tokens 16 t + col), k granule 4 s + g
+    auto compute = [&](int st) {
+        const unsigned char LDS_AS* sw = sW[st];
+        const unsigned char LDS_AS* sa = sA[st];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++) {
+            bf16x8 wf[RBW], af[MT];
+#pragma unroll
+            for (int r = 0; r < RBW; r++) {
+                const int row = 16 * (RBW * wave + r) + col;
+                wf[r] = *(const bf16x8 LDS_AS*)(sw + row * kRowBytes + 16 * ((4 * s2 + g) ^ fg_swz(row)));
+            }
+#pragma unroll
+            for (int t = 0; t < MT; t++) {
+                const int tok = 16 * t + col;
+                af[t] = *(const bf16x8 LDS_AS*)(sa + tok * kRowBytes + 16 * ((4 * s2 + g) ^ fg_swz(tok)));
+            }
+#pragma unroll
+            for (int r = 0; r < RBW; r++)
+#pragma unroll
+                for (int t = 0; t < MT; t++)
+                    acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[r], af[t], acc[r][t], 0, 0, 0);
+        }
+    };
+    // this thread's loads of the chunk issued last may stay in flight; the
+    // earlier chunk's have landed, and after the barrier every thread's have
+    auto wait_prev = [&]() {
+        if constexpr (WL + AL == 10) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+        else if constexpr (WL + AL == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    };
+    auto lds_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+    if (c1 > c0) {
+        issue(c0, 0);
+        int ch = c0;
+        // chunk ch in stage (ch - c0) % 2: its loads were issued one chunk
+        // earlier; the next chunk's loads go out before its MFMAs
+        for (; ch + 1 < c1; ch += 2) {
+            issue(ch + 1, 1);
+            wait_prev();
+            compute(0);
+            lds_barrier();                 // stage 0 is rewritten next
+            if (ch + 2 < c1) issue(ch + 2, 0);
+            if (ch + 2 < c1) wait_prev();
+            else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            compute(1);
+            lds_barrier();                 // stage 1 is rewritten next
+        }
+        if (ch < c1) {                     // an odd count: the last chunk, in stage 0
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            compute(0);
+        }
+    }
+
+    // C^T block (row block r, token tile t): lane l holds rows 4 g + q of the
+    // block for token 16 t + col, i.e. 4 consecutive columns of C, stored as
+    // one vector when n and the output pointer allow it
+    const bool vec = (n & 3) == 0 &&
+                     ((splits > 1) || ((size_t)c & (OUT_F32 ? 15 : 7)) == 0);
+#pragma unroll
+    for (int r = 0; r < RBW; r++) {
+        const int nrow0 = n0 + 16 * (RBW * wave + r) + 4 * g;
+#pragma unroll
+        for (int t = 0; t < MT; t++) {
+            const int token = 16 * t + col;
+            if (token >= m) continue;
+            const f32x4 v = acc[r][t];
+            if (splits > 1) {
+                float* dst = ws + ((size_t)split * m + token) * n + nrow0;
+                if (vec && nrow0 + 3 < n) *(f32x4*)dst = v;
+                else
+                    for (int q = 0; q < 4; q++)
+                        if (nrow0 + q < n) dst[q] = v[q];
+            } else if (OUT_F32) {
+                float* dst = (float*)c + (size_t)token * n + nrow0;
+                if (vec && nrow0 + 3 < n) *(f32x4*)dst = v;
+                else
+                    for (int q = 0; q < 4; q++)
+                        if (nrow0 + q < n) dst[q] = v[q];
+            } else {
+                uint16_t* dst = (uint16_t*)c + (size_t)token * n + nrow0;
+                if (vec && nrow0 + 3 < n)
+                    *(u32x2*)dst = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                else
+                    for (int q = 0; q < 4; q++)
+                        if (nrow0 + q < n) dst[q] = f32_to_bf16(v[q]);
+            }
+        }
+    }
+}
+
 // C = the sum of the `splits` fp32 partials, added in slice order.
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void flat_gemm_reduce_kernel(const float* __restrict__ ws,
@@ -227,7 +430,38 @@ int flat_gemm_batch_steps(int m, int row_blocks) {
     return row_blocks == 4 ? batch_steps<4>(m) : row_blocks == 2 ? batch_steps<2>(m) : batch_steps<1>(m);
 }
 
+template <int MT, int RBW, bool OUT_F32>
+hipError_t go_lds(const FlatGemmArgs& p, hipStream_t stream) {
+    const int tiles = (p.n + 64 * RBW - 1) / (64 * RBW);
+    flat_gemm_lds_kernel<MT, RBW, OUT_F32><<<dim3(tiles * p.splits), 256, 0, stream>>>(
+        (const uint16_t*)p.a, (const uint16_t*)p.w, p.c, p.ws, p.m, p.n, p.k, p.splits,
+        p.chunks_per_split);
+    if (p.splits > 1) {
+        const long mn = (long)p.m * p.n;
+        const int blocks = (int)std::min<long>((mn + 255) / 256, 4096);
+        flat_gemm_reduce_kernel<OUT_F32><<<blocks, 256, 0, stream>>>(p.ws, p.c, mn, p.splits);
+    }
+    return hipGetLastError();
+}
+
+template <int RBW, bool OUT_F32>
+hipError_t go_lds_mt(const FlatGemmArgs& p, hipStream_t stream) {
+    switch ((p.m + 15) / 16) {
+        case 2: return go_lds<2, RBW, OUT_F32>(p, stream);
+        case 3: return go_lds<3, RBW, OUT_F32>(p, stream);
+        default: return go_lds<4, RBW, OUT_F32>(p, stream);
+    }
+}
+
+template <bool OUT_F32>
+hipError_t launch_lds(const FlatGemmArgs& p, hipStream_t stream) {
+    if (p.lds_rows == 256) return go_lds_mt<4, OUT_F32>(p, stream);
+    if (p.lds_rows == 128) return go_lds_mt<2, OUT_F32>(p, stream);
+    return go_lds_mt<1, OUT_F32>(p, stream);
+}
+
 hipError_t launch_flat_gemm(const FlatGemmArgs& p, hipStream_t stream) {
+    if (p.lds_rows > 0) return p.out_f32 ? launch_lds<true>(p, stream) : launch_lds<false>(p, stream);
     if (p.row_blocks == 4) return p.out_f32 ? go_mt<4, true>(p, stream) : go_mt<4, false>(p, stream);
     if (p.row_blocks == 2) return p.out_f32 ? go_mt<2, true>(p, stream) : go_mt<2, false>(p, stream);
     return p.out_f32 ? go_mt<1, true>(p, stream) : go_mt<1, false>(p, stream);

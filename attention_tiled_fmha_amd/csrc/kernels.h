@@ -125,6 +125,8 @@ struct FlatGemmArgs {
     int splits, steps_per_split;
     int row_blocks;
     int waves;          // wavefronts per workgroup: 4 or 8
+    int lds_rows;       // > 0: the LDS-tiled kernel with this many rows of W per workgroup
+    int chunks_per_split;   // LDS-tiled kernel: 64-wide k chunks per slice
     bool out_f32;
 };
 // k steps per register batch of the kernel instantiated for this m

@@ -397,29 +397,46 @@ int attn_decode_shared_prefix_fp8(const void *q, const void *k_pages, const void
  * Errors: ATTN_E_NULL, ATTN_E_SHAPE (negative sizes or options),
  * ATTN_E_UNSUPPORTED (m > 64, k not a multiple of 8 or above 2^22, dtype
  * other than bf16, c_dtype other than bf16 / fp32, rows_per_workgroup other
- * than 0, 16, 32, 64, waves_per_workgroup other than 0, 4, 8),
+ * than 0, 16, 32, 64, 128, 256, waves_per_workgroup other than 0, 4, 8,
+ * kernel above 2, and options that fit neither kernel: the LDS-tiled one
+ * forced with m <= 16, k > 2^20, rows below 64 or 8 wavefronts, the
+ * register-streaming one forced with rows above 64),
  * ATTN_E_WORKSPACE,
  * ATTN_E_ARG (alignment), ATTN_E_HIP.
  *
+ * Two kernels.  Register-streaming (m <= 16 by default): operands go from
+ * HBM straight into registers, 16, 32 or 64 rows of w per workgroup.
+ * LDS-tiled (m > 16 and k <= 2^20 by default): a workgroup owns 64, 128 or
+ * 256 rows of w and stages 64-wide k chunks of w and A in LDS, so one A
+ * tile serves all its rows.
+ *
  * attn_flat_gemm_plan: host-only.  The planner's choice for this shape on
- * num_cus compute units (<= 0: the current device's, else 256): rows of w per workgroup (16 for
- * m <= 8, and for m <= 16 on weights of at most 2^24 elements; 32 for
- * m <= 32 on weights with at least 1.25 blocks of 64 rows per CU; else 64,
- * so that one A fragment serves four row blocks) and k slices across
- * workgroups (at most 4, and only when the row blocks alone leave compute
- * units idle or unevenly loaded); workgroups are 4 wavefronts.  Fields of opts that are > 0 override the choice; splits is
- * clamped to the number of 32-wide k steps.
+ * num_cus compute units (<= 0: the current device's, else 256): the kernel
+ * (*kernel = 1 register-streaming, 2 LDS-tiled; kernel may be NULL), rows
+ * of w per workgroup and k slices across workgroups.  Register-streaming:
+ * 16 rows for m <= 8, and for m <= 16 on weights of at most 2^24 elements;
+ * 32 for m <= 32 on weights with at least 1.25 blocks of 64 rows per CU;
+ * else 64, so that one A fragment serves four row blocks; at most 4 slices,
+ * and only when the row blocks alone leave compute units idle or unevenly
+ * loaded.  LDS-tiled: 64 rows (128 when n >= 16384), slices doubled until
+ * the grid holds two workgroups per CU, each slice at least 4 chunks.
+ * Workgroups are 4 wavefronts.  Fields of opts that are > 0 override the
+ * choice; splits is clamped to the number of 32-wide k steps
+ * (register-streaming) or 64-wide chunks (LDS-tiled).
  * attn_flat_gemm_workspace_bytes returns 0 for an unsupported shape.
  */
 typedef struct {
     int splits;               /* 0 = planner; > 0 forces that many k slices       */
-    int rows_per_workgroup;   /* 0 = planner; 16, 32 or 64 forces it              */
-    int waves_per_workgroup;  /* 0 = planner; 4 or 8 forces it                    */
-    int reserved[5];
+    int rows_per_workgroup;   /* 0 = planner; 16, 32, 64 (register-streaming) or
+                                 64, 128, 256 (LDS-tiled) forces it               */
+    int waves_per_workgroup;  /* 0 = planner; 4 or 8 forces it (8: register-
+                                 streaming kernel only)                           */
+    int kernel;               /* 0 = planner; 1 register-streaming, 2 LDS-tiled   */
+    int reserved[4];
 } attn_flat_gemm_opts;
 
 int attn_flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts *opts,
-                        int *splits, int *rows_per_workgroup);
+                        int *splits, int *rows_per_workgroup, int *kernel);
 size_t attn_flat_gemm_workspace_bytes(int m, int n, int k, const attn_flat_gemm_opts *opts);
 int attn_flat_gemm(const void *a, const void *w, void *c, int m, int n, int k, int dtype,
                    int c_dtype, void *workspace, size_t workspace_bytes, void *stream,

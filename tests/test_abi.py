@@ -313,31 +313,51 @@ def test_flat_gemm_checks(lib):
 
 def test_flat_gemm_plan(lib):
     plan = attn.attn_flat_gemm_plan
+    R, L = attn.FG_REGISTER, attn.FG_LDS
     proj = ((12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008))   # qkv, o, gate_up, down
-    # m <= 8: 16 rows per workgroup.  qkv, o and down have 256..768 row
-    # blocks: one round of resident 4-wavefront workgroups, no k slices and
-    # no workspace; gate_up's 1376 fill 1.3 rounds, so k is sliced 4 ways
+    # m <= 8: register-streaming, 16 rows per workgroup.  qkv, o and down
+    # have 256..768 row blocks: one round of resident 4-wavefront
+    # workgroups, no k slices and no workspace; gate_up's 1376 fill 1.3
+    # rounds, so k is sliced 4 ways
     for m in (1, 8):
-        assert [plan(m, n, k) for n, k in proj] == [(1, 16), (1, 16), (4, 16), (1, 16)]
+        assert [plan(m, n, k) for n, k in proj] == [(1, 16, R), (1, 16, R), (4, 16, R), (1, 16, R)]
         assert attn.attn_flat_gemm_workspace_bytes(m, 4096, 4096) == 0
-    # m = 16: 64 rows, except on the 2^24-element o weight; m = 64: 64 rows.
-    # With 64 rows, 192 row blocks take no slices, 64 take 4, and 344
-    # (between one and two per CU) take 2
-    # gate_up's 344 blocks of 64 rows are >= 1.25 per CU: 32 rows for m <= 32
-    assert [plan(16, n, k) for n, k in proj] == [(1, 64), (1, 16), (1, 32), (4, 64)]
-    assert [plan(32, n, k) for n, k in proj] == [(1, 64), (4, 64), (1, 32), (4, 64)]
-    assert [plan(64, n, k) for n, k in proj] == [(1, 64), (4, 64), (2, 64), (4, 64)]
-    assert attn.attn_flat_gemm_workspace_bytes(64, 4096, 4096) == 4 * 64 * 4096 * 4
+    # m = 16: 64 rows, except on the 2^24-element o weight; gate_up's 344
+    # blocks of 64 rows are >= 1.25 per CU: 32 rows
+    assert [plan(16, n, k) for n, k in proj] == [(1, 64, R), (1, 16, R), (1, 32, R), (4, 64, R)]
+    # m > 16: LDS-tiled, 64 rows (128 on gate_up, n >= 16384), k slices
+    # doubled until the grid holds two workgroups per CU: qkv 192 tiles x 4,
+    # o and down 64 x 8, gate_up 172 x 4
+    for m in (17, 32, 48, 64):
+        assert [plan(m, n, k) for n, k in proj] == [(4, 64, L), (8, 64, L), (4, 128, L), (8, 64, L)]
+    assert attn.attn_flat_gemm_workspace_bytes(64, 4096, 4096) == 8 * 64 * 4096 * 4
+    # the register-streaming kernel forced at m = 64: 64 rows; 64 blocks of
+    # them take 4 slices
+    assert plan(64, 4096, 4096, kernel=R) == (4, 64, R)
     # a short, deep weight (16 row blocks of 16, 256 steps): slices double
     # while CUs stay idle and each wavefront keeps an 8-step batch
-    assert plan(16, 256, 8192, rows_per_workgroup=16) == (8, 16)
-    assert plan(16, 256, 8192, num_cus=16, rows_per_workgroup=16) == (1, 16)
-    # 64 rows over 16 steps: 2 slices keep two 1-step batches per wavefront
-    assert plan(64, 4096, 512) == (2, 64)
-    # forced counts are clamped to the number of 32-wide k steps
-    assert plan(4, 64, 256, splits=100) == (8, 16)
-    assert plan(4, 64, 256, splits=3) == (3, 16)
-    assert plan(1, 1, 0) == (1, 16)
+    assert plan(16, 256, 8192, rows_per_workgroup=16) == (8, 16, R)
+    assert plan(16, 256, 8192, num_cus=16, rows_per_workgroup=16) == (1, 16, R)
+    # 8 chunks of 64: at most 2 slices of 4 chunks (LDS-tiled); the
+    # register-streaming kernel over 16 steps: 2 slices keep two 1-step
+    # batches per wavefront
+    assert plan(64, 4096, 512) == (2, 64, L)
+    assert plan(64, 4096, 512, kernel=R) == (2, 64, R)
+    # forced counts are clamped to the number of k steps (chunks)
+    assert plan(4, 64, 256, splits=100) == (8, 16, R)
+    assert plan(4, 64, 256, splits=3) == (3, 16, R)
+    assert plan(40, 300, 2048, splits=64, rows_per_workgroup=64) == (32, 64, L)
+    assert plan(1, 1, 0) == (1, 16, R)
+    # rows above 64 select the LDS-tiled kernel; options it cannot take
+    assert plan(40, 300, 2048, rows_per_workgroup=256)[1:] == (256, L)
+    for bad in (dict(kernel=L, m=16), dict(kernel=L, rows_per_workgroup=32),
+                dict(kernel=R, rows_per_workgroup=128), dict(kernel=3)):
+        kw = dict(bad)
+        m = kw.pop("m", 40)
+        with pytest.raises(attn.AttnError):
+            plan(m, 300, 2048, **kw)
+    with pytest.raises(attn.AttnError):
+        plan(40, 300, (1 << 20) + 8, kernel=L)
     with pytest.raises(attn.AttnError):
         plan(65, 64, 256)
 

@@ -19,11 +19,15 @@ from gpu_util import dev, host, require_gpu
 pytestmark = pytest.mark.gpu
 
 
-def run(d, c_dtype="bf16", splits=0, cols=None, rows=0, waves=0):
+def run(d, c_dtype="bf16", splits=0, cols=None, rows=0, waves=0, kernel=0, c_offset=0):
     a, w = dev(d["a"]), dev(d["w"])
-    c = torch.full((d["m"], d["n"]), float("nan"),
-                   dtype=torch.bfloat16 if c_dtype == "bf16" else torch.float32, device="cuda")
-    attn.attn_flat_gemm(a, w, c, splits=splits, rows_per_workgroup=rows, waves_per_workgroup=waves)
+    # c_offset > 0: C starts that many elements into its buffer (a pointer
+    # aligned to 4 bytes only, which rules out the vector stores)
+    buf = torch.full((d["m"] * d["n"] + c_offset,), float("nan"),
+                     dtype=torch.bfloat16 if c_dtype == "bf16" else torch.float32, device="cuda")
+    c = buf[c_offset:].view(d["m"], d["n"])
+    attn.attn_flat_gemm(a, w, c, splits=splits, rows_per_workgroup=rows, waves_per_workgroup=waves,
+                        kernel=kernel)
     torch.cuda.synchronize()
     out = host(c)
     return out if cols is None else out[:, cols]
@@ -73,6 +77,36 @@ def test_flat_gemm_forced_splits(splits, rows, waves):
                   what=f"m {m} splits {splits} rows {rows} waves {waves} {c_dtype}")
 
 
+LDS_SHAPES = [(17, 33, 96), (32, 200, 520), (40, 1000, 1032), (48, 300, 264), (64, 1000, 1024),
+              (64, 4200, 2056), (33, 4096, 64)]
+
+
+@pytest.mark.parametrize("rows", [64, 128, 256])
+@pytest.mark.parametrize("splits", [0, 1, 3, 7])
+@pytest.mark.parametrize("shape", LDS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_flat_gemm_lds_kernel(shape, splits, rows):
+    """The LDS-tiled kernel (m > 16): 64, 128 or 256 rows of W per
+    workgroup, k in 64-wide chunks (ragged tails of 8 .. 56), k slices with
+    partials, n off every tile, 2 .. 4 token tiles; bf16 and fp32 C, and C
+    at a 4-byte offset (scalar stores)."""
+    require_gpu()
+    m, n, k = shape
+    d = wl.flat_gemm_inputs(m, n, k, 500 + m + n + k)
+    # offsets of 4 bytes: C keeps the 4-byte alignment the interface asks for
+    for c_dtype, off in (("bf16", 0), ("f32", 0), ("bf16", 2), ("f32", 1)):
+        check(run(d, c_dtype, splits=splits, rows=rows, kernel=attn.FG_LDS, c_offset=off), d,
+              c_dtype, what=f"{shape} splits {splits} rows {rows} {c_dtype} offset {off}")
+
+
+@pytest.mark.parametrize("m", [17, 40, 64])
+def test_flat_gemm_register_kernel_forced(m):
+    """The register-streaming kernel stays available for m > 16."""
+    require_gpu()
+    d = wl.flat_gemm_inputs(m, 1000, 1024, 600 + m)
+    for c_dtype in ("bf16", "f32"):
+        check(run(d, c_dtype, kernel=attn.FG_REGISTER), d, c_dtype, what=f"m {m} {c_dtype}")
+
+
 def test_flat_gemm_planner_splits_small_n():
     """A short, deep weight (n = 256, k = 8192) leaves CUs idle with whole-k
     row blocks, so the planner slices k; the result still matches."""
@@ -97,6 +131,10 @@ def test_flat_gemm_one_hot_selects_columns():
     want = wl.bf16_to_f32(d["w"][:, picks].T).astype(np.float64)
     for rows in (16, 64):
         assert np.array_equal(run(d, "f32", rows=rows), want), f"rows {rows}"
+    for rows in (128, 256):
+        for splits in (0, 3):
+            got = run(d, "f32", rows=rows, splits=splits, kernel=attn.FG_LDS)
+            assert np.array_equal(got, want), f"LDS rows {rows} splits {splits}"
 
 
 def test_flat_gemm_zero_k_and_empty():

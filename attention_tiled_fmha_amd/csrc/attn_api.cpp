@@ -151,19 +151,24 @@ int flat_gemm_plan(int m, int n, int k, int num_cus, const attn_flat_gemm_opts* 
     if (o && o->waves_per_workgroup && o->waves_per_workgroup != 4 && o->waves_per_workgroup != 8)
         return ATTN_E_UNSUPPORTED;
     if (num_cus <= 0) num_cus = attn::device_cus();
-    // which kernel: forced, else the LDS-tiled one for m > 16 unless the
-    // options only fit the register-streaming one
+    // which kernel: forced, else the LDS-tiled one for m > 16, and for
+    // m >= 8 on weights above 2^24 elements (measured at m = 8 / 16: qkv 22.7
+    // / 22.9 us against 25.6 / 27.3, gate_up 37.0 / 38.1 against 42.4 / 48.4,
+    // down 22.9 / 23.2 against 22.6 / 26.6; on the 2^24-element o weight and
+    // at m = 1 the register-streaming kernel stays ahead), unless the options
+    // only fit the register-streaming one
     const int fk = o ? o->kernel : 0;
     const int fw = o ? o->waves_per_workgroup : 0;
     bool lds;
     if (fk == 2) {
-        if (m <= 16 || k > kFgLdsMaxK || (fr && fr < 64) || fw == 8) return ATTN_E_UNSUPPORTED;
+        if (k > kFgLdsMaxK || (fr && fr < 64) || fw == 8) return ATTN_E_UNSUPPORTED;
         lds = true;
     } else if (fk == 1) {
         if (fr > 64) return ATTN_E_UNSUPPORTED;
         lds = false;
     } else {
-        lds = fr > 64 || (m > 16 && k <= kFgLdsMaxK && !(fr && fr < 64) && fw != 8);
+        const bool shape = m > 16 || (m >= 8 && (long)n * k > (1L << 24));
+        lds = fr > 64 || (shape && k <= kFgLdsMaxK && !(fr && fr < 64) && fw != 8);
     }
     if (lds) {
         int tr = 0, cps = 0;

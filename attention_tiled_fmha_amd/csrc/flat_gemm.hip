@@ -447,6 +447,7 @@ hipError_t go_lds(const FlatGemmArgs& p, hipStream_t stream) {
 template <int RBW, bool OUT_F32>
 hipError_t go_lds_mt(const FlatGemmArgs& p, hipStream_t stream) {
     switch ((p.m + 15) / 16) {
+        case 1: return go_lds<1, RBW, OUT_F32>(p, stream);
         case 2: return go_lds<2, RBW, OUT_F32>(p, stream);
         case 3: return go_lds<3, RBW, OUT_F32>(p, stream);
         default: return go_lds<4, RBW, OUT_F32>(p, stream);

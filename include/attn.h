@@ -399,16 +399,17 @@ int attn_decode_shared_prefix_fp8(const void *q, const void *k_pages, const void
  * other than bf16, c_dtype other than bf16 / fp32, rows_per_workgroup other
  * than 0, 16, 32, 64, 128, 256, waves_per_workgroup other than 0, 4, 8,
  * kernel above 2, and options that fit neither kernel: the LDS-tiled one
- * forced with m <= 16, k > 2^20, rows below 64 or 8 wavefronts, the
+ * forced with k > 2^20, rows below 64 or 8 wavefronts, the
  * register-streaming one forced with rows above 64),
  * ATTN_E_WORKSPACE,
  * ATTN_E_ARG (alignment), ATTN_E_HIP.
  *
- * Two kernels.  Register-streaming (m <= 16 by default): operands go from
- * HBM straight into registers, 16, 32 or 64 rows of w per workgroup.
- * LDS-tiled (m > 16 and k <= 2^20 by default): a workgroup owns 64, 128 or
- * 256 rows of w and stages 64-wide k chunks of w and A in LDS, so one A
- * tile serves all its rows.
+ * Two kernels.  Register-streaming: operands go from HBM straight into
+ * registers, 16, 32 or 64 rows of w per workgroup.  LDS-tiled (k <= 2^20):
+ * a workgroup owns 64, 128 or 256 rows of w and stages 64-wide k chunks of
+ * w and A in LDS, so one A tile serves all its rows.  The planner takes the
+ * LDS-tiled kernel for m > 16, and for m >= 8 on weights of more than 2^24
+ * elements.
  *
  * attn_flat_gemm_plan: host-only.  The planner's choice for this shape on
  * num_cus compute units (<= 0: the current device's, else 256): the kernel

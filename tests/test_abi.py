@@ -315,21 +315,26 @@ def test_flat_gemm_plan(lib):
     plan = attn.attn_flat_gemm_plan
     R, L = attn.FG_REGISTER, attn.FG_LDS
     proj = ((12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008))   # qkv, o, gate_up, down
-    # m <= 8: register-streaming, 16 rows per workgroup.  qkv, o and down
+    # m < 8: register-streaming, 16 rows per workgroup.  qkv, o and down
     # have 256..768 row blocks: one round of resident 4-wavefront
     # workgroups, no k slices and no workspace; gate_up's 1376 fill 1.3
     # rounds, so k is sliced 4 ways
-    for m in (1, 8):
+    for m in (1, 7):
         assert [plan(m, n, k) for n, k in proj] == [(1, 16, R), (1, 16, R), (4, 16, R), (1, 16, R)]
         assert attn.attn_flat_gemm_workspace_bytes(m, 4096, 4096) == 0
-    # m = 16: 64 rows, except on the 2^24-element o weight; gate_up's 344
-    # blocks of 64 rows are >= 1.25 per CU: 32 rows
-    assert [plan(16, n, k) for n, k in proj] == [(1, 64, R), (1, 16, R), (1, 32, R), (4, 64, R)]
-    # m > 16: LDS-tiled, 64 rows (128 on gate_up, n >= 16384), k slices
-    # doubled until the grid holds two workgroups per CU: qkv 192 tiles x 4,
-    # o and down 64 x 8, gate_up 172 x 4
+    # LDS-tiled for m > 16, and for m >= 8 on weights above 2^24 elements:
+    # 64 rows (128 on gate_up, n >= 16384), k slices doubled until the grid
+    # holds two workgroups per CU: qkv 192 tiles x 4, o and down 64 x 8,
+    # gate_up 172 x 4.  The 2^24-element o weight at m = 8 / 16 stays on the
+    # register-streaming kernel (16 rows)
+    for m in (8, 16):
+        assert [plan(m, n, k) for n, k in proj] == [(4, 64, L), (1, 16, R), (4, 128, L), (8, 64, L)]
     for m in (17, 32, 48, 64):
         assert [plan(m, n, k) for n, k in proj] == [(4, 64, L), (8, 64, L), (4, 128, L), (8, 64, L)]
+    # m = 16 on the register-streaming kernel: 64 rows, except on the o
+    # weight; gate_up's 344 blocks of 64 rows are >= 1.25 per CU: 32 rows
+    assert [plan(16, n, k, kernel=R) for n, k in proj] == [(1, 64, R), (1, 16, R), (1, 32, R),
+                                                           (4, 64, R)]
     assert attn.attn_flat_gemm_workspace_bytes(64, 4096, 4096) == 8 * 64 * 4096 * 4
     # the register-streaming kernel forced at m = 64: 64 rows; 64 blocks of
     # them take 4 slices
@@ -350,7 +355,8 @@ def test_flat_gemm_plan(lib):
     assert plan(1, 1, 0) == (1, 16, R)
     # rows above 64 select the LDS-tiled kernel; options it cannot take
     assert plan(40, 300, 2048, rows_per_workgroup=256)[1:] == (256, L)
-    for bad in (dict(kernel=L, m=16), dict(kernel=L, rows_per_workgroup=32),
+    assert plan(1, 300, 2048, kernel=L) == (8, 64, L)     # forced at m = 1: 5 tiles x 8 slices
+    for bad in (dict(kernel=L, rows_per_workgroup=32),
                 dict(kernel=R, rows_per_workgroup=128), dict(kernel=3)):
         kw = dict(bad)
         m = kw.pop("m", 40)

@@ -77,17 +77,17 @@ def test_flat_gemm_forced_splits(splits, rows, waves):
                   what=f"m {m} splits {splits} rows {rows} waves {waves} {c_dtype}")
 
 
-LDS_SHAPES = [(17, 33, 96), (32, 200, 520), (40, 1000, 1032), (48, 300, 264), (64, 1000, 1024),
-              (64, 4200, 2056), (33, 4096, 64)]
+LDS_SHAPES = [(1, 100, 264), (8, 300, 520), (16, 1000, 1032), (17, 33, 96), (32, 200, 520),
+              (40, 1000, 1032), (48, 300, 264), (64, 1000, 1024), (64, 4200, 2056), (33, 4096, 64)]
 
 
 @pytest.mark.parametrize("rows", [64, 128, 256])
 @pytest.mark.parametrize("splits", [0, 1, 3, 7])
 @pytest.mark.parametrize("shape", LDS_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_flat_gemm_lds_kernel(shape, splits, rows):
-    """The LDS-tiled kernel (m > 16): 64, 128 or 256 rows of W per
-    workgroup, k in 64-wide chunks (ragged tails of 8 .. 56), k slices with
-    partials, n off every tile, 2 .. 4 token tiles; bf16 and fp32 C, and C
+    """The LDS-tiled kernel: 64, 128 or 256 rows of W per workgroup, k in
+    64-wide chunks (ragged tails of 8 .. 56), k slices with partials, n off
+    every tile, 1 .. 4 token tiles (m from 1 to 64); bf16 and fp32 C, and C
     at a 4-byte offset (scalar stores)."""
     require_gpu()
     m, n, k = shape

@@ -30,11 +30,11 @@
 //
 // Every K or V fragment read from LDS feeds both blocks' MFMAs, so a
 // wavefront reads half as many LDS bytes per MFMA as with 32-row
-// wavefronts.  On gfx950 an MFMA and VALU work share the SIMD's issue
-// capacity whether they come from one wavefront or two, so the three jobs of
-// a step run interleaved in one instruction stream: step t issues the MFMAs
-// of S(t+1) and of O += P(t-1) V(t-1) while the VALU runs the softmax of
-// S(t).
+// wavefronts (with two of those per SIMD the softmax hides better under the
+// MFMAs, but the causal prefill ran slower: twice the LDS reads and
+// barriers).  The three jobs of a step run interleaved in one instruction
+// stream: step t issues the MFMAs of S(t+1) and of O += P(t-1) V(t-1) while
+// the VALU runs the softmax of S(t).
 //
 // K/V tiles go from HBM straight into LDS (buffer loads with the LDS
 // destination, no VGPR staging): step t issues the loads of its tile pair

@@ -137,6 +137,19 @@ def test_flat_gemm_one_hot_selects_columns():
             assert np.array_equal(got, want), f"LDS rows {rows} splits {splits}"
 
 
+def test_flat_gemm_lds_zero_k():
+    """k = 0 on the LDS-tiled kernel (planner's and forced, with slices):
+    C = 0 exactly."""
+    require_gpu()
+    for kw in (dict(), dict(kernel=attn.FG_LDS), dict(kernel=attn.FG_LDS, splits=3, rows_per_workgroup=256)):
+        c = torch.full((40, 300), float("nan"), device="cuda")
+        a = torch.empty((40, 0), dtype=torch.bfloat16, device="cuda")
+        w = torch.empty((300, 0), dtype=torch.bfloat16, device="cuda")
+        attn.attn_flat_gemm(a, w, c, **kw)
+        torch.cuda.synchronize()
+        assert (c == 0).all(), kw
+
+
 def test_flat_gemm_zero_k_and_empty():
     require_gpu()
     c = torch.full((3, 5), float("nan"), device="cuda")

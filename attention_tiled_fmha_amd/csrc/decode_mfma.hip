@@ -38,10 +38,11 @@
 // sequence holds many empty chunks (a batch of mixed lengths); as separate
 // workgroups each of them cost a launch and a cold length load, here a few
 // scalar instructions.  With chunks of at most 512 tokens an item holds two
-// consecutive chunks of one (sequence, kv head): the first chunk's state is
-// merged and written while the second chunk's first pages are in flight,
-// which saves one pipeline start per two chunks (measured 2-3% on 512-token
-// chunks of bf16, 4-5% of FP8); each chunk still gets its own partial state.
+// consecutive chunks of one (sequence, kv head), four over an FP8 cache: the
+// page pipeline runs on across the chunk boundaries, which saves one pipeline
+// start per chunk after the first (two chunks: measured 2-3% on 512-token
+// chunks of bf16, 4-5% of FP8; four FP8 chunks another 4%); each chunk still
+// gets its own partial state.
 #include "common.h"
 #include "kernels.h"
 
@@ -97,13 +98,16 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Chunks per work item: two consecutive chunks of one (sequence, kv head)
-// share an item when each chunk's pages split evenly over the wavefronts'
-// unit pairs and both fit one 64-entry table window; the page pipeline then
-// runs on across the chunk boundary.  The unified-max path keeps one.
+// Chunks per work item: consecutive chunks of one (sequence, kv head) share
+// an item when each chunk's pages split evenly over the wavefronts' unit
+// pairs and the item fits two 64-entry table windows; the page pipeline then
+// runs on across the chunk boundaries.  bf16 items hold two chunks, FP8
+// items (half the bytes per page, so the per-item start weighs twice as
+// much) four.  The unified-max path keeps one.
 __host__ __device__ inline int chunks_per_item(const DecodeArgs& a, bool fp8) {
     const int unit = fp8 ? 2 : 1;   // pages per unit
-    return (!a.unified && a.split_tokens <= 32 * kPage && a.split_tokens % (8 * kPage * unit) == 0) ? 2 : 1;
+    return (!a.unified && a.split_tokens <= 32 * kPage && a.split_tokens % (8 * kPage * unit) == 0)
+               ? (fp8 ? 4 : 2) : 1;
 }
 
 template <int D, bool FP8>
@@ -169,10 +173,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             }
         }
 
-        // the item's block-table entries (at most 64 pages): entry pg0 + lane,
-        // picked with v_readlane
+        // the item's block-table entries (at most 128 pages): entries pg0 + lane
+        // and pg0 + 64 + lane, picked with v_readlane
         const int tblv = lane < npg ? table[pg0 + lane] : 0;
-        auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(tblv, j); };
+        const int tblv2 = lane + 64 < npg ? table[pg0 + 64 + lane] : 0;
+        auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(j < 64 ? tblv : tblv2, j & 63); };
 
         // byte offsets of this lane's K and V elements in a page tile
         const int voff_k = col * D * EB + 8 * EB * grp;
@@ -383,12 +388,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             Unit ba, bb;
             load_u(ba, wave);
             int n = 0;
-            if (ncs == 2) {
-                // the first chunk is full and gives every wavefront the same,
-                // even number of units; its state is published to the first
-                // set while the second chunk's first loads are in flight, and
-                // merged with the second chunk's at the end of the item
-                const int nb = a.split_tokens / (kPage * PU * 4);
+            // every chunk but the last is full and gives every wavefront the
+            // same, even number of units
+            const int nb = a.split_tokens / (kPage * PU * 4);
+            if constexpr (FP8) {
+                // up to four chunks: each full chunk's state is published (the
+                // two sets alternate) and merged while the next chunk's first
+                // loads are in flight
+                for (int h = 0; h + 1 < ncs; h++) {
+                    for (; n < (h + 1) * nb; n += 2) {
+                        load_u(bb, wave + 4 * (n + 1));
+                        compute_u(ba, wave + 4 * n);
+                        load_u(ba, wave + 4 * (n + 2));
+                        compute_u(bb, wave + 4 * (n + 1));
+                    }
+                    publish(h & 1);
+                    finish(c + h, h & 1);
+                    m_run = exact ? -INFINITY : phi_l2;
+                    l_run = 0.f;
+                    smax = -INFINITY;
+    #pragma unroll
+                    for (int i = 0; i < NB; i++) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            } else if (ncs == 2) {
+                // the first chunk's state is published to the first set while
+                // the second chunk's first loads are in flight, and merged with
+                // the second chunk's at the end of the item (merging it right
+                // away measured 4% slower for bf16)
                 for (; n < nb; n += 2) {
                     load_u(bb, wave + 4 * (n + 1));
                     compute_u(ba, wave + 4 * n);
@@ -409,7 +435,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 load_u(ba, wave + 4 * (n + 2));
                 compute_u(bb, wave + 4 * (n + 1));
             }
-            publish(ncs == 2 ? 1 : 0);
+            publish(FP8 ? (ncs - 1) & 1 : (ncs == 2 ? 1 : 0));
         };
 
         if (a.unified) {
@@ -435,7 +461,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             pass(std::true_type{});
         }
 
-        for (int h = 0; h < ncs; h++) finish(c + h, h);
+        if constexpr (FP8) finish(c + ncs - 1, (ncs - 1) & 1);
+        else
+            for (int h = 0; h < ncs; h++) finish(c + h, h);
         __syncthreads();   // the published states are rewritten by the next item
     };
     // persistent workgroups walk the (chunk, kv head, sequence) items; empty

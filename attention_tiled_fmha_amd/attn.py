@@ -44,6 +44,9 @@ SIGNATURES = {
     "attn_flat_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp, _vp]),
     "attn_decode_paged_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                        _i, _i, _i, _i, _f, _vp]),
+    "attn_cascade_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "attn_decode_cascade": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                 _i, _i, _i, _i, _f, _f, _f, _vp, _sz, _vp]),
     "attn_probe_block_bytes": (_i, []),
     "attn_probe_hbm_read": (_i, [_vp, _vp, _i, _vp, _vp]),
 }
@@ -389,6 +392,63 @@ def attn_decode_shared_prefix_fp8(q, k_pages, v_pages, k_scale, v_scale, prefix_
         _p(q), _p(k_pages), _p(v_pages), float(k_scale), float(v_scale), _p(prefix_pages),
         int(prefix_len), _p(o), _p(lse), B, Hq, Hkv, D, page, _dtype(o), float(scale),
         _p(workspace), ws_bytes, _stream(stream)), "attn_decode_shared_prefix_fp8")
+
+
+def attn_cascade_workspace_bytes(batch, heads_q, heads_kv, head_dim, prefix_len, max_suffix_len,
+                                 dtype=BF16):
+    return load().attn_cascade_workspace_bytes(batch, heads_q, heads_kv, head_dim, prefix_len,
+                                               max_suffix_len, dtype)
+
+
+def attn_decode_cascade(q, k_pages, v_pages, prefix_pages, prefix_len, suffix_table, suffix_lens,
+                        o, lse=None, max_suffix_len=None, scale=None, k_scale=1.0, v_scale=1.0,
+                        workspace=None, stream=None):
+    """Shared-prefix cascade decode in one call (prefix stage, own-token
+    decode and one combine over both's chunk states): q, o [B,Hq,D]; pages
+    [P,Hkv,16,D] bf16, or uint8 E4M3 bytes (values k_scale * e4m3,
+    v_scale * e4m3); prefix_pages int32 [ceil(prefix_len/16)];
+    suffix_table int32 [B, max_pages]; suffix_lens int32 [B] or None."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (o, "o")):
+        _dense(t, n)
+    B, Hq, D = q.shape
+    P, Hkv, page, _ = k_pages.shape
+    if o.shape != q.shape or v_pages.shape != k_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bf16")
+    if k_pages.dtype == torch.uint8 and v_pages.dtype == torch.uint8:
+        dt = FP8_E4M3
+    elif k_pages.dtype == torch.bfloat16 and v_pages.dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise TypeError("the pages must both be bf16 or both uint8 (E4M3 bytes)")
+    if prefix_len > 0:
+        _dense(prefix_pages, "prefix_pages")
+        if prefix_pages.dtype != torch.int32 or prefix_pages.numel() * page < prefix_len:
+            raise ValueError("prefix_pages must be int32 covering prefix_len tokens")
+    _dense(suffix_table, "suffix_table")
+    if suffix_table.dtype != torch.int32 or suffix_table.dim() != 2 or suffix_table.shape[0] != B:
+        raise ValueError("suffix_table must be int32 [B, max_pages]")
+    if suffix_lens is not None:
+        _dense(suffix_lens, "suffix_lens")
+        if suffix_lens.dtype != torch.int32 or suffix_lens.shape != (B,):
+            raise ValueError("suffix_lens must be int32 [B]")
+    if max_suffix_len is None:
+        max_suffix_len = int(suffix_lens.max().item()) if (suffix_lens is not None and B) else 0
+    if lse is not None:
+        _dense(lse, "lse")
+        if lse.shape != (B, Hq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B, Hq]")
+    scale = D ** -0.5 if scale is None else scale
+    need = attn_cascade_workspace_bytes(B, Hq, Hkv, D, prefix_len, max_suffix_len, dt)
+    if workspace is None and need:
+        workspace = _workspace(need, q.device, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().attn_decode_cascade(
+        _p(q), _p(k_pages), _p(v_pages), _p(prefix_pages), int(prefix_len), _p(suffix_table),
+        _p(suffix_lens), _p(o), _p(lse), B, Hq, Hkv, D, page, suffix_table.shape[1],
+        int(max_suffix_len), dt, _dtype(o), float(scale), float(k_scale), float(v_scale),
+        _p(workspace), ws_bytes, _stream(stream)), "attn_decode_cascade")
 
 
 class FlatGemmOpts(ctypes.Structure):

@@ -650,6 +650,117 @@ int attn_flat_gemm(const void* a, const void* w, void* c, int m, int n, int k, i
     return check_hip(attn::launch_flat_gemm(p, (hipStream_t)stream));
 }
 
+// Cascade in one call: the prefix stage (the dense prefix kernel, its chunks
+// as the shared-prefix entry plans them) writes its chunk states to the first
+// slots of every row of the decode workspace, the sequences' own chunks (the
+// decode planner's split) follow them, and the decode's combine merges both,
+// so neither the prefix chunk combine nor the state merge runs on its own.
+static void cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_suffix_len,
+                         int* split, int* max_splits_s, int* prefix_chunk, int* prefix_slots) {
+    plan(batch, heads_kv, max_suffix_len, 0, 0, split, max_splits_s);
+    *prefix_chunk = 0;
+    *prefix_slots = 0;
+    if (prefix_len > 0) prefix_plan(batch, heads_q, heads_kv, prefix_len, prefix_chunk, prefix_slots);
+}
+
+size_t attn_cascade_workspace_bytes(int batch, int heads_q, int heads_kv, int head_dim,
+                                    int prefix_len, int max_suffix_len, int dtype) {
+    if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || heads_q % heads_kv || head_dim <= 0 ||
+        prefix_len < 0 || max_suffix_len < 0 || (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3))
+        return 0;
+    int split = 0, ms = 0, pc = 0, ps = 0;
+    cascade_plan(batch, heads_q, heads_kv, prefix_len, max_suffix_len, &split, &ms, &pc, &ps);
+    return decode_ws_bytes(batch, heads_q, head_dim, ps + ms);
+}
+
+int attn_decode_cascade(const void* q, const void* k_pages, const void* v_pages,
+                        const int32_t* prefix_pages, int prefix_len,
+                        const int32_t* suffix_table, const int32_t* suffix_lens, void* o,
+                        float* lse, int batch, int heads_q, int heads_kv, int head_dim,
+                        int page_size, int max_pages_per_seq, int max_suffix_len, int dtype,
+                        int o_dtype, float scale, float k_scale, float v_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    const bool fp8 = dtype == ATTN_FP8_E4M3;
+    if ((dtype != ATTN_BF16 && !fp8) || !dtype_ok(o_dtype)) return ATTN_E_UNSUPPORTED;
+    if (batch < 0 || heads_q <= 0 || heads_kv <= 0 || prefix_len < 0 || max_suffix_len < 0 ||
+        max_pages_per_seq < 0 || heads_q % heads_kv)
+        return ATTN_E_SHAPE;
+    if (!dim_ok(head_dim) || page_size != kPageSize) return ATTN_E_UNSUPPORTED;
+    if (heads_q / heads_kv > 16) return ATTN_E_UNSUPPORTED;   // the decode kernel's group limit
+    if ((long)max_pages_per_seq * page_size < max_suffix_len) return ATTN_E_SHAPE;
+    if (!fp8) k_scale = v_scale = 1.f;
+    if (!scale_ok(scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return ATTN_E_ARG;
+    if (batch == 0) return ATTN_OK;
+    if (!q || !k_pages || !v_pages || !o || (!prefix_pages && prefix_len > 0) ||
+        (!suffix_table && max_suffix_len > 0))
+        return ATTN_E_NULL;
+    if (!al16(q) || !al16(k_pages) || !al16(v_pages) || !al16(o) || !al16(workspace) ||
+        !al4(lse) || !al4(prefix_pages) || !al4(suffix_table) || !al4(suffix_lens))
+        return ATTN_E_ARG;
+    const long rows = (long)batch * (heads_q / heads_kv);
+    if (batch > kGridYZ || heads_kv > kGridYZ || (rows + 63) / 64 > kGridYZ)
+        return ATTN_E_UNSUPPORTED;
+    int split = 0, ms = 0, pc = 0, ps = 0;
+    cascade_plan(batch, heads_q, heads_kv, prefix_len, max_suffix_len, &split, &ms, &pc, &ps);
+    const int slots = ps + ms;
+    const size_t need = decode_ws_bytes(batch, heads_q, head_dim, slots);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_E_WORKSPACE;
+    const size_t nrow = (size_t)batch * heads_q * slots;
+    float* ws_o = need ? (float*)workspace : nullptr;
+    float* ws_lse = need ? (float*)((char*)workspace + align256(nrow * head_dim * sizeof(float)))
+                         : nullptr;
+
+    if (ps > 0) {
+        attn::PrefixArgs p{};
+        p.q = q;
+        p.k_pages = k_pages;
+        p.v_pages = v_pages;
+        p.pages = prefix_pages;
+        p.prefix_len = prefix_len;
+        p.ws_o = ws_o;
+        p.ws_lse = ws_lse;
+        p.R = batch;
+        p.Hq = heads_q;
+        p.Hkv = heads_kv;
+        p.D = head_dim;
+        p.chunk = pc;
+        p.out_f32 = o_dtype == ATTN_F32;
+        p.in_fp8 = fp8;
+        p.k_scale = k_scale;
+        p.v_scale = v_scale;
+        p.scale = scale;
+        p.ws_slots = slots;
+        const hipError_t e = attn::launch_prefix(p, (hipStream_t)stream);
+        if (e != hipSuccess) return check_hip(e);
+    }
+    attn::DecodeArgs a{};
+    a.q = q;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.block_table = suffix_table;
+    a.bt_stride = max_pages_per_seq;
+    a.kv_lens = suffix_lens;
+    a.fixed_len = max_suffix_len;
+    a.max_len = max_suffix_len;
+    a.o = o;
+    a.lse = lse;
+    a.ws_o = ws_o;
+    a.ws_lse = ws_lse;
+    a.B = batch;
+    a.Hq = heads_q;
+    a.Hkv = heads_kv;
+    a.D = head_dim;
+    a.split_tokens = split;
+    a.max_splits = slots;
+    a.out_f32 = o_dtype == ATTN_F32;
+    a.in_fp8 = fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.scale = scale;
+    a.prefix_slots = ps;
+    return check_hip(attn::launch_decode_mfma(a, (hipStream_t)stream));
+}
+
 int attn_probe_block_bytes(void) { return attn::hbm_probe_block_bytes(); }
 
 int attn_probe_hbm_read(const void* buf, const int32_t* order, int n_blocks, uint32_t* sink,

@@ -328,8 +328,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     const float l0 = pre ? ls[grp] : -INFINITY;
     const f32x4 o0 = pre ? os[(size_t)grp * LPR] : f32x4{0.f, 0.f, 0.f, 0.f};
     const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
-    const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
-    if (nsplit <= 1) return;  // written directly by the split kernel (uniform per workgroup)
+    // a cascade's rows hold prefix_slots prefix states before their own chunks'
+    const int nsplit = a.prefix_slots + (L + a.split_tokens - 1) / a.split_tokens;
+    // one chunk outside a cascade: written directly by the split kernel
+    // (uniform per workgroup)
+    if (nsplit <= 1 && a.prefix_slots == 0) return;
     float m = -INFINITY, l = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c = grp; c < nsplit; c += NG) {

@@ -127,14 +127,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ float s_o[2][4][kMaxG][D];
     const float phi_l2 = a.phi * kLog2e;
     const int cpi = chunks_per_item(a, FP8);
+    // in a cascade the first prefix_slots workspace slots of every row hold the
+    // prefix stage's chunk states: the sequence's chunks follow them, and every
+    // chunk (also a sequence's only one) goes to the workspace
+    const int slot0 = a.prefix_slots;
+    const bool cascade = slot0 > 0;
     auto item = [&](const int ci, const int kvh, const int b) {
         // lengths past the host bound are clamped, so no index leaves the planned
         // split range or the block-table row
         const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
         const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
 
-        if (L <= 0) {  // nothing to attend: O = 0, lse = -inf
-            if (ci == 0 && wave == 0) {
+        if (L <= 0) {  // nothing to attend: O = 0, lse = -inf (a cascade's
+                       // combine merges the prefix slots alone)
+            if (!cascade && ci == 0 && wave == 0) {
                 for (int g = 0; g < G; g++) {
                     const size_t row = (size_t)b * a.Hq + kvh * G + g;
                     for (int d = lane; d < D; d += kWave) {
@@ -233,13 +239,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 const float ov = ot * inv;
                 const float lse = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
                 const size_t row = (size_t)b * a.Hq + kvh * G + g;
-                if (nsplit == 1) {
+                if (nsplit == 1 && !cascade) {
                     if (a.out_f32) ((float*)a.o)[row * D + d] = ov;
                     else ((uint16_t*)a.o)[row * D + d] = f32_to_bf16(ov);
                     if (a.lse && d == 0) a.lse[row] = lse;
                 } else {
-                    a.ws_o[(row * a.max_splits + cc) * D + d] = ov;
-                    if (d == 0) a.ws_lse[row * a.max_splits + cc] = lse;
+                    a.ws_o[(row * a.max_splits + slot0 + cc) * D + d] = ov;
+                    if (d == 0) a.ws_lse[row * a.max_splits + slot0 + cc] = lse;
                 }
             }
         };
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     };
     // persistent workgroups walk the (chunk, kv head, sequence) items; empty
     // chunks of short sequences cost a few scalar instructions
-    const long n_items = (long)((a.max_splits + cpi - 1) / cpi) * a.Hkv * a.B;
+    const long n_items = (long)((a.max_splits - a.prefix_slots + cpi - 1) / cpi) * a.Hkv * a.B;
     for (long n = blockIdx.x; n < n_items; n += gridDim.x) {
         const int kvh = (int)(n % a.Hkv);
         const long r = n / a.Hkv;
@@ -485,7 +491,7 @@ bool decode_mfma_supported(const DecodeArgs& a) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
     const int cpi = chunks_per_item(a, a.in_fp8);
-    const long n_items = (long)((a.max_splits + cpi - 1) / cpi) * a.Hkv * a.B;
+    const long n_items = (long)((a.max_splits - a.prefix_slots + cpi - 1) / cpi) * a.Hkv * a.B;
     const dim3 grid((unsigned)std::min<long>(n_items, 8192));
     if (a.in_fp8) {
         if (a.D == 64) decode_mfma_kernel<64, true><<<grid, 256, 0, stream>>>(a);
@@ -495,7 +501,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
         else decode_mfma_kernel<128, false><<<grid, 256, 0, stream>>>(a);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.max_splits <= 1) return e;
+    if (e != hipSuccess || (a.max_splits <= 1 && a.prefix_slots == 0)) return e;
     return launch_decode_combine(a, stream);
 }
 

@@ -68,6 +68,12 @@ struct DecodeArgs {
     bool unified;
     float phi;
     int* fallback_count;
+    // cascade (matrix-core kernel only): workspace slots 0 .. prefix_slots - 1
+    // of every row hold the prefix stage's chunk states; sequence chunk c goes
+    // to slot prefix_slots + c (max_splits counts both, so no chunk is written
+    // to the output directly) and the combine merges prefix_slots + nsplit(b)
+    // slots of every row
+    int prefix_slots;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
@@ -104,6 +110,9 @@ struct PrefixArgs {
     bool in_fp8;
     float k_scale, v_scale;
     float scale;
+    // > 0: every chunk's state goes to workspace slot c of ws_slots per row
+    // (the first slots of a cascade's decode workspace), also for one chunk
+    int ws_slots;
 };
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
 

@@ -386,9 +386,10 @@ void prefix_mfma_kernel(PrefixArgs a) {
             if (n >= N) continue;
             const size_t row = qrow_of(kvh, n);
             const f32x4 v = *(const f32x4*)(s_o + rr * LD::STRIDE + d0);
-            if (n_chunks > 1) {
-                *(f32x4*)(a.ws_o + (row * n_chunks + c) * D + d0) = v;
-                if (d0 == 0) a.ws_lse[row * n_chunks + c] = s_m[rr];
+            if (n_chunks > 1 || a.ws_slots > 0) {
+                const size_t slot = row * (a.ws_slots > 0 ? a.ws_slots : n_chunks) + c;
+                *(f32x4*)(a.ws_o + slot * D + d0) = v;
+                if (d0 == 0) a.ws_lse[slot] = s_m[rr];
             } else {
                 if (a.out_f32) *(f32x4*)((float*)a.o + row * D + d0) = v;
                 else *(u32x2*)((uint16_t*)a.o + row * D + d0) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};

@@ -372,6 +372,53 @@ int attn_decode_shared_prefix_fp8(const void *q, const void *k_pages, const void
                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_decode_cascade -- shared-prefix cascade decode in one call.  Every
+ * request attends the prefix all requests share (prefix_len tokens through
+ * prefix_pages, as attn_decode_shared_prefix) and then its own tokens
+ * (suffix_lens[b] through row b of suffix_table, as attn_decode_paged); the
+ * result is attention over the prefix and the request's own tokens together,
+ * the cascade's two stages merged by their log-sum-exp ("FlashInfer kernel
+ * library ...", sections 2 and 4).  Three launches: the prefix stage of
+ * attn_decode_shared_prefix (each prefix page read once per kv head for all
+ * requests) writes its chunk states into the first slots of every row of the
+ * workspace, the paged decode of the requests' own tokens writes its chunk
+ * states after them, and one combine merges each row's slots.  The result
+ * equals attn_decode_shared_prefix + attn_decode_paged + attn_merge_states
+ * up to the order of the sums, without the prefix chunk combine and the
+ * merge as launches of their own.
+ *
+ *   q, o         : [batch, heads_q, head_dim]                 bf16 / `o_dtype`
+ *   k_pages,
+ *   v_pages      : [num_pages, heads_kv, page_size, head_dim]  bf16 (dtype
+ *                  ATTN_BF16) or OCP E4M3 bytes (ATTN_FP8_E4M3: values
+ *                  k_scale * e4m3 and v_scale * e4m3, finite and > 0; the
+ *                  scales are ignored for bf16)
+ *   prefix_pages : int32 [ceil(prefix_len / page_size)]
+ *   suffix_table : int32 [batch, max_pages_per_seq]
+ *   suffix_lens  : int32 [batch], clamped to [0, max_suffix_len], or NULL
+ *                  (every request has max_suffix_len own tokens)
+ *   lse          : fp32 [batch, heads_q], natural log, or NULL
+ *   workspace    : attn_cascade_workspace_bytes(...) bytes, 16-byte aligned
+ *                  (NULL when that is 0)
+ * heads_q / heads_kv <= 16, head_dim 64 or 128, page_size 16.
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE (negative sizes, heads_q % heads_kv,
+ * max_pages_per_seq * page_size < max_suffix_len), ATTN_E_UNSUPPORTED (dtype
+ * other than ATTN_BF16 / ATTN_FP8_E4M3, head_dim, page_size, more than 16
+ * query heads per kv head), ATTN_E_ARG (scales, alignment), ATTN_E_WORKSPACE,
+ * ATTN_E_HIP.
+ */
+size_t attn_cascade_workspace_bytes(int batch, int heads_q, int heads_kv, int head_dim,
+                                    int prefix_len, int max_suffix_len, int dtype);
+int attn_decode_cascade(const void *q, const void *k_pages, const void *v_pages,
+                        const int32_t *prefix_pages, int prefix_len,
+                        const int32_t *suffix_table, const int32_t *suffix_lens,
+                        void *o, float *lse,
+                        int batch, int heads_q, int heads_kv, int head_dim,
+                        int page_size, int max_pages_per_seq, int max_suffix_len,
+                        int dtype, int o_dtype, float scale, float k_scale, float v_scale,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Flat GEMM of the decode phase: C = A W^T.
  *
  * In decode the projections around attention (K/Q/V, O, the two FFN layers)

@@ -189,6 +189,50 @@ def test_shared_prefix_fp8_checks(lib):
                                          16, 2, 0, 0.1, None, 0, None) == E_UNSUP
 
 
+def test_cascade_checks(lib):
+    # every case here is rejected on the host, before anything is launched
+    f = lambda **kw: lib.attn_decode_cascade(
+        kw.get("q", FAKE), FAKE, FAKE, kw.get("pp", FAKE), kw.get("plen", 64),
+        kw.get("st", FAKE), None, FAKE, None, kw.get("B", 4), kw.get("Hq", 4), kw.get("Hkv", 4),
+        kw.get("D", 128), kw.get("page", 16), kw.get("mp", 8), kw.get("ml", 100),
+        kw.get("dt", 0), kw.get("odt", 0), kw.get("scale", 0.1), kw.get("ks", 1.0),
+        kw.get("vs", 1.0), kw.get("ws", None), 0, None)
+    assert f(q=None) == E_NULL
+    assert f(pp=None) == E_NULL
+    assert f(st=None) == E_NULL
+    assert f(plen=-1) == E_SHAPE
+    assert f(ml=-1) == E_SHAPE
+    assert f(Hq=6, Hkv=4) == E_SHAPE
+    assert f(mp=6) == E_SHAPE          # 6 pages hold 96 < 100 tokens
+    assert f(page=8) == E_UNSUP
+    assert f(D=96) == E_UNSUP
+    assert f(odt=2) == E_UNSUP
+    assert f(dt=1) == E_UNSUP          # fp32 caches are not taken
+    assert f(Hq=68, Hkv=4) == E_UNSUP  # 17 query heads per kv head
+    assert f(dt=2, ks=0.0) == E_ARG
+    assert f(dt=2, vs=float("inf")) == E_ARG
+    assert f(ks=0.0) == E_WS           # bf16 ignores the scales; no workspace given
+    assert f(scale=-2.0) == E_ARG
+    assert f(ws=ctypes.c_void_p(0x1002)) == E_ARG
+    assert f() == E_WS                 # prefix and own-chunk states need a workspace
+    assert f(B=0) == OK
+
+
+def test_cascade_workspace(lib):
+    # 64 requests, 32 heads, 4096-token prefix: the prefix stage's 4 chunks of
+    # 1024 tokens beside the planner's own chunks (1024 tokens: one per request)
+    s, n = attn.attn_decode_plan(64, 32, 1024)
+    rows = 64 * 32 * (4 + n)
+    expect = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert attn.attn_cascade_workspace_bytes(64, 32, 32, 128, 4096, 1024) == expect
+    # a prefix shorter than one chunk still has one slot
+    rows = 3 * 4 * (1 + attn.attn_decode_plan(3, 4, 100)[1])
+    expect = -(-rows * 64 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert attn.attn_cascade_workspace_bytes(3, 4, 4, 64, 15, 100) == expect
+    assert attn.attn_cascade_workspace_bytes(64, 32, 5, 128, 4096, 100) == 0   # bad group
+    assert attn.attn_cascade_workspace_bytes(64, 32, 32, 128, 4096, 100, dtype=1) == 0
+
+
 def test_misaligned_pointers(lib):
     # rejected on the host before any launch: tensors need 16-byte alignment,
     # lse / tables / lengths 4-byte

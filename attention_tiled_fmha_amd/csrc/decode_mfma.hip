@@ -33,6 +33,16 @@
 // once into a register and picked with v_readlane.  The four wavefronts'
 // states are merged through LDS at the end, as in the vector kernel.
 //
+// An FP8 (E4M3) cache is widened to bf16 in registers, exactly.  Its loads
+// are wider than the bf16 layout above would give: K is read as one 16-byte
+// load per lane per 64 dims (token l % 16, dims 16(l/16 + 4j) .. +15) and
+// S^T contracts the dims in that order (k-step s takes half s % 2 of load
+// s / 2; Q^T is loaded in the same order), and with D = 128 V is read as one
+// 8-byte load per token (dims 8(l % 16) .. +7 of token 4(l/16) + t), whose
+// two words give four 16-dim blocks each.  Against 8-byte K and 4-byte V
+// loads this took the FP8 GQA workload from 614 to 572 us and MHA from 218
+// to 210.
+//
 // The grid is persistent: a fixed number of workgroups walks the
 // (chunk, kv head, sequence) items chunk-major.  The grid over the longest
 // sequence holds many empty chunks (a batch of mixed lengths); as separate
@@ -69,8 +79,9 @@ struct PageBuf {
 };
 template <int D>
 struct PageBuf<D, true> {
-    u32x2 k[D / 32];          // K of k-step s: 8 E4M3 bytes, dims 32s + 8(l/16) ..
-    uint32_t v[4][D / 64];    // V: token 4(l/16) + t, dims 64c + 4(l%16) .. +3
+    u32x4 k[D / 64];          // K: 16 E4M3 bytes, token l%16, dims 16(l/16 + 4j) .. +15
+    uint32_t v[4][D / 64];    // V: token 4(l/16) + t; D = 128: dims 8(l%16) + 4c .. +3,
+                              // D = 64: dims 4(l%16) .. +3
 };
 
 // Two E4M3 bytes (the low or high half of w) -> two bf16, exactly (every
@@ -173,7 +184,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.Hq + kvh * G + min(col, G - 1)) * D;
     #pragma unroll
             for (int s = 0; s < KS; s++) {
-                u32x4 w = *(const u32x4*)(qrow + 32 * s + 8 * grp);
+                // FP8: k-step s contracts the dims 16(grp + 4(s/2)) + 8(s%2) .. +7,
+                // those of the half s%2 of the lane's 16-byte K load s/2
+                const int d0 = FP8 ? 16 * (grp + 4 * (s >> 1)) + 8 * (s & 1) : 32 * s + 8 * grp;
+                u32x4 w = *(const u32x4*)(qrow + d0);
                 if (col >= G) w = u32x4{0, 0, 0, 0};
                 qf[s] = __builtin_bit_cast(bf16x8, w);
             }
@@ -201,12 +215,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, bytes, kRsrcWord3);
             if constexpr (FP8) {
     #pragma unroll
-                for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b64(rk, voff_k + 32 * s, 0, 0);
+                for (int jj = 0; jj < D / 64; jj++)
+                    pb.k[jj] = __builtin_amdgcn_raw_buffer_load_b128(rk, col * D + 16 * (grp + 4 * jj), 0, 0);
     #pragma unroll
                 for (int t = 0; t < 4; t++)
     #pragma unroll
                     for (int cc = 0; cc < D / 64; cc++)
-                        pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D + 64 * cc, 0, 0);
+                        if constexpr (D == 128) {
+                            // one 8-byte load: dims 8 col .. +7 of token 4 grp + t
+                            if (cc == 0) {
+                                const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rv, (4 * grp + t) * D + 8 * col, 0, 0);
+                                pb.v[t][0] = w[0];
+                                pb.v[t][1] = w[1];
+                            }
+                        } else {
+                            pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D + 64 * cc, 0, 0);
+                        }
             } else {
     #pragma unroll
                 for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + 64 * s, 0, 0);
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 // K A operand of k-step ks (FP8: 8 bytes widened to bf16)
                 auto kop = [&](int ks) -> bf16x8 {
                     if constexpr (FP8) {
-                        const uint32_t w0 = pb.k[ks][0], w1 = pb.k[ks][1];
+                        const uint32_t w0 = pb.k[ks >> 1][2 * (ks & 1)], w1 = pb.k[ks >> 1][2 * (ks & 1) + 1];
                         return __builtin_bit_cast(bf16x8, u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
                                                                 e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)});
                     } else {
@@ -383,7 +407,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                     for (int r = 0; r < 4; r++) {
                         // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2 (bf16),
                         // 64(i/4) + 4(4grp + r) + i%4 (FP8)
-                        const int dim = FP8 ? 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3)
+                        const int dim = FP8 ? (D == 128 ? 8 * (4 * grp + r) + 4 * (i >> 2) + (i & 3)
+                                                        : 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3))
                                             : 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
                         s_o[set][wave][col][dim] = oacc[i][r];
                     }

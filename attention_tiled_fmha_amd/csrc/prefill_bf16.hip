@@ -68,12 +68,12 @@
 // alone (half the MFMAs and softmax), which removes most of the work above
 // the diagonal.  When there are at least two query tiles per CU, a
 // workgroup takes query tiles p and n - 1 - p of one (b, h) (equal causal
-// work per workgroup), in an order that alternates between neighbouring
-// heads so that the workgroups switch tiles (Q load, O store) at four
-// different times rather than two, and the workgroups of one (b, h) sit on
-// one XCD at the same time, so each K/V tile is fetched from HBM about once
-// and hit in that XCD's L2 afterwards.  Otherwise every workgroup takes one
-// query tile, heaviest first.
+// work per workgroup), the heavier one first, and the workgroups of one
+// (b, h) sit on one XCD at the same time: their heavier tiles walk the
+// shared keys in step, so one fetch from HBM serves both through that XCD's
+// L2.  The lighter tiles come later and fetch their keys again (an XCD's L2
+// holds about the last 8 key tiles of its 32 workgroups).  Otherwise every
+// workgroup takes one query tile, heaviest first.
 #include <type_traits>
 
 #include "common.h"
@@ -306,9 +306,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     }
 
     const int n_my = paired ? ((n_qtiles - 1 - unit) == unit ? 1 : 2) : 1;
-    // half of the pairs run their heavier tile first, so that the tile
-    // switches (Q load, O store) of the workgroups are spread over four times
-    const int first = (slot & 1) ? n_qtiles - 1 - unit : unit;
+    // the heavier tile of a pair first (the pairs of one (b, h) then share
+    // their longest runs of key tiles)
+    const int first = n_qtiles - 1 - unit;
     auto tile_of = [&](int u) {
         return paired ? (u == 0 ? first : n_qtiles - 1 - first) : n_qtiles - 1 - unit;
     };

@@ -23,7 +23,10 @@
 // the rescale multiplies them in place; with AGPR accumulators the compiler
 // copied all of them out and back around the rescale branch on every page.  K is loaded straight into operand order and V transposed in
 // registers, through per-page buffer descriptors that cover only the prefix
-// (the tail of the last page reads zeros).
+// (the tail of the last page reads zeros).  An FP8 cache is read with the
+// paged decode kernel's FP8 layout: 16-byte K loads over a permuted
+// contraction order (Q^T loaded in the same order) and, with D = 128, one
+// 8-byte V load per token.
 //
 // An item is (chunk of the prefix, kv head, block of 32 rows); a persistent
 // grid walks the items, kv head fastest, so the row blocks of one chunk and
@@ -74,8 +77,9 @@ struct PrefixPage {
 };
 template <int D>
 struct PrefixPage<D, true> {
-    u32x2 k[D / 32];          // K of k-step s: 8 E4M3 bytes, dims 32s + 8(l/16) ..
-    uint32_t v[4][D / 64];    // V: token 4(l/16) + t, dims 64c + 4(l%16) .. +3
+    u32x4 k[D / 64];          // K: 16 E4M3 bytes, token l%16, dims 16(l/16 + 4j) .. +15
+    uint32_t v[4][D / 64];    // V: token 4(l/16) + t; D = 128: dims 8(l%16) + 4c .. +3,
+                              // D = 64: dims 4(l%16) .. +3
 };
 
 // Two E4M3 bytes (the low or high half of w) -> two bf16, exactly.
@@ -84,12 +88,16 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// Head dimension of register r of O^T block i for lane group grp: bf16 pages
+// Head dimension of register r of O^T block i for lane group grp (row
+// m = 4 grp + r of the block, held by lane m of the V operand): bf16 pages
 // give blocks of even / odd dims of each 32-dim column, FP8 pages blocks of
-// dims 4k + i%4 of each 64-dim column.
-template <bool FP8>
+// dims 4m + i%4 of each 64-dim column, or with D = 128 (V operand lane m
+// holding dims 8m .. 8m + 7) dims 8m + i.
+template <int D, bool FP8>
 __device__ __forceinline__ int ot_dim(int i, int grp, int r) {
-    return FP8 ? 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3) : 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
+    if constexpr (!FP8) return 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
+    return D == 128 ? 8 * (4 * grp + r) + 4 * (i >> 2) + (i & 3)
+                    : 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3);
 }
 
 template <int D>
@@ -145,7 +153,10 @@ void prefix_mfma_kernel(PrefixArgs a) {
             const uint16_t* qr = (const uint16_t*)a.q + qrow_of(kvh, min(n, N - 1)) * D;
 #pragma unroll
             for (int s = 0; s < KS; s++) {
-                u32x4 w = *(const u32x4*)(qr + 32 * s + 8 * grp);
+                // FP8: k-step s contracts the dims 16(grp + 4(s/2)) + 8(s%2) .. +7,
+                // those of the half s%2 of the lane's 16-byte K load s/2
+                const int d0 = FP8 ? 16 * (grp + 4 * (s >> 1)) + 8 * (s & 1) : 32 * s + 8 * grp;
+                u32x4 w = *(const u32x4*)(qr + d0);
                 if (n >= N) w = u32x4{0, 0, 0, 0};
                 qf[j][s] = __builtin_bit_cast(bf16x8, w);
             }
@@ -163,12 +174,19 @@ void prefix_mfma_kernel(PrefixArgs a) {
                 __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, bytes, kRsrcWord3);
             if constexpr (FP8) {
 #pragma unroll
-                for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b64(rk, voff_k + 32 * s, 0, 0);
+                for (int jj = 0; jj < D / 64; jj++)
+                    pb.k[jj] = __builtin_amdgcn_raw_buffer_load_b128(rk, col * D + 16 * (grp + 4 * jj), 0, 0);
 #pragma unroll
-                for (int t = 0; t < 4; t++)
-#pragma unroll
-                    for (int cc = 0; cc < D / 64; cc++)
-                        pb.v[t][cc] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D + 64 * cc, 0, 0);
+                for (int t = 0; t < 4; t++) {
+                    if constexpr (D == 128) {
+                        // one 8-byte load: dims 8 col .. +7 of token 4 grp + t
+                        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rv, (4 * grp + t) * D + 8 * col, 0, 0);
+                        pb.v[t][0] = w[0];
+                        pb.v[t][1] = w[1];
+                    } else {
+                        pb.v[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v + t * D, 0, 0);
+                    }
+                }
             } else {
 #pragma unroll
                 for (int s = 0; s < KS; s++) pb.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + 64 * s, 0, 0);
@@ -197,7 +215,7 @@ void prefix_mfma_kernel(PrefixArgs a) {
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
                 if constexpr (FP8) {
-                    const uint32_t w0 = pb.k[ks][0], w1 = pb.k[ks][1];
+                    const uint32_t w0 = pb.k[ks >> 1][2 * (ks & 1)], w1 = pb.k[ks >> 1][2 * (ks & 1) + 1];
                     kf[ks] = __builtin_bit_cast(bf16x8, u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
                                                               e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)});
                 } else {
@@ -335,7 +353,7 @@ void prefix_mfma_kernel(PrefixArgs a) {
                 for (int i = 0; i < NB; i++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        o[(16 * j + col) * LD::STRIDE + ot_dim<FP8>(i, grp, r)] = oacc[j][i][r];
+                        o[(16 * j + col) * LD::STRIDE + ot_dim<D, FP8>(i, grp, r)] = oacc[j][i][r];
             }
         };
         auto take = [&](int slot) {
@@ -353,7 +371,7 @@ void prefix_mfma_kernel(PrefixArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; r++)
                         oacc[j][i][r] = wa * oacc[j][i][r] +
-                                        wb * o[(16 * j + col) * LD::STRIDE + ot_dim<FP8>(i, grp, r)];
+                                        wb * o[(16 * j + col) * LD::STRIDE + ot_dim<D, FP8>(i, grp, r)];
             }
         };
         if (wave >= 2) put(wave - 2);
@@ -375,7 +393,7 @@ void prefix_mfma_kernel(PrefixArgs a) {
                 for (int i = 0; i < NB; i++)
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        o[(16 * j + col) * LD::STRIDE + ot_dim<FP8>(i, grp, r)] = oacc[j][i][r] * inv;
+                        o[(16 * j + col) * LD::STRIDE + ot_dim<D, FP8>(i, grp, r)] = oacc[j][i][r] * inv;
             }
         }
         __syncthreads();

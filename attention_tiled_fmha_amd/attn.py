@@ -13,9 +13,13 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
+# the same interface with device-side index checks and an error word
+CHECKED_LIB_PATH = os.path.join(_PKG, "libattn_checked.so")
 
 BF16, F32, FP8_E4M3 = 0, 1, 2
+DEV_ERR_KV_LEN, DEV_ERR_PAGE = 1, 2      # the checked library's error-word bits
 _lib = None
+_libs = {}
 
 # Every symbol include/attn.h declares, with (restype, argtypes).
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -47,6 +51,9 @@ SIGNATURES = {
     "attn_cascade_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_decode_cascade": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                  _i, _i, _i, _i, _f, _f, _f, _vp, _sz, _vp]),
+    "attn_checked_build": (_i, []),
+    "attn_device_errors": (_i, [ctypes.POINTER(ctypes.c_uint), _i]),
+    "attn_device_pool_pages": (_i, [_vp, _sz, ctypes.POINTER(ctypes.c_int)]),
     "attn_probe_block_bytes": (_i, []),
     "attn_probe_hbm_read": (_i, [_vp, _vp, _i, _vp, _vp]),
 }
@@ -66,10 +73,17 @@ class DecodeOpts(ctypes.Structure):
                 ("fallback_count", ctypes.c_void_p), ("reserved", ctypes.c_int * 4)]
 
 
-def load(path=LIB_PATH):
-    """Load libattn.so and declare every exported signature."""
+def load(path=None):
+    """The library the calls of this module go to, with every exported
+    signature declared.  With no path: the one in use, else libattn.so, or
+    libattn_checked.so when the environment sets ATTN_CHECKED=1.  With a
+    path: that library, which then stays in use."""
     global _lib
-    if _lib is None:
+    if path is None:
+        if _lib is not None:
+            return _lib
+        path = CHECKED_LIB_PATH if os.environ.get("ATTN_CHECKED") == "1" else LIB_PATH
+    if path not in _libs:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build() or "
                                "python -m attention_tiled_fmha_amd.build")
@@ -78,8 +92,26 @@ def load(path=LIB_PATH):
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        _lib = lib
+        _libs[path] = lib
+    _lib = _libs[path]
     return _lib
+
+
+def device_errors(clear=True):
+    """The checked library's device error word (ATTN_DEV_ERR_* bits) after
+    the device has finished its work; clears it by default."""
+    flags = ctypes.c_uint(0)
+    _check(load().attn_device_errors(ctypes.byref(flags), int(clear)), "attn_device_errors")
+    return flags.value
+
+
+def device_pool_pages(pages):
+    """The page bound the checked library holds indices into `pages` to."""
+    n = ctypes.c_int(0)
+    page_bytes = pages[0].numel() * pages.element_size() if pages.shape[0] else 0
+    _check(load().attn_device_pool_pages(_p(pages), page_bytes, ctypes.byref(n)),
+           "attn_device_pool_pages")
+    return n.value
 
 
 def status_str(status):

@@ -1,10 +1,12 @@
-"""Build libattn.so (the gfx950 HIP kernels and their C ABI) in-tree.
+"""Build libattn.so (the gfx950 HIP kernels and their C ABI) in-tree, and
+its checked twin libattn_checked.so (the same sources with ATTN_CHECKED=1:
+device-side index checks with an error word).
 
     python -m attention_tiled_fmha_amd.build
 
 Each source is compiled with hipcc for gfx950 only, in parallel, then linked
-into attention_tiled_fmha_amd/libattn.so.  Packed-fp32 instruction selection
-is switched off for device code.
+into attention_tiled_fmha_amd/libattn.so (and libattn_checked.so).
+Packed-fp32 instruction selection is switched off for device code.
 """
 import os
 import subprocess
@@ -16,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+LIB_CHECKED = os.path.join(PKG, "libattn_checked.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
@@ -41,8 +44,8 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src, extra, objdir):
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
@@ -52,19 +55,28 @@ def _compile(src, extra):
     return obj
 
 
-def build(extra=(), verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+def _build_one(extra, out, objdir, verbose):
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(extra), objdir), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {out}")
+    return out
+
+
+def build(extra=(), verbose=False, checked=True):
+    """Build libattn.so and, with checked, libattn_checked.so."""
+    _build_one(list(extra), LIB, BUILD, verbose)
+    if checked:
+        _build_one(list(extra) + ["-DATTN_CHECKED=1"], LIB_CHECKED,
+                   os.path.join(BUILD, "checked"), verbose)
     return LIB
 
 

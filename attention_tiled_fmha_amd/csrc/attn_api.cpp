@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -84,6 +85,62 @@ void* device_scratch() {
         g_scratch_ptr[dev] = ptr;
     }
     return g_scratch_ptr[dev];
+}
+
+#if ATTN_CHECKED
+// The checked build's device error word (bits kDevErrKvLen, kDevErrPage),
+// one per GPU, reached like the scratch array through its per-device address.
+static __device__ unsigned int dev_errors;
+void* g_err_ptr[kMaxDevices] = {};
+#endif
+
+// Address of the current device's error word; NULL in the release build.
+unsigned* device_error_word() {
+#if ATTN_CHECKED
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_err_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(dev_errors)) != hipSuccess || !ptr) return nullptr;
+        g_err_ptr[dev] = ptr;
+    }
+    return (unsigned*)g_err_ptr[dev];
+#else
+    return nullptr;
+#endif
+}
+
+// Whole pages of page_bytes from p to the end of the device allocation that
+// holds p: the bound the checked build holds page indices to (INT_MAX when
+// the runtime knows no allocation at p).
+int pool_pages(const void* p, size_t page_bytes) {
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (!p || page_bytes == 0 ||
+        hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess || !base) {
+        (void)hipGetLastError();
+        return INT_MAX;
+    }
+    const size_t avail = (size_t)((const char*)base + size - (const char*)p);
+    return (int)std::min<size_t>(avail / page_bytes, INT_MAX);
+}
+
+// The checked build's error word and pool bound for a call over the pools
+// k_pages / v_pages of page_bytes per page (NULL and 0 in the release build,
+// where the kernels compile the checks away).
+void set_checks(unsigned** err, int* num_pages, const void* k_pages, const void* v_pages,
+                size_t page_bytes) {
+#if ATTN_CHECKED
+    *err = device_error_word();
+    *num_pages = std::min(pool_pages(k_pages, page_bytes), pool_pages(v_pages, page_bytes));
+#else
+    (void)k_pages;
+    (void)v_pages;
+    (void)page_bytes;
+    *err = nullptr;
+    *num_pages = 0;
+#endif
 }
 
 // Flat GEMM planning, from sweeps of (rows, wavefronts, k slices) over the
@@ -307,6 +364,8 @@ int decode_common(const void* q, const void* k_pages, const void* v_pages,
     a.unified = unified;
     a.phi = phi;
     a.fallback_count = fallback_count;
+    set_checks(&a.err, &a.num_pages, k_pages, v_pages,
+               (size_t)heads_kv * kPageSize * head_dim * (fp8 ? 1 : dtype == ATTN_F32 ? 4 : 2));
     // bf16 and FP8 caches go to the matrix-core kernel; fp32 caches and
     // chunks longer than it takes go to the vector kernel (no unified-max
     // mode, no FP8, G in {1, 2, 4, 8})
@@ -395,10 +454,13 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
         !al4(block_table) || !al4(kv_lens))
         return ATTN_E_ARG;
     if ((long)batch * heads_q * ((seq_q + 255) / 256) > 0x7fffffffL) return ATTN_E_UNSUPPORTED;
+    unsigned* err = nullptr;
+    int num_pages = 0;
+    set_checks(&err, &num_pages, k_pages, v_pages, (size_t)heads_kv * kPageSize * head_dim * 2);
     return check_hip(attn::launch_prefill_paged_bf16(q, k_pages, v_pages, block_table, kv_lens, o,
                                                      lse, batch, heads_q, heads_kv, seq_q,
                                                      head_dim, max_pages_per_seq, causal != 0,
-                                                     scale, (hipStream_t)stream));
+                                                     scale, (hipStream_t)stream, err, num_pages));
 }
 
 int attn_decode_plan(int batch, int heads_kv, int max_kv_len, int num_cus, int requested_split,
@@ -558,6 +620,8 @@ static int shared_prefix_common(const void* q, const void* k_pages, const void* 
     a.k_scale = k_scale;
     a.v_scale = v_scale;
     a.scale = scale;
+    set_checks(&a.err, &a.num_pages, k_pages, v_pages,
+               (size_t)heads_kv * kPageSize * head_dim * (fp8 ? 1 : 2));
     hipError_t e = attn::launch_prefix(a, (hipStream_t)stream);
     if (e != hipSuccess || n_chunks <= 1) return check_hip(e);
 
@@ -730,6 +794,8 @@ int attn_decode_cascade(const void* q, const void* k_pages, const void* v_pages,
         p.v_scale = v_scale;
         p.scale = scale;
         p.ws_slots = slots;
+        set_checks(&p.err, &p.num_pages, k_pages, v_pages,
+                   (size_t)heads_kv * kPageSize * head_dim * (fp8 ? 1 : 2));
         const hipError_t e = attn::launch_prefix(p, (hipStream_t)stream);
         if (e != hipSuccess) return check_hip(e);
     }
@@ -758,7 +824,39 @@ int attn_decode_cascade(const void* q, const void* k_pages, const void* v_pages,
     a.v_scale = v_scale;
     a.scale = scale;
     a.prefix_slots = ps;
+    set_checks(&a.err, &a.num_pages, k_pages, v_pages,
+               (size_t)heads_kv * kPageSize * head_dim * (fp8 ? 1 : 2));
     return check_hip(attn::launch_decode_mfma(a, (hipStream_t)stream));
+}
+
+int attn_checked_build(void) { return ATTN_CHECKED; }
+
+int attn_device_errors(unsigned int* flags, int clear) {
+#if ATTN_CHECKED
+    if (!flags) return ATTN_E_NULL;
+    unsigned* p = device_error_word();
+    if (!p) return ATTN_E_HIP;
+    unsigned v = 0;
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(&v, p, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+        return ATTN_E_HIP;
+    if (clear) {
+        const unsigned z = 0;
+        if (hipMemcpy(p, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return ATTN_E_HIP;
+    }
+    *flags = v;
+    return ATTN_OK;
+#else
+    (void)flags;
+    (void)clear;
+    return ATTN_E_UNSUPPORTED;
+#endif
+}
+
+int attn_device_pool_pages(const void* pages, size_t page_bytes, int* num_pages) {
+    if (!num_pages) return ATTN_E_NULL;
+    *num_pages = pool_pages(pages, page_bytes);
+    return ATTN_OK;
 }
 
 int attn_probe_block_bytes(void) { return attn::hbm_probe_block_bytes(); }

@@ -76,4 +76,34 @@ __device__ __forceinline__ void transpose4x4_bf16(const u32x2 rows[4], u32x2 out
     }
 }
 
+// Checked build (compiled with ATTN_CHECKED=1): the kernels validate the
+// device-side indices they are given, record what was out of range in a
+// per-device error word and go on with a safe value, so a bad block table or
+// length cannot make them read outside the page pool.  The release build
+// compiles these checks away.
+#ifndef ATTN_CHECKED
+#define ATTN_CHECKED 0
+#endif
+constexpr unsigned kDevErrKvLen = 1u;   // a length outside [0, its host bound]
+constexpr unsigned kDevErrPage = 2u;    // a page index outside [0, num_pages)
+
+// Flags a length outside [0, bound]; the caller clamps it as in the release
+// build.
+__device__ __forceinline__ void check_len(int len, int bound, unsigned* err) {
+    if constexpr (ATTN_CHECKED) {
+        if ((len < 0 || len > bound) && err) atomicOr(err, kDevErrKvLen);
+    }
+}
+// A page index, or page 0 (inside any non-empty pool) with the error flagged
+// when it lies outside [0, num_pages).
+__device__ __forceinline__ int checked_page(int p, int num_pages, unsigned* err) {
+    if constexpr (ATTN_CHECKED) {
+        if (p < 0 || p >= num_pages) {
+            if (err) atomicOr(err, kDevErrPage);
+            return 0;
+        }
+    }
+    return p;
+}
+
 }  // namespace attn

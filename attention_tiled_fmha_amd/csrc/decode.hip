@@ -144,7 +144,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     // lengths past the host bound are clamped, so no index leaves the planned
     // split range or the block-table row
-    const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
+    const int L_in = a.kv_lens ? a.kv_lens[b] : a.fixed_len;
+    if (c == 0) check_len(L_in, a.max_len, a.err);
+    const int L = min(L_in, a.max_len);
     const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
     const T* q = (const T*)a.q;
 
@@ -223,17 +225,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     PageRegs<T, D, G> ra, rb;
     int pg = pg0 + wave;
     if (pg < pg1) load_page<T, D, G>(ra, (const T*)a.k_pages, (const T*)a.v_pages,
-                                     (size_t)table[pg] * page_elems + head_off, lane);
+                                     (size_t)checked_page(table[pg], a.num_pages, a.err) * page_elems + head_off, lane);
     while (pg < pg1) {
         const int pn = pg + 4;
         if (pn < pg1) load_page<T, D, G>(rb, (const T*)a.k_pages, (const T*)a.v_pages,
-                                         (size_t)table[pn] * page_elems + head_off, lane);
+                                         (size_t)checked_page(table[pn], a.num_pages, a.err) * page_elems + head_off, lane);
         process(ra, pg);
         pg = pn;
         if (pg >= pg1) break;
         const int pn2 = pg + 4;
         if (pn2 < pg1) load_page<T, D, G>(ra, (const T*)a.k_pages, (const T*)a.v_pages,
-                                          (size_t)table[pn2] * page_elems + head_off, lane);
+                                          (size_t)checked_page(table[pn2], a.num_pages, a.err) * page_elems + head_off, lane);
         process(rb, pg);
         pg = pn2;
     }

@@ -146,7 +146,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     auto item = [&](const int ci, const int kvh, const int b) {
         // lengths past the host bound are clamped, so no index leaves the planned
         // split range or the block-table row
-        const int L = min(a.kv_lens ? a.kv_lens[b] : a.fixed_len, a.max_len);
+        const int L_in = a.kv_lens ? a.kv_lens[b] : a.fixed_len;
+        if (ci == 0) check_len(L_in, a.max_len, a.err);
+        const int L = min(L_in, a.max_len);
         const int nsplit = (L + a.split_tokens - 1) / a.split_tokens;
 
         if (L <= 0) {  // nothing to attend: O = 0, lse = -inf (a cascade's
@@ -195,8 +197,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
         // the item's block-table entries (at most 128 pages): entries pg0 + lane
         // and pg0 + 64 + lane, picked with v_readlane
-        const int tblv = lane < npg ? table[pg0 + lane] : 0;
-        const int tblv2 = lane + 64 < npg ? table[pg0 + 64 + lane] : 0;
+        const int tblv = lane < npg ? checked_page(table[pg0 + lane], a.num_pages, a.err) : 0;
+        const int tblv2 = lane + 64 < npg ? checked_page(table[pg0 + 64 + lane], a.num_pages, a.err) : 0;
         auto phys_of = [&](int j) { return __builtin_amdgcn_readlane(j < 64 ? tblv : tblv2, j & 63); };
 
         // byte offsets of this lane's K and V elements in a page tile

@@ -7,6 +7,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// 1 in the checked build (libattn_checked.so): device-data checks with an
+// error word, see common.h
+#ifndef ATTN_CHECKED
+#define ATTN_CHECKED 0
+#endif
+
 namespace attn {
 
 // Compute units of the current device, read once per device; 256 (MI355X)
@@ -30,7 +36,8 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
 hipError_t launch_prefill_paged_bf16(const void* q, const void* k_pages, const void* v_pages,
                                      const int32_t* block_table, const int32_t* kv_lens,
                                      void* o, float* lse, int B, int Hq, int Hkv, int Tq, int D,
-                                     int bt_stride, bool causal, float scale, hipStream_t stream);
+                                     int bt_stride, bool causal, float scale, hipStream_t stream,
+                                     unsigned* err = nullptr, int num_pages = 0);
 
 // Dense prefill, fp32 in/out, fp32 arithmetic (the exactness test mode).
 hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* o,
@@ -74,6 +81,10 @@ struct DecodeArgs {
     // to the output directly) and the combine merges prefix_slots + nsplit(b)
     // slots of every row
     int prefix_slots;
+    // checked build: the error word and the pool size the page indices are
+    // checked against (unused otherwise)
+    unsigned* err;
+    int num_pages;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
@@ -113,6 +124,9 @@ struct PrefixArgs {
     // > 0: every chunk's state goes to workspace slot c of ws_slots per row
     // (the first slots of a cascade's decode workspace), also for one chunk
     int ws_slots;
+    // checked build: error word and pool size (unused otherwise)
+    unsigned* err;
+    int num_pages;
 };
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t stream);
 

@@ -136,6 +136,8 @@ struct KVSrc {
     const uint16_t* v;
     const int32_t* table;   // paged: this sequence's block-table row
     int Hkv, kvh, Tk;
+    unsigned* err;          // checked build: error word and pool size
+    int num_pages;
 };
 
 // Thread tid's granules of a tile: g = tid + 256 j lands at byte 16 g of the
@@ -190,7 +192,8 @@ __device__ __forceinline__ void dma_tiles(unsigned char LDS_AS* kdst, unsigned c
                 const int valid = t < 0 ? 0 : max(0, min(16, src.Tk - p * 16));
                 base = pool;
                 if (__builtin_amdgcn_readfirstlane(valid) > 0) {
-                    const int phys = __builtin_amdgcn_readfirstlane(src.table[p]);
+                    const int phys = __builtin_amdgcn_readfirstlane(
+                        checked_page(src.table[p], src.num_pages, src.err));
                     base = pool + ((size_t)phys * src.Hkv + src.kvh) * 16 * D;
                 }
                 bytes = valid * C::ROW;
@@ -237,7 +240,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                          float* __restrict__ lse, int BH, int Hq, int Hkv, int Tq, int Tk_dense,
                          int n_qtiles, int paired, float scale_log2,
                          const int32_t* __restrict__ block_table,
-                         const int32_t* __restrict__ kv_lens, int bt_stride) {
+                         const int32_t* __restrict__ kv_lens, int bt_stride,
+                         unsigned* err, int num_pages) {
     using C = Cfg<D>;
     // two K and two V stages, each its own LDS object: the compiler then
     // tracks the direct-to-LDS loads into one stage separately from reads of
@@ -272,6 +276,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     // paged: the sequence's own key count (its chunk of Tq queries is its
     // last Tq positions, so the causal diagonal sits at kv_len - Tq), clamped
     // to what its block-table row can map so no page index leaves the row
+    if constexpr (PAGED) {
+        if (blockIdx.x < BH && threadIdx.x == 0) check_len(kv_lens[b], bt_stride * 16, err);
+    }
     const int Tk = PAGED ? __builtin_amdgcn_readfirstlane(max(0, min(kv_lens[b], bt_stride * 16)))
                          : Tk_dense;
     const int diag = Tk - Tq;
@@ -284,6 +291,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     src.Hkv = Hkv;
     src.kvh = kvh;
     src.Tk = Tk;
+    src.err = err;
+    src.num_pages = num_pages;
     const LoadPlan<D> lp(tid, PAGED);
 
     // Per-lane LDS offsets of the MFMA operands within a K or V tile.
@@ -672,7 +681,8 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
     auto go = [&](auto kern) {
         kern<<<grid, kThreads, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k,
                                             (const uint16_t*)v, (uint16_t*)o, lse, BH, Hq, Hkv,
-                                            Tq, Tk, n_qtiles, paired, sl2, nullptr, nullptr, 0);
+                                            Tq, Tk, n_qtiles, paired, sl2, nullptr, nullptr, 0,
+                                            nullptr, 0);
     };
     if (D == 64)
         causal ? go(prefill_bf16_kernel<64, true, false>) : go(prefill_bf16_kernel<64, false, false>);
@@ -684,7 +694,8 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
 hipError_t launch_prefill_paged_bf16(const void* q, const void* k_pages, const void* v_pages,
                                      const int32_t* block_table, const int32_t* kv_lens,
                                      void* o, float* lse, int B, int Hq, int Hkv, int Tq, int D,
-                                     int bt_stride, bool causal, float scale, hipStream_t stream) {
+                                     int bt_stride, bool causal, float scale, hipStream_t stream,
+                                     unsigned* err, int num_pages) {
     const int BH = B * Hq;
     const int n_qtiles = (Tq + kBM - 1) / kBM;
     dim3 grid;
@@ -695,7 +706,7 @@ hipError_t launch_prefill_paged_bf16(const void* q, const void* k_pages, const v
         kern<<<grid, kThreads, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k_pages,
                                             (const uint16_t*)v_pages, (uint16_t*)o, lse, BH, Hq,
                                             Hkv, Tq, 0, n_qtiles, paired, sl2, block_table, kv_lens,
-                                            bt_stride);
+                                            bt_stride, err, num_pages);
     };
     if (D == 64)
         causal ? go(prefill_bf16_kernel<64, true, true>) : go(prefill_bf16_kernel<64, false, true>);

@@ -161,7 +161,7 @@ void prefix_mfma_kernel(PrefixArgs a) {
                 qf[j][s] = __builtin_bit_cast(bf16x8, w);
             }
         }
-        const int tblv = lane < npg ? a.pages[pg0 + lane] : 0;
+        const int tblv = lane < npg ? checked_page(a.pages[pg0 + lane], a.num_pages, a.err) : 0;
 
         auto load = [&](PrefixPage<D, FP8>& pb, int j) {
             const int pg = pg0 + j;

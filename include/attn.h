@@ -491,6 +491,40 @@ int attn_flat_gemm(const void *a, const void *w, void *c, int m, int n, int k, i
                    const attn_flat_gemm_opts *opts);
 
 /*
+ * Checked build.  libattn_checked.so is built from the same sources with
+ * ATTN_CHECKED=1 and exports this same interface.  Its kernels also check the
+ * indices they read from device memory, which the release build takes on
+ * trust (a block table maps a sequence's logical pages to scattered physical
+ * ones: xhh.club summary, "how does paged attention manage the KV cache"):
+ *   - a length (kv_lens[b], or a paged prefill's kv_lens[b]) outside
+ *     [0, its host bound] sets ATTN_DEV_ERR_KV_LEN and is clamped as in the
+ *     release build;
+ *   - a page index (block-table or prefix-page entry) outside
+ *     [0, num_pages) sets ATTN_DEV_ERR_PAGE and page 0 is read instead, so
+ *     a bad table cannot make a kernel read outside the pool.  num_pages is
+ *     the number of whole pages from k_pages (and from v_pages) to the end
+ *     of the device allocation that holds it, attn_device_pool_pages below;
+ *     it is INT_MAX, and only negative indices are caught, when the runtime
+ *     knows no allocation at that pointer.
+ * The results of a call with valid data equal the release build's bit for
+ * bit.  The checks cost a little time; the release build has none of them.
+ *
+ * attn_checked_build: 1 in the checked library, 0 in the release one.
+ * attn_device_errors: waits for the current device (hipDeviceSynchronize),
+ *   stores its error word (an OR of ATTN_DEV_ERR_* bits since it was last
+ *   cleared) in *flags and clears it when `clear` is nonzero.  Not
+ *   capturable.  The word is shared by every call on that device.  Errors:
+ *   ATTN_E_UNSUPPORTED in the release library, ATTN_E_NULL, ATTN_E_HIP.
+ * attn_device_pool_pages: the page bound above, for `pages` and pages of
+ *   page_bytes bytes, in *num_pages (host-only query, both builds).
+ */
+#define ATTN_DEV_ERR_KV_LEN 1u
+#define ATTN_DEV_ERR_PAGE 2u
+int attn_checked_build(void);
+int attn_device_errors(unsigned int *flags, int clear);
+int attn_device_pool_pages(const void *pages, size_t page_bytes, int *num_pages);
+
+/*
  * attn_probe_hbm_read -- measurement aid, not part of the attention path: a
  * kernel that only reads, used to measure the HBM read rate that plain
  * 16-byte vector loads reach on this GPU, the practical ceiling of the

@@ -38,6 +38,34 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(attn.SIGNATURES), "binding and header disagree"
 
 
+def test_checked_library(lib):
+    """The checked twin exports the same interface, says which build it is,
+    and answers its host-side queries (nothing here touches a device)."""
+    chk = attn.load(attn.CHECKED_LIB_PATH)
+    try:
+        for name in declared_functions():
+            assert hasattr(chk, name), f"{name} not exported by the checked library"
+        assert chk.attn_checked_build() == 1
+        assert lib.attn_checked_build() == 0
+        flags = ctypes.c_uint(7)
+        assert lib.attn_device_errors(ctypes.byref(flags), 1) == E_UNSUP
+        assert chk.attn_device_errors(None, 1) == E_NULL
+        n = ctypes.c_int(0)
+        # no allocation known at NULL: only negative indices would be caught
+        assert chk.attn_device_pool_pages(None, 4096, ctypes.byref(n)) == OK
+        assert n.value == 2 ** 31 - 1
+        assert chk.attn_device_pool_pages(None, 4096, None) == E_NULL
+        # the host-side argument checks are the release build's
+        assert chk.attn_decode_shared_prefix(None, FAKE, FAKE, FAKE, 64, FAKE, None, 4, 4, 4, 128,
+                                             16, 0, 0, 0.1, None, 0, None) == E_NULL
+    finally:
+        attn.load(attn.LIB_PATH)
+    text = open(HEADER).read()
+    bits = dict(re.findall(r"#define (ATTN_DEV_ERR_\w+) (\d+)u", text))
+    assert bits == {"ATTN_DEV_ERR_KV_LEN": str(attn.DEV_ERR_KV_LEN),
+                    "ATTN_DEV_ERR_PAGE": str(attn.DEV_ERR_PAGE)}
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert attn.status_str(s) and attn.status_str(s) != "unknown status"

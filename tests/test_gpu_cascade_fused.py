@@ -185,3 +185,49 @@ def test_fused_cascade_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, want_o) and torch.equal(lse, want_l)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_fused_cascade_edges(fp8):
+    """No prefix (the call is the paged decode of the requests' own tokens);
+    no own tokens at all (max_suffix_len 0: the prefix alone); suffix_lens
+    NULL (every request has max_suffix_len tokens); 16 query heads per kv
+    head (the largest group)."""
+    require_gpu()
+    dt = "fp8" if fp8 else "bf16"
+    # no prefix
+    c = wl.cascade_inputs(6, 4, 128, dt, 811, prefix_len=0, suffix_range=(1, 900), Hkv=2)
+    kw = dict(k_scale=c["k_scale"], v_scale=c["v_scale"]) if fp8 else {}
+    o, lse = fused(c, "f32", **kw)
+    if fp8:
+        ro, rl = oracle.decode_paged_fp8(c["q"], c["k_pages"], c["v_pages"], c["k_scale"],
+                                         c["v_scale"], c["suffix_table"], c["suffix_lens"],
+                                         c["scale"])
+    else:
+        ro, rl = oracle.decode_paged(c["q"], c["k_pages"], c["v_pages"], c["suffix_table"],
+                                     c["suffix_lens"], c["scale"])
+    assert_close(o, ro, "bf16", "no prefix O")
+    assert_close(lse, rl, "bf16", "no prefix lse")
+    # no own tokens: max_suffix_len 0
+    c = wl.cascade_inputs(5, 4, 128, dt, 812, prefix_len=1000, suffix_range=(1, 2), Hkv=4)
+    kw = dict(k_scale=c["k_scale"], v_scale=c["v_scale"]) if fp8 else {}
+    zeros = np.zeros(5, np.int32)
+    o, lse = fused(c, "f32", lens=zeros, **kw)
+    ro, rl = oracle_cascade(c, zeros, fp8)
+    assert_close(o, ro, "bf16", "prefix alone O")
+    assert_close(lse, rl, "bf16", "prefix alone lse")
+    # suffix_lens NULL, G = 16
+    L = 300
+    c = wl.cascade_inputs(3, 16, 64, dt, 813, prefix_len=700, suffix_lens=np.full(3, L, np.int32),
+                          Hkv=1)
+    q = dev(c["q"])
+    o = torch.full(q.shape, float("nan"), device="cuda")
+    lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+    kw = dict(k_scale=c["k_scale"], v_scale=c["v_scale"]) if fp8 else {}
+    attn.attn_decode_cascade(q, dev(c["k_pages"]), dev(c["v_pages"]), dev(c["prefix_pages"]),
+                             c["prefix_len"], dev(c["suffix_table"]), None, o, lse,
+                             max_suffix_len=L, scale=c["scale"], **kw)
+    torch.cuda.synchronize()
+    ro, rl = oracle_cascade(c, c["suffix_lens"], fp8)
+    assert_close(host(o), ro, "bf16", "suffix_lens NULL, G = 16 O")
+    assert_close(host(lse), rl, "bf16", "suffix_lens NULL, G = 16 lse")

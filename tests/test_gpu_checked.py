@@ -1,0 +1,193 @@
+"""The checked library (libattn_checked.so: the release kernels plus
+device-side index checks and an error word) on the GPU.
+
+Valid data: every result equals the release library's bit for bit and the
+error word stays 0.  Out-of-range data (a length past its host bound or
+below 0, a page index outside the pool): the kernels set the matching bits
+and go on with the clamped length and page 0, so each result equals the
+release library's on the inputs with those values replaced.  Bad page
+indices are planted only far past the pool bound the checked library reports
+for the tensors (and -1), so each one is caught; the release library only
+ever sees the replaced, valid inputs."""
+import numpy as np
+import pytest
+import torch
+
+from attention_tiled_fmha_amd import attn
+from attention_tiled_fmha_amd import workloads as wl
+from gpu_util import dev, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+BAD_PAGE = 1 << 30
+
+
+def on(path, fn):
+    """fn() with the binding's calls going to the library at path."""
+    attn.load(path)
+    try:
+        out = fn()
+        torch.cuda.synchronize()
+        return tuple(host(t) for t in out)
+    finally:
+        attn.load(attn.LIB_PATH)
+
+
+def checked(fn):
+    attn.load(attn.CHECKED_LIB_PATH)
+    try:
+        attn.device_errors(clear=True)
+        out = on(attn.CHECKED_LIB_PATH, fn)
+        attn.load(attn.CHECKED_LIB_PATH)
+        flags = attn.device_errors(clear=True)
+    finally:
+        attn.load(attn.LIB_PATH)
+    return out, flags
+
+
+def same(a, b):
+    return all(np.array_equal(x, y, equal_nan=True) for x, y in zip(a, b))
+
+
+def decode_fn(d, fp8=False, table=None, lens=None):
+    q = dev(d["q"])
+    kp, vp = dev(d["k_pages"]), dev(d["v_pages"])
+    bt = dev(d["block_table"] if table is None else table)
+    kl = dev(d["kv_lens"] if lens is None else lens)
+    out_dtype = torch.float32
+
+    def go():
+        o = torch.full(q.shape, float("nan"), dtype=out_dtype, device="cuda")
+        lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+        if fp8:
+            attn.attn_decode_paged_fp8(q, kp, vp, d["k_scale"], d["v_scale"], bt, kl, o, lse,
+                                       max_kv_len=d["max_kv_len"], scale=d["scale"])
+        else:
+            attn.attn_decode_paged(q, kp, vp, bt, kl, o, lse, max_kv_len=d["max_kv_len"],
+                                   scale=d["scale"])
+        return o, lse
+    return go, kp, vp
+
+
+def prefix_fn(c, pages=None):
+    q = dev(c["q"])
+    kp, vp = dev(c["k_pages"]), dev(c["v_pages"])
+    pp = dev(c["prefix_pages"] if pages is None else pages)
+
+    def go():
+        o = torch.full(q.shape, float("nan"), device="cuda")
+        lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+        attn.attn_decode_shared_prefix(q, kp, vp, pp, c["prefix_len"], o, lse, scale=c["scale"])
+        return o, lse
+    return go, kp, vp
+
+
+def prefill_fn(d, table=None, lens=None):
+    q = dev(d["q"])
+    kp, vp = dev(d["k_pages"]), dev(d["v_pages"])
+    bt = dev(d["block_table"] if table is None else table)
+    kl = dev(d["kv_lens"] if lens is None else lens)
+
+    def go():
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), device="cuda")
+        attn.attn_prefill_paged(q, kp, vp, bt, kl, o, lse, causal=True, scale=d["scale"])
+        return o, lse
+    return go, kp, vp
+
+
+def workloads():
+    lens = [700, 3000, 1500, 40, 2049]
+    return dict(
+        decode_bf16=(decode_fn, wl.paged_decode_inputs(5, 8, 2, 128, "bf16", 901, lengths=lens), {}),
+        decode_fp8=(decode_fn, wl.paged_decode_fp8_inputs(5, 8, 2, 128, 902, lengths=lens),
+                    dict(fp8=True)),
+        decode_f32=(decode_fn, wl.paged_decode_inputs(5, 4, 4, 64, "f32", 903, lengths=lens), {}),
+    )
+
+
+def test_checked_equals_release_on_valid_data():
+    require_gpu()
+    cases = {k: (f(d, **kw)[0]) for k, (f, d, kw) in workloads().items()}
+    c = wl.cascade_inputs(20, 8, 128, "bf16", 904, prefix_len=1500, suffix_range=(1, 2), Hkv=2)
+    cases["shared_prefix"] = prefix_fn(c)[0]
+    p = wl.paged_prefill_inputs(2, 8, 2, 300, 128, "bf16", 905, lengths=[300, 1000])
+    cases["prefill_paged"] = prefill_fn(p)[0]
+    for name, go in cases.items():
+        want = on(attn.LIB_PATH, go)
+        got, flags = checked(go)
+        assert flags == 0, f"{name}: error word {flags} on valid data"
+        assert same(got, want), f"{name}: checked and release results differ"
+
+
+def planted(table):
+    """Two planted entries (far past any pool bound, and -1) and the table
+    with them replaced by page 0."""
+    bad = table.copy()
+    bad[2, 0] = BAD_PAGE
+    bad[4, 1] = -1
+    fixed = bad.copy()
+    fixed[(fixed < 0) | (fixed >= BAD_PAGE)] = 0
+    return bad, fixed
+
+
+def guarded(built, P):
+    """The go() of built = (go, k_pages, v_pages), after checking that the
+    checked library bounds page indices into those very tensors below
+    BAD_PAGE (so every planted index is caught before any read)."""
+    go, kp, vp = built
+    attn.load(attn.CHECKED_LIB_PATH)
+    try:
+        bounds = [attn.device_pool_pages(kp), attn.device_pool_pages(vp)]
+    finally:
+        attn.load(attn.LIB_PATH)
+    assert all(P <= b < BAD_PAGE for b in bounds), f"pool bounds {bounds} for {P} pages"
+    return go
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "decode_fp8", "decode_f32"])
+def test_checked_flags_bad_lengths_and_pages(name):
+    require_gpu()
+    f, d, kw = workloads()[name]
+    P = d["k_pages"].shape[0]
+    bad_t, fixed_t = planted(d["block_table"])
+    lens = d["kv_lens"].copy()
+    lens[1] = d["max_kv_len"] + 100      # past the host bound (row 1 is the longest)
+    lens[3] = -5
+    fixed_l = np.minimum(lens, d["max_kv_len"])
+    fixed_l[3] = 0
+    got, flags = checked(guarded(f(d, table=bad_t, lens=lens, **kw), P))
+    assert flags == attn.DEV_ERR_KV_LEN | attn.DEV_ERR_PAGE
+    want = on(attn.LIB_PATH, f(d, table=fixed_t, lens=fixed_l, **kw)[0])
+    assert same(got, want)
+    assert np.isneginf(got[1][3]).all() and (got[0][3] == 0).all()
+    # each kind alone sets only its bit
+    _, flags = checked(f(d, lens=lens, **kw)[0])
+    assert flags == attn.DEV_ERR_KV_LEN
+    _, flags = checked(guarded(f(d, table=bad_t, **kw), P))
+    assert flags == attn.DEV_ERR_PAGE
+
+
+def test_checked_flags_bad_prefix_page_and_prefill_table():
+    require_gpu()
+    c = wl.cascade_inputs(20, 8, 128, "bf16", 906, prefix_len=1500, suffix_range=(1, 2), Hkv=2)
+    P = c["k_pages"].shape[0]
+    pages = c["prefix_pages"].copy()
+    pages[3], pages[50] = BAD_PAGE, -1
+    fixed = pages.copy()
+    fixed[3] = fixed[50] = 0
+    got, flags = checked(guarded(prefix_fn(c, pages=pages), P))
+    assert flags == attn.DEV_ERR_PAGE
+    assert same(got, on(attn.LIB_PATH, prefix_fn(c, pages=fixed)[0]))
+
+    p = wl.paged_prefill_inputs(5, 8, 2, 64, 128, "bf16", 907,
+                                lengths=[300, 1000, 200, 500, 640])
+    P = p["k_pages"].shape[0]
+    bad_t, fixed_t = planted(p["block_table"])
+    lens = p["kv_lens"].copy()
+    lens[1] = p["block_table"].shape[1] * 16 + 40     # past what the row maps
+    fixed_l = lens.copy()
+    fixed_l[1] = p["block_table"].shape[1] * 16
+    got, flags = checked(guarded(prefill_fn(p, table=bad_t, lens=lens), P))
+    assert flags == attn.DEV_ERR_KV_LEN | attn.DEV_ERR_PAGE
+    assert same(got, on(attn.LIB_PATH, prefill_fn(p, table=fixed_t, lens=fixed_l)[0]))

@@ -84,6 +84,50 @@ def test_graph_replay_split_decode():
     assert_close(host(lse), rl, "bf16", "replayed lse")
 
 
+def test_graph_replay_decode_gqa_full_size():
+    """The GQA decode workload (B128 Hq32 Hkv8, L ~ logU[1024, 32768], 512-
+    token chunks; more item slots than the persistent grid, so every
+    workgroup walks several) captured once and replayed with new queries and
+    lengths each time: every replay equals the eager launch."""
+    require_gpu()
+    d = wl.workload(wl.DECODE_GQA)
+    gen = wl.generator(4103)
+    B, Hq, D = d["B"], d["Hq"], d["D"]
+    maxlen = int(d["kv_lens"].max())
+    split = 512
+    q = dev(d["q"])
+    kp, vp, bt = dev(d["k_pages"]), dev(d["v_pages"]), dev(d["block_table"])
+    kl = dev(d["kv_lens"])
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), device="cuda")
+    ws = torch.empty(attn.attn_decode_workspace_bytes(B, Hq, d["Hkv"], D, maxlen, split),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(o=o, lse=lse):
+        attn.attn_decode_paged(q, kp, vp, bt, kl, o, lse, max_kv_len=maxlen, scale=d["scale"],
+                               workspace=ws, split_tokens=split)
+
+    g = capture(step)
+    o_ref, lse_ref = torch.empty_like(o), torch.empty_like(lse)
+    for rep in range(3):
+        q_new = wl.normal(gen, (B, Hq, D), "bf16")
+        lens = (d["kv_lens"] * gen.uniform(0.3, 1.0, size=B)).astype(np.int32)
+        q.copy_(dev(q_new))
+        kl.copy_(dev(lens))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        step(o_ref, lse_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {rep}: O differs from the eager launch"
+        assert torch.equal(lse, lse_ref), f"replay {rep}: lse differs from the eager launch"
+    rows = [0, 57, 127]
+    ro, rl = oracle.decode_paged(q_new[rows], d["k_pages"], d["v_pages"], d["block_table"][rows],
+                                 lens[rows], d["scale"])
+    assert_close(host(o)[rows], ro, "bf16", "replayed O")
+    assert_close(host(lse)[rows], rl, "bf16", "replayed lse")
+
+
 def test_graph_replay_cascade():
     """Prefix stage, suffix decode and merge captured as one graph, replayed
     with new queries and new suffix lengths."""

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ float s_m[2][4][kMaxG];
     __shared__ float s_l[2][4][kMaxG];
     __shared__ float s_x[4][kMaxG];     // unified max: largest raw score per row
-    __shared__ float s_o[2][4][kMaxG][D];
+    __shared__ __attribute__((aligned(16))) float s_o[2][4][kMaxG][D];
     const float phi_l2 = a.phi * kLog2e;
     const int cpi = chunks_per_item(a, FP8);
     // in a cascade the first prefix_slots workspace slots of every row hold the
@@ -403,17 +403,34 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                     s_l[set][wave][col] = l_run;
                     s_x[wave][col] = smax;
                 }
+                // Block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2 (bf16),
+                // 64(i/4) + 4(4grp + r) + i%4 (FP8; D = 128: 8(4grp + r) +
+                // 4(i/4) + i%4), written 2 (bf16) or 4 (FP8) dims at a time.
+                // Only the G real query rows (col < G) are read back; the 16
+                // rows of a lane group lie D floats apart, in one LDS bank, so
+                // writing the padding rows would only add bank conflicts.
+                if (col < G) {
+                    float* row = &s_o[set][wave][col][0];
+                    if constexpr (FP8) {
     #pragma unroll
-                for (int i = 0; i < NB; i++)
+                        for (int w = 0; w < NB / 4; w++)
     #pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        // block i row 4grp + r -> dim 32(i/2) + 2(4grp + r) + i%2 (bf16),
-                        // 64(i/4) + 4(4grp + r) + i%4 (FP8)
-                        const int dim = FP8 ? (D == 128 ? 8 * (4 * grp + r) + 4 * (i >> 2) + (i & 3)
-                                                        : 64 * (i >> 2) + 4 * (4 * grp + r) + (i & 3))
-                                            : 32 * (i >> 1) + 2 * (4 * grp + r) + (i & 1);
-                        s_o[set][wave][col][dim] = oacc[i][r];
+                            for (int r = 0; r < 4; r++) {
+                                const int d0 = D == 128 ? 8 * (4 * grp + r) + 4 * w : 64 * w + 4 * (4 * grp + r);
+                                *(f32x4*)(row + d0) = f32x4{oacc[4 * w][r], oacc[4 * w + 1][r],
+                                                            oacc[4 * w + 2][r], oacc[4 * w + 3][r]};
+                            }
+                    } else {
+    #pragma unroll
+                        for (int pp = 0; pp < NB / 2; pp++)
+    #pragma unroll
+                            for (int r = 0; r < 4; r++) {
+                                typedef float f32x2 __attribute__((ext_vector_type(2)));
+                                *(f32x2*)(row + 32 * pp + 2 * (4 * grp + r)) =
+                                    f32x2{oacc[2 * pp][r], oacc[2 * pp + 1][r]};
+                            }
                     }
+                }
                 __syncthreads();
             };
             const int nunits = (npg + PU - 1) / PU;

@@ -248,30 +248,38 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         // chunk cc's result (straight to the output when the sequence is one
         // chunk); the caller synchronises before the set is published again
         auto finish = [&](int cc, int set) {
-            for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-                const int g = idx / D, d = idx % D;
+            // a thread per 4 consecutive dims of a row: the four wavefronts'
+            // weights once, then 16-byte LDS reads and global writes
+            for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
+                const int g = idx / (D / 4), d0 = 4 * (idx % (D / 4));
                 float M = -INFINITY;
                 for (int w = 0; w < 4; w++) M = fmaxf(M, s_m[set][w][g]);
-                float lt = 0.f, ot = 0.f;
+                float lt = 0.f;
+                f32x4 ot = {0.f, 0.f, 0.f, 0.f};
                 if (M != -INFINITY) {
                     for (int w = 0; w < 4; w++) {
                         const float sm = s_m[set][w][g];
                         const float wt = (sm == -INFINITY) ? 0.f : fast_exp2(sm - M);
                         lt = fmaf(wt, s_l[set][w][g], lt);
-                        ot = fmaf(wt, s_o[set][w][g][d], ot);
+                        const f32x4 ow = *(const f32x4*)&s_o[set][w][g][d0];
+#pragma unroll
+                        for (int e = 0; e < 4; e++) ot[e] = fmaf(wt, ow[e], ot[e]);
                     }
                 }
                 const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
-                const float ov = ot * inv;
+                f32x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; e++) ov[e] = ot[e] * inv;
                 const float lse = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
                 const size_t row = (size_t)b * a.Hq + kvh * G + g;
                 if (nsplit == 1 && !cascade) {
-                    if (a.out_f32) ((float*)a.o)[row * D + d] = ov;
-                    else ((uint16_t*)a.o)[row * D + d] = f32_to_bf16(ov);
-                    if (a.lse && d == 0) a.lse[row] = lse;
+                    if (a.out_f32) *(f32x4*)((float*)a.o + row * D + d0) = ov;
+                    else *(u32x2*)((uint16_t*)a.o + row * D + d0) =
+                             u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+                    if (a.lse && d0 == 0) a.lse[row] = lse;
                 } else {
-                    a.ws_o[(row * a.max_splits + slot0 + cc) * D + d] = ov;
-                    if (d == 0) a.ws_lse[row * a.max_splits + slot0 + cc] = lse;
+                    *(f32x4*)(a.ws_o + (row * a.max_splits + slot0 + cc) * D + d0) = ov;
+                    if (d0 == 0) a.ws_lse[row * a.max_splits + slot0 + cc] = lse;
                 }
             }
         };

@@ -232,6 +232,39 @@ def bench_prefill_noncausal(steps, warmup):
                 frac_mfma=round(flops / (mean_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
 
 
+def bench_torch_sdpa(steps, warmup):
+    """Context, not the product: PyTorch's own fused attention
+    (scaled_dot_product_attention restricted to its flash, then its
+    memory-efficient backend, never the unfused math path) on the prefill
+    shape, causal and not, timed like the prefill lines."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    sets = []
+    for s in range(3):
+        inp = wl.workload(wl.PREFILL_CAUSAL, seed=1002 + 100 * s)
+        sets.append(tuple(dev(inp[x]) for x in ("q", "k", "v")))
+    B, H, T, D = 4, 32, 1024, 128
+    out = dict(library="torch.nn.functional.scaled_dot_product_attention", torch=torch.__version__)
+    for name, backend in (("flash", SDPBackend.FLASH_ATTENTION),
+                          ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([backend]):
+                for causal in (True, False):
+                    def step(i):
+                        q, k, v = sets[i % 3]
+                        torch.nn.functional.scaled_dot_product_attention(
+                            q, k, v, is_causal=causal, scale=1.0 / math.sqrt(D))
+
+                    _, span, _ = time_launches(step, steps, warmup)
+                    flops = 4.0 * D * (T * (T + 1) / 2 if causal else T * T) * B * H
+                    out["causal_tflops" if causal else "noncausal_tflops"] = round(
+                        flops / (span / steps * 1e-3) / 1e12, 2)
+            out["backend"] = name
+            return out
+        except RuntimeError as e:
+            out[f"{name}_unavailable"] = str(e)[:160]
+    return out
+
+
 def bench_prefill_f32(steps, warmup):
     """The fp32 test mode, non-causal B1 H1 T128 D64 (4.19 MFLOP;
     launch-latency bound, reported in microseconds and against the fp32
@@ -625,7 +658,8 @@ def cpu_baseline(target_s=10.0):
                 seconds=round(t_used, 2))
 
 
-SECTIONS = ("prefill", "prefill_noncausal", "prefill_f32", "prefill_paged", "decode_mha",
+SECTIONS = ("prefill", "prefill_noncausal", "torch_sdpa", "prefill_f32", "prefill_paged",
+            "decode_mha",
             "decode_gqa", "decode_mha_fp8", "decode_gqa_fp8", "cascade", "cascade_fp8", "graph",
             "flat_gemm", "hbm_read")
 
@@ -668,6 +702,7 @@ def main():
         run = {
             "prefill": lambda: bench_prefill(K, W),
             "prefill_noncausal": lambda: bench_prefill_noncausal(K, W),
+            "torch_sdpa": lambda: bench_torch_sdpa(K, W),
             "prefill_f32": lambda: bench_prefill_f32(K, W),
             "prefill_paged": lambda: bench_prefill_paged(K, W),
             "decode_mha": lambda: bench_decode(wl.DECODE_MHA, K, W),
@@ -693,6 +728,15 @@ def main():
     flat = None
     noncausal = bench_prefill_noncausal(K, W)
     log(f"  non-causal: {noncausal['tflops']:.1f} TFLOP/s")
+    log("torch's fused attention on the same shape (context) ...")
+    try:
+        library = bench_torch_sdpa(K, W)
+    except Exception as e:   # context only: never let it stop the bench
+        library = dict(unavailable=f"{type(e).__name__}: {str(e)[:160]}")
+    if "causal_tflops" in library:
+        library["this_library_causal_ratio"] = round(pre["tflops"] / library["causal_tflops"], 3)
+        log(f"  {library.get('backend')}: causal {library['causal_tflops']:.1f}, non-causal "
+            f"{library.get('noncausal_tflops', float('nan')):.1f} TFLOP/s")
     f32_mode = bench_prefill_f32(K, W)
     log(f"  fp32 test mode (B1 H1 T128 D64): {f32_mode['us']:.1f} us per launch")
     ceiling = None
@@ -772,6 +816,7 @@ def main():
                        for kk, vv in v.items()} for k, v in decode.items()},
         "prefill_paged": paged_prefill,
         "prefill_noncausal": noncausal,
+        "prefill_library_reference": library,
         "prefill_f32_test_mode": f32_mode,
         "flat_gemm": flat,
         "hbm_read_ceiling": ceiling,

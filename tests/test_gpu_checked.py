@@ -96,6 +96,35 @@ def prefill_fn(d, table=None, lens=None):
     return go, kp, vp
 
 
+def cascade_fn(c):
+    q = dev(c["q"])
+    kp, vp = dev(c["k_pages"]), dev(c["v_pages"])
+    pp, st, sl = dev(c["prefix_pages"]), dev(c["suffix_table"]), dev(c["suffix_lens"])
+
+    def go():
+        o = torch.full(q.shape, float("nan"), device="cuda")
+        lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+        attn.attn_decode_cascade(q, kp, vp, pp, c["prefix_len"], st, sl, o, lse,
+                                 max_suffix_len=int(c["suffix_lens"].max()), scale=c["scale"],
+                                 k_scale=c["k_scale"], v_scale=c["v_scale"])
+        return o, lse
+    return go
+
+
+def noalloc_fn(d):
+    q = dev(d["q"])
+    kp, vp = dev(d["k_pages"]), dev(d["v_pages"])
+    bt, kl = dev(d["block_table"]), dev(d["kv_lens"])
+
+    def go():
+        o = torch.full(q.shape, float("nan"), device="cuda")
+        lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+        attn.attn_decode_paged_noalloc(q, kp, vp, bt, kl, o, lse, max_kv_len=d["max_kv_len"],
+                                       scale=d["scale"])
+        return o, lse
+    return go
+
+
 def workloads():
     lens = [700, 3000, 1500, 40, 2049]
     return dict(
@@ -113,6 +142,10 @@ def test_checked_equals_release_on_valid_data():
     cases["shared_prefix"] = prefix_fn(c)[0]
     p = wl.paged_prefill_inputs(2, 8, 2, 300, 128, "bf16", 905, lengths=[300, 1000])
     cases["prefill_paged"] = prefill_fn(p)[0]
+    cc = wl.cascade_inputs(24, 8, 128, "fp8", 908, prefix_len=1000, suffix_range=(1, 700), Hkv=2)
+    cases["cascade_fp8"] = cascade_fn(cc)
+    d = workloads()["decode_bf16"][1]
+    cases["decode_noalloc"] = noalloc_fn(d)
     for name, go in cases.items():
         want = on(attn.LIB_PATH, go)
         got, flags = checked(go)

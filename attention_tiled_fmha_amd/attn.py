@@ -306,7 +306,7 @@ def attn_decode_paged_noalloc(q, k_pages, v_pages, block_table, kv_lens, o, lse=
 
 def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, kv_lens, o,
                           lse=None, max_kv_len=None, scale=None, workspace=None, split_tokens=0,
-                          stream=None):
+                          stream=None, unified_max=False, phi=0.0, fallback_count=None):
     """attn_decode_paged over an FP8 cache: q bf16 [B,Hq,D]; k_pages, v_pages
     uint8 [P,Hkv,16,D] holding OCP E4M3 bytes, the cached values being
     k_scale * e4m3 and v_scale * e4m3; o bf16 or fp32 [B,Hq,D]."""
@@ -334,7 +334,12 @@ def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, kv
     if workspace is None and need:
         workspace = _workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    opts = DecodeOpts(split_tokens=int(split_tokens))
+    if fallback_count is not None:
+        _dense(fallback_count, "fallback_count")
+        if fallback_count.dtype != torch.int32 or fallback_count.numel() != 1:
+            raise TypeError("fallback_count must be one int32 element")
+    opts = DecodeOpts(split_tokens=int(split_tokens), use_unified_max=int(bool(unified_max)),
+                      phi=float(phi), fallback_count=_p(fallback_count))
     _check(load().attn_decode_paged_fp8(
         _p(q), _p(k_pages), _p(v_pages), float(k_scale), float(v_scale), _p(block_table),
         _p(kv_lens), _p(o), _p(lse), B, Hq, Hkv, D, page, block_table.shape[1], int(max_kv_len),

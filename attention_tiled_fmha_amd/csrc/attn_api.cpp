@@ -519,11 +519,14 @@ int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_page
     if (batch > 0 && !kv_lens) return ATTN_E_NULL;
     const int requested = opts ? opts->split_tokens : 0;
     if (requested < 0) return ATTN_E_ARG;
-    if (opts && opts->use_unified_max) return ATTN_E_UNSUPPORTED;
+    const bool unified = opts && opts->use_unified_max;
+    const float phi = opts ? opts->phi : 0.f;
+    if (unified && !std::isfinite(phi)) return ATTN_E_ARG;
     return decode_common(q, k_pages, v_pages, block_table, max_pages_per_seq, kv_lens, 0, o,
                          lse, batch, heads_q, heads_kv, head_dim, page_size, max_pages_per_seq,
                          max_kv_len, ATTN_FP8_E4M3, o_dtype, scale, workspace, workspace_bytes,
-                         stream, requested, false, 0.f, nullptr, k_scale, v_scale);
+                         stream, requested, unified, phi, opts ? opts->fallback_count : nullptr,
+                         k_scale, v_scale);
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -507,7 +507,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             for (int g = 0; g < G; g++) {
                 float M = -INFINITY;
                 for (int w = 0; w < 4; w++) M = fmaxf(M, s_x[w][g]);
-                const float z = M * a.scale - a.phi;
+                // the raw scores are q.k of the cached values over k_scale
+                // (1 for bf16): the scaled score is raw * scale * k_scale
+                const float z = M * a.scale * a.k_scale - a.phi;
                 if (z > kUnifiedWindow || z < -kUnifiedWindow) n_out++;
             }
             if (n_out > 0) {
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
 bool decode_mfma_supported(const DecodeArgs& a) {
     return !a.in_f32 && (a.D == 64 || a.D == 128) && a.Hq / a.Hkv <= kMaxG &&
-           a.split_tokens <= 64 * kPage && !(a.in_fp8 && a.unified);
+           a.split_tokens <= 64 * kPage;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {

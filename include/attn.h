@@ -211,8 +211,10 @@ int attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
  *                     could overflow an fp32 sum or the largest term
  *                     underflow) falls back: its chunk is recomputed with the
  *                     exact online softmax.  Results equal the plain path's
- *                     within the same tolerance.  bf16 caches with
- *                     heads_q / heads_kv <= 16 only (else ATTN_E_UNSUPPORTED).
+ *                     within the same tolerance.  bf16 caches (and FP8
+ *                     caches through attn_decode_paged_fp8, where s is
+ *                     scale * q.(k_scale * e4m3)) with heads_q / heads_kv
+ *                     <= 16 only (else ATTN_E_UNSUPPORTED).
  *   phi             : the unified max, in units of scaled scores (finite,
  *                     else ATTN_E_ARG); 0 suits scores of order one.
  *   fallback_count  : device int, or NULL.  The number of (query row, chunk)
@@ -283,9 +285,8 @@ int attn_decode_paged_noalloc(const void *q, const void *k_pages, const void *v_
  *   v_pages     : uint8 [num_pages, heads_kv, page_size, head_dim], E4M3
  *   k_scale,
  *   v_scale     : the per-tensor scales (finite and > 0, else ATTN_E_ARG)
- *   opts        : as for attn_decode_paged_ex (may be NULL); only
- *                 split_tokens is used; use_unified_max gives
- *                 ATTN_E_UNSUPPORTED
+ *   opts        : as for attn_decode_paged_ex (may be NULL): split_tokens,
+ *                 use_unified_max, phi and fallback_count
  *   everything else, the workspace size (attn_decode_workspace_bytes), the
  *   preconditions and the errors: as attn_decode_paged.  heads_q / heads_kv
  *   <= 16; chunks of at most 1024 tokens.

@@ -155,8 +155,8 @@ def test_decode_fp8_checks(lib):
     assert decode_fp8(lib, vs=float("nan")) == E_ARG
     assert decode_fp8(lib, ks=-1.0) == E_ARG
     assert decode_fp8(lib, scale=float("inf")) == E_ARG
-    uni = attn.DecodeOpts(use_unified_max=1)
-    assert decode_fp8(lib, opts=ctypes.byref(uni)) == E_UNSUP
+    uni = attn.DecodeOpts(use_unified_max=1, phi=float("nan"))
+    assert decode_fp8(lib, opts=ctypes.byref(uni)) == E_ARG   # the unified max must be finite
     neg = attn.DecodeOpts(split_tokens=-1)
     assert decode_fp8(lib, opts=ctypes.byref(neg)) == E_ARG
     need = lib.attn_decode_workspace_bytes(2, 8, 2, 128, 100000, 0)

@@ -218,3 +218,75 @@ def test_fp8_cascade_r64_prefix4096_full_size():
                                      c["v_scale"], table.astype(np.int32), lens, c["scale"])
     assert_close(o[rows], ro, "bf16", "cascade O")
     assert_close(lse[rows], rl, "bf16", "cascade lse")
+
+
+# --- unified max (asynchronous softmax) over an FP8 cache ----------------------
+
+def run_fp8_unified(d, phi, split_tokens):
+    q = dev(d["q"])
+    o = empty_like_out(q.shape, "bf16")
+    lse = torch.full(q.shape[:2], float("nan"), device="cuda")
+    count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    attn.attn_decode_paged_fp8(q, dev(d["k_pages"]), dev(d["v_pages"]), d["k_scale"],
+                               d["v_scale"], dev(d["block_table"]), dev(d["kv_lens"]), o, lse,
+                               max_kv_len=int(d["kv_lens"].max(initial=0)), scale=d["scale"],
+                               split_tokens=split_tokens, unified_max=True, phi=phi,
+                               fallback_count=count)
+    torch.cuda.synchronize()
+    return host(o), host(lse), int(count.item())
+
+
+def fp8_model_count(d, split, phi):
+    """The oracle's fp64 fallback model on the dequantised cache (each E4M3
+    byte decoded by the oracle, times k_scale); the case must not sit within
+    0.01 of the window edge."""
+    table = np.array([oracle.e4m3_value(b) for b in range(256)], np.float64)
+    k = (table[d["k_pages"]] * d["k_scale"]).astype(np.float32)
+    q = wl.bf16_to_f32(d["q"]).astype(np.float32)
+    args = (q, k, d["block_table"], d["kv_lens"], d["scale"], split, phi)
+    n = oracle.unified_fallback_count(*args)
+    assert n == oracle.unified_fallback_count(*args, window=59.99) == \
+        oracle.unified_fallback_count(*args, window=60.01), "case too close to the window edge"
+    return n
+
+
+UNI_LENS = [0, 1, 16, 17, 300, 512, 513, 1000, 2049]
+
+
+@pytest.mark.parametrize("phi", [0.0, 100.0, -100.0])
+@pytest.mark.parametrize("heads", [(8, 8), (32, 8)])
+def test_fp8_unified_max(phi, heads):
+    """The unified-max softmax over an FP8 cache: the window test uses the
+    scaled score scale * q.(k_scale * e4m3).  With phi = 0 no (row, chunk)
+    pair of N(0,1)-sized scores falls back, with phi = +-100 every pair does;
+    either way the result is the plain attention and the GPU's fallback
+    count is the fp64 model's."""
+    require_gpu()
+    Hq, Hkv = heads
+    split = 256
+    d = wl.paged_decode_fp8_inputs(len(UNI_LENS), Hq, Hkv, 128, 60 + Hq, lengths=UNI_LENS)
+    o, lse, n = run_fp8_unified(d, phi, split)
+    ro, rl = oracle_fp8(d)
+    assert_close(o, ro, "bf16", "O")
+    assert_close(lse, rl, "bf16", "lse")
+    pairs = Hq * sum((L + split - 1) // split for L in UNI_LENS)
+    assert n == fp8_model_count(d, split, phi) == (0 if phi == 0.0 else pairs)
+
+
+def test_fp8_unified_max_mixed_fallback():
+    """Queries of half the sequences scaled by 50 (scores up to a few hundred
+    against a window of +-60 around phi = 0): those pairs are recomputed, the
+    count matches the model and the result the oracle."""
+    require_gpu()
+    split = 128
+    lens = [33, 200, 700, 1500, 64, 129, 900, 2000]
+    d = wl.paged_decode_fp8_inputs(len(lens), 16, 4, 128, 67, lengths=lens)
+    q = wl.bf16_to_f32(d["q"])
+    q[::2] *= 50.0
+    d["q"] = wl.bf16_bits(q)
+    o, lse, n = run_fp8_unified(d, 0.0, split)
+    ro, rl = oracle_fp8(d)
+    assert_close(o, ro, "bf16", "O")
+    assert_close(lse, rl, "bf16", "lse")
+    assert n == fp8_model_count(d, split, 0.0)
+    assert 0 < n < 16 * sum((L + split - 1) // split for L in lens)

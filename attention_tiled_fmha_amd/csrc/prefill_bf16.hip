@@ -12,11 +12,12 @@
 //
 // gfx950 mapping
 // --------------
-// A workgroup is 4 wavefronts, one per SIMD, and owns 256 query rows of one
-// (batch, head).  Each wavefront holds two 32-row blocks of queries (blocks w
-// and 7 - w of the 8 in the tile, which gives every wavefront the same share
-// of the causal diagonal).  Per key tile of 32 keys a wavefront computes, for
-// both blocks,
+// A workgroup is 4 wavefronts, one per SIMD, and owns 128 query rows of one
+// (batch, head); each wavefront holds one 32-row block of them.  Two
+// workgroups share a CU (at most 256 registers per wavefront), so every
+// SIMD runs two wavefronts of two independent workgroups: while one waits at
+// its workgroup's barrier or for its loads, or runs its softmax on the VALU,
+// the other issues MFMAs.  Per key tile of 32 keys a wavefront computes
 //
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q held in
 //                   VGPRs.  S^T puts one query row per lane and 16 of the 32
@@ -28,13 +29,14 @@
 //   O^T += V^T P^T  A = V^T read from the row-major V tile with the gfx950
 //                   transposing LDS read ds_read_b64_tr_b16.
 //
-// Every K or V fragment read from LDS feeds both blocks' MFMAs, so a
-// wavefront reads half as many LDS bytes per MFMA as with 32-row
-// wavefronts (with two of those per SIMD the softmax hides better under the
-// MFMAs, but the causal prefill ran slower: twice the LDS reads and
-// barriers).  The three jobs of a step run interleaved in one instruction
-// stream: step t issues the MFMAs of S(t+1) and of O += P(t-1) V(t-1) while
-// the VALU runs the softmax of S(t).
+// The three jobs of a step run interleaved in one instruction stream: step
+// t issues the MFMAs of S(t+1) and of O += P(t-1) V(t-1) while the VALU runs
+// the softmax of S(t).  kOne = false selects the earlier mapping (256-row
+// tiles, two 32-row blocks per wavefront, blocks w and 7 - w, one workgroup
+// per CU: every K/V fragment read from LDS feeds two blocks, but a barrier
+// wait or an unhidden softmax leaves the SIMD idle); the single-block mapping
+// gives bit-identical results and ran the causal prefill 4.3% faster, the
+// non-causal 2.4% and the chunked prefill 5% in interleaved A/B runs.
 //
 // K/V tiles go from HBM straight into LDS (buffer loads with the LDS
 // destination, no VGPR staging): step t issues the loads of its tile pair
@@ -49,8 +51,10 @@
 // Registers: the MFMAs write VGPRs (the library builds this file with the
 // VGPR form of the matrix instructions), so the softmax reads S without
 // copies, and the Q fragments, which only the S MFMAs read, are placed in
-// AGPRs; the 512 registers of one wavefront per SIMD then hold both blocks'
-// O and S, Q, P and the LDS reads issued several MFMAs ahead.
+// AGPRs; a wavefront's block then needs about 200 registers (O, two sets of
+// S, Q, P and the LDS reads issued several MFMAs ahead), within the 256 that
+// two wavefronts per SIMD leave each (the two-block mapping used ~405 of 512
+// at one wavefront per SIMD).
 //
 // Softmax reference.  Each row's exponentials are taken against the row max
 // of its first key tile, held for the whole pass, so no running max is kept
@@ -63,12 +67,13 @@
 // that the MFMA multiplies with V.
 //
 // Causal masking (key j visible to query i iff j <= i + Tk - Tq) is applied
-// only on tiles that cross a block's diagonal.  Once a wavefront's earlier
-// block is past its last visible key tile, its steps run on the later block
-// alone (half the MFMAs and softmax), which removes most of the work above
-// the diagonal.  When there are at least two query tiles per CU, a
-// workgroup takes query tiles p and n - 1 - p of one (b, h) (equal causal
-// work per workgroup), the heavier one first, and the workgroups of one
+// only on tiles that cross a block's diagonal.  Once a wavefront's block is
+// past its last visible key tile, its remaining steps only load and
+// synchronise (two-block mapping: they run on the later block alone), which
+// removes most of the work above the diagonal.  When there are at least two
+// query tiles per workgroup slot (four per CU), a workgroup takes query
+// tiles p and n - 1 - p of one (b, h) (equal causal work per workgroup), the
+// heavier one first, and the workgroups of one
 // (b, h) sit on one XCD at the same time: their heavier tiles walk the
 // shared keys in step, so one fetch from HBM serves both through that XCD's
 // L2.  The lighter tiles come later and fetch their keys again (an XCD's L2
@@ -87,7 +92,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = 256;                 // query rows per query tile (8 blocks of 32)
+// single-block mode: one 32-row block per wavefront, 128-row query tiles,
+// two workgroups per CU
+constexpr bool kOne = true;
+constexpr int kBM = kOne ? 128 : 256;    // query rows per query tile
 constexpr int kBN = 32;                  // keys per K/V tile
 constexpr float kRescaleThresh = 8.0f;   // log2 units
 
@@ -234,7 +242,7 @@ __device__ __forceinline__ void dma_barrier() {
 }
 
 template <int D, bool CAUSAL, bool PAGED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOne ? 2 : 1, kOne ? 2 : 1)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                          float* __restrict__ lse, int BH, int Hq, int Hkv, int Tq, int Tk_dense,
@@ -259,7 +267,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
     const int li = lane & 31, hi = lane >> 5;
-    const int rb0 = wave, rb1 = 7 - wave;   // this wavefront's two 32-row blocks
+    const int rb0 = wave, rb1 = kOne ? wave : 7 - wave;   // this wavefront's 32-row blocks
 
     // Workgroups are dealt to the 8 XCDs round-robin, so id % 8 picks the
     // XCD.  slot = id % BH: kv group kg = slot % (B * Hkv), head within the
@@ -333,7 +341,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     auto issue_tile = [&](int u) {
         const int q0u = tile_of(u) * kBM;
 #pragma unroll
-        for (int a = 0; a < 2; a++) {
+        for (int a = kOne ? 1 : 0; a < 2; a++) {
             const int qrow = q0u + 32 * (a ? rb1 : rb0) + li;
             const int qr = min(qrow, max(Tq - 1, 0));
 #pragma unroll
@@ -361,7 +369,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         // first tile that needs a mask for either block: the one holding key
         // Tk (partial tile) or, causal, the first key past the earlier block's
         // first row
-        const int t_mask = CAUSAL ? max(0, min(Tk, qa0 + diag + 1)) / kBN : Tk / kBN;
+        const int t_mask = CAUSAL ? max(0, min(Tk, (kOne ? qa1 : qa0) + diag + 1)) / kBN : Tk / kBN;
         // per-block last visible key of this lane's row
         const int lim0 = CAUSAL ? min(Tk - 1, qrow0 + diag) : Tk - 1;
         const int lim1 = CAUSAL ? min(Tk - 1, qrow1 + diag) : Tk - 1;
@@ -379,7 +387,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             for (int s = 0; s < C::KS; s++) {
                 const bf16x8 kf = *(const bf16x8 LDS_AS*)(sk + koff[s]);
 #pragma unroll
-                for (int a = 0; a < 2; a++)
+                for (int a = kOne ? 1 : 0; a < 2; a++)
                     sacc[P][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         kf, qf[a][s], s == 0 ? f32x16{} : sacc[P][a], 0, 0, 0);
             }
@@ -426,7 +434,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             float m_eff[2];
             int limt[2];   // masked steps: register r of block a is visible iff 8(r/4) + r%4 <= limt[a]
 #pragma unroll
-            for (int a = 0; a < 2; a++) {
+            for (int a = kOne ? 1 : 0; a < 2; a++) {
                 limt[a] = (a ? lim1 : lim0) - t_cur * kBN - 4 * hi;
                 if constexpr (decltype(FIRST)::value) {
                     mask_tile(sacc[P][a], a);
@@ -519,7 +527,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
         // last key tile of this wavefront's block 0 (the one that holds the
         // last key its last row sees; -1 when it sees none)
-        const int T0 = CAUSAL ? (min(Tk - 1, qa0 + 31 + diag) >= 0 ? min(Tk - 1, qa0 + 31 + diag) / kBN : -1)
+        const int qaT = kOne ? qa1 : qa0;
+        const int T0 = CAUSAL ? (min(Tk - 1, qaT + 31 + diag) >= 0 ? min(Tk - 1, qaT + 31 + diag) / kBN : -1)
                               : n - 1;
         // One pass over the key tiles.  Step t: S(t+1), softmax(t), PV(t-1);
         // pair t (K(t+2), V(t)) is loaded into LDS stage t%2, which step t - 1
@@ -567,7 +576,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             // unmasked pairs while both steps precede t_mask, then masked pairs
             // up to step n (masking a tile that needs none, or running a step
             // past n, changes nothing).
-            const Jobs<2, 2, 2> BOTH;
+            using BothJ = std::conditional_t<kOne, Jobs<1, 1, 1>, Jobs<2, 2, 2>>;
+            const BothJ BOTH;
             step(0, P0, Y, std::integral_constant<bool, !G>{}, BOTH);
             int t = 1;
             for (; t + 2 <= t_mask; t += 2) {
@@ -583,9 +593,12 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                 step(t + 1, P0, Y, N, BOTH);
             }
             if constexpr (CAUSAL) {
+                // single-block mode: past its block's last key tile a
+                // wavefront only loads and synchronises
+                using HalfJ = std::conditional_t<kOne, Jobs<0, 0, 0>, Jobs<1, 1, 1>>;
                 for (; t <= n; t += 2) {
-                    step(t, P1, Y, N, Jobs<1, 1, 1>{});
-                    step(t + 1, P0, Y, N, Jobs<1, 1, 1>{});
+                    step(t, P1, Y, N, HalfJ{});
+                    step(t + 1, P0, Y, N, HalfJ{});
                 }
             }
             return flag;
@@ -607,7 +620,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                     dma_barrier();
                     s_mfma(std::integral_constant<int, 0>{});
 #pragma unroll
-                    for (int a = 0; a < 2; a++) {
+                    for (int a = kOne ? 1 : 0; a < 2; a++) {
                         t_cur = t;
                         mask_tile(sacc[0][a], a);
                         m_ref[a] = fmaxf(m_ref[a], row_max(sacc[0][a]));
@@ -633,7 +646,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
         // ---- epilogue: O = O / l, lse = m ln2 + ln l ------------------------
 #pragma unroll
-        for (int a = 0; a < 2; a++) {
+        for (int a = kOne ? 1 : 0; a < 2; a++) {
             const int qrow = a ? qrow1 : qrow0;
             const float l_tot = half_swap_sum(l_run[a]);
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -663,7 +676,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 // Pair query tiles p and n - 1 - p in one workgroup when that still leaves
 // at least one workgroup per CU.
 void grid_of(int BH, int n_qtiles, dim3* grid, int* paired) {
-    *paired = (long)BH * n_qtiles >= 2L * device_cus() && n_qtiles >= 2;
+    // pairs only while they still leave kOne ? 2 : 1 workgroups per CU
+    *paired = (long)BH * n_qtiles >= (kOne ? 4L : 2L) * device_cus() && n_qtiles >= 2;
     *grid = dim3(BH * (*paired ? (n_qtiles + 1) / 2 : n_qtiles));
 }
 

@@ -205,8 +205,8 @@ def test_prefill_late_dominant_key_bf16(causal, D):
 @pytest.mark.parametrize("Tk", [300, 700])
 def test_prefill_paired_tiles_with_empty_rows(Tk):
     """B4 H32 Tq1024 D128 causal bf16 with fewer keys than queries
-    (bottom-right diagonal at Tk - Tq): 512 query tiles, so each workgroup
-    takes two, and with Tk = 300 both tiles of some workgroups see no key at
+    (bottom-right diagonal at Tk - Tq): 1024 query tiles of 128 rows, so
+    each workgroup takes two, and with Tk = 300 both tiles of some workgroups see no key at
     all while others pair an empty tile with a full one.  Rows before
     Tq - Tk are O = 0 with lse = -inf; sampled (b, h) pairs match the
     oracle."""
@@ -218,5 +218,26 @@ def test_prefill_paired_tiles_with_empty_rows(Tk):
     for b, h in [(0, 0), (1, 5), (2, 17), (3, 30), (3, 31)]:
         ro, rl = oracle.attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, h:h + 1],
                                   inp["v"][b:b + 1, h:h + 1], True, inp["scale"])
+        assert_close(o[b, h], ro[0, 0], "bf16", f"O (b={b},h={h})")
+        assert_close(lse[b, h], rl[0, 0], "bf16", f"lse (b={b},h={h})")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("Hkv,D", [(32, 128), (8, 128), (32, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_paired_odd_tile_count_ragged(Hkv, D, causal):
+    """B5 Hq32 T840: seven 128-row query tiles per (b, h), the last holding
+    72 rows, and 1120 tiles in all, enough for workgroups to take tiles p and
+    6 - p; the middle workgroup of each (b, h) takes tile 3 alone.  Sampled
+    (b, h) pairs, one per kv group where grouped, match the oracle."""
+    require_gpu()
+    B, Hq, T = 5, 32, 840
+    inp = wl.prefill_inputs(B, Hq, Hkv, T, T, D, "bf16", 930 + Hkv + D + int(causal))
+    o, lse = run_prefill(inp, causal=causal)
+    G = Hq // Hkv
+    for b, h in [(0, 0), (1, 9), (2, 18), (3, 27), (4, 31)]:
+        kh = h // G
+        ro, rl = oracle.attention(inp["q"][b:b + 1, h:h + 1], inp["k"][b:b + 1, kh:kh + 1],
+                                  inp["v"][b:b + 1, kh:kh + 1], causal, inp["scale"])
         assert_close(o[b, h], ro[0, 0], "bf16", f"O (b={b},h={h})")
         assert_close(lse[b, h], rl[0, 0], "bf16", f"lse (b={b},h={h})")

@@ -80,3 +80,23 @@ def test_prefill_paged_chunk512_sampled():
                                   d["block_table"], d["kv_lens"], True, d["scale"])
     assert_close(o[:, heads], ro, "bf16", "chunk O")
     assert_close(lse[:, heads], rl, "bf16", "chunk lse")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_paged_paired_tiles(causal):
+    """B4 Hq32 Hkv8 D128 with a 1000-token chunk: eight 128-row query tiles
+    per (b, h), the last holding 104 rows, 1024 in all, so workgroups take
+    tiles p and 7 - p; one sequence (600 tokens) is shorter than the chunk,
+    so its first 400 rows see no key.  Two kv heads and their query heads,
+    every sequence, against the oracle."""
+    require_gpu()
+    d = wl.paged_prefill_inputs(4, 32, 8, 1000, 128, "bf16", 1213 + int(causal),
+                                lengths=[1000, 1700, 3000, 600])
+    o, lse = run(d, causal)
+    for kvh in (0, 5):
+        heads = slice(4 * kvh, 4 * kvh + 4)
+        ro, rl = oracle.prefill_paged(d["q"][:, heads], d["k_pages"][:, kvh:kvh + 1],
+                                      d["v_pages"][:, kvh:kvh + 1], d["block_table"],
+                                      d["kv_lens"], causal, d["scale"])
+        assert_close(o[:, heads], ro, "bf16", f"O (kv head {kvh})")
+        assert_close(lse[:, heads], rl, "bf16", f"lse (kv head {kvh})")
